@@ -1,0 +1,193 @@
+"""Python binding of libgdn, the HIP library of the Gated DeltaNet recurrent
+mixer for MI355X (gfx950).  The C ABI is include/gdn.h; this module only
+marshals torch tensors (device memory) and streams into those calls and
+checks that each tensor has the size, dtype and device the call expects, so
+that a mistake in Python raises here instead of reaching a kernel.
+
+Every computation runs in the HIP library.  If libgdn.so is missing this
+module raises on import: there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
+    "prefill_workspace_bytes", "conv_update", "decode_step", "tree_verify", "commit_path",
+    "tree_tables", "prefill_chunked", "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH",
+    "PREFILL_CHUNK", "F32", "BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+MAX_TREE_NODES = 32
+MAX_TREE_DEPTH = 8
+PREFILL_CHUNK = 64
+F32, BF16 = 0, 1
+_STATUS_TREE = 5
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m gated_deltanet_decode_amd.build`")
+
+_lib = C.CDLL(LIB_PATH)
+
+
+class Dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("batch", "num_k_heads", "num_v_heads", "head_k_dim",
+                                         "head_v_dim", "conv_width", "act_dtype")]
+
+    @property
+    def C(self) -> int:
+        return 2 * self.num_k_heads * self.head_k_dim + self.num_v_heads * self.head_v_dim
+
+    @property
+    def act_torch(self):
+        return torch.bfloat16 if self.act_dtype == BF16 else torch.float32
+
+
+def dims(batch, num_k_heads, num_v_heads, head_k_dim, head_v_dim, conv_width=4, act="bf16") -> Dims:
+    return Dims(batch, num_k_heads, num_v_heads, head_k_dim, head_v_dim, conv_width,
+                BF16 if act in ("bf16", BF16, torch.bfloat16) else F32)
+
+
+_P = C.c_void_p
+_D = C.POINTER(Dims)
+_I = C.c_int32
+_sig = {
+    "gdn_abi_version": ([], C.c_int),
+    "gdn_status_str": ([C.c_int], C.c_char_p),
+    "gdn_conv_channels": ([_D], C.c_size_t),
+    "gdn_state_bytes": ([_D], C.c_size_t),
+    "gdn_conv_tail_bytes": ([_D], C.c_size_t),
+    "gdn_prefill_workspace_bytes": ([_D, _I], C.c_size_t),
+    "gdn_conv_update": ([_D, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_decode_step": ([_D, _P, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
+    "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
+}
+for _name, (_args, _res) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call}: {_lib.gdn_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise GdnError(status, call)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _t(t: torch.Tensor, name: str, dtype, numel: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype, numel):
+    return None if t is None else _t(t, name, dtype, numel)
+
+
+def conv_channels(d: Dims) -> int:
+    return _lib.gdn_conv_channels(C.byref(d))
+
+
+def state_bytes(d: Dims) -> int:
+    return _lib.gdn_state_bytes(C.byref(d))
+
+
+def conv_tail_bytes(d: Dims) -> int:
+    return _lib.gdn_conv_tail_bytes(C.byref(d))
+
+
+def prefill_workspace_bytes(d: Dims, T: int) -> int:
+    return _lib.gdn_prefill_workspace_bytes(C.byref(d), T)
+
+
+def conv_update(d: Dims, x, tail, w, y, stream=None) -> None:
+    B, Cc = d.batch, d.C
+    _check(_lib.gdn_conv_update(C.byref(d), _t(x, "x", d.act_torch, B * Cc),
+                                _t(tail, "conv_tail", d.act_torch, B * Cc * 4),
+                                _t(w, "conv_w", d.act_torch, Cc * 4),
+                                _t(y, "y", torch.float32, B * Cc), _stream(stream)), "gdn_conv_update")
+
+
+def decode_step(d: Dims, state, y, a, b, o, stream=None) -> None:
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_decode_step(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                _t(y, "y", torch.float32, B * Cc), _t(a, "a", torch.float32, B * Hv),
+                                _t(b, "b", torch.float32, B * Hv), _t(o, "o", torch.float32, B * Hv * dv),
+                                _stream(stream)), "gdn_decode_step")
+
+
+def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, stream=None) -> None:
+    n = parent.numel()
+    Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_tree_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, Hv * dv * dk),
+                                _t(tail, "conv_tail", d.act_torch, Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                                n, _t(parent, "parent", torch.int32, n), _t(x, "x", d.act_torch, n * Cc),
+                                _t(a, "a", torch.float32, n * Hv), _t(b, "b", torch.float32, n * Hv),
+                                _t(o, "o", torch.float32, n * Hv * dv), _opt(status, "tree_status", torch.int32, 1),
+                                _stream(stream)), "gdn_tree_verify")
+
+
+def commit_path(d: Dims, state, tail, w, parent, x, a, b, path, o=None, status=None, stream=None) -> None:
+    n, L = parent.numel(), path.numel()
+    Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_commit_path(C.byref(d), _t(state, "state", torch.float32, Hv * dv * dk),
+                                _t(tail, "conv_tail", d.act_torch, Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                                n, _t(parent, "parent", torch.int32, n), _t(x, "x", d.act_torch, n * Cc),
+                                _t(a, "a", torch.float32, n * Hv), _t(b, "b", torch.float32, n * Hv),
+                                L, _t(path, "path", torch.int32, L), _opt(o, "o", torch.float32, L * Hv * dv),
+                                _opt(status, "tree_status", torch.int32, 1), _stream(stream)), "gdn_commit_path")
+
+
+def tree_tables(parent, depth, order, status, stream=None) -> None:
+    n = parent.numel()
+    _check(_lib.gdn_tree_tables(n, _t(parent, "parent", torch.int32, n), _t(depth, "depth", torch.int32, n),
+                                _t(order, "order", torch.int32, n), _t(status, "tree_status", torch.int32, 1),
+                                _stream(stream)), "gdn_tree_tables")
+
+
+def prefill_chunked(d: Dims, state, tail, w, x, a, b, o, workspace=None, stream=None) -> None:
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    if x.numel() % (B * Cc):
+        raise ValueError("x must be [B][T][C]")
+    T = x.numel() // (B * Cc)
+    need = prefill_workspace_bytes(d, T)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace of {ws_bytes} bytes, need {need}")
+    _check(_lib.gdn_prefill_chunked(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                    _t(tail, "conv_tail", d.act_torch, B * Cc * 4),
+                                    _t(w, "conv_w", d.act_torch, Cc * 4), T, _t(x, "x", d.act_torch, B * T * Cc),
+                                    _t(a, "a", torch.float32, B * T * Hv), _t(b, "b", torch.float32, B * T * Hv),
+                                    _t(o, "o", torch.float32, B * T * Hv * dv), ws_ptr, ws_bytes, _stream(stream)),
+           "gdn_prefill_chunked")

@@ -1,0 +1,185 @@
+// gdn_core.hpp -- the per-token arithmetic shared by every recurrent kernel.
+//
+// Decode, tree verify and commit must agree bit for bit (the repository
+// "Architecture" page says of the second model that its verify rows equal its
+// decode rows bit for bit; section 8.1 of the first page asks for exact undo
+// and branch).  Floating point does not associate, so the three kernels call
+// the functions below and nothing else for: the conv tap sum and SiLU, the
+// gates, the q/k L2 norm and k.q reduction (one fixed wave-wide butterfly),
+// and the row update (one fixed lane-to-column map and butterfly).  The build
+// passes -ffp-contract=off; every fused multiply-add here is written out.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr float kEps = 1e-6f;  // q/k L2-norm epsilon
+constexpr int kWave = 64;
+constexpr int kMaxNodes = 32;
+constexpr int kMaxDepth = 8;
+
+template <int D>
+struct Scale;  // 1/sqrt(dk), written as the correctly rounded fp32 constant
+template <>
+struct Scale<32> { static constexpr float value = 0.17677669529663687f; };
+template <>
+struct Scale<128> { static constexpr float value = 0.08838834764831845f; };
+
+// ------------------------------------------------------------ activation storage
+
+// bf16 activations travel as raw 16-bit patterns; widening is a shift.
+__device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+__device__ __forceinline__ float widen(float f) { return f; }
+
+// Four consecutive activation values (one tail or weight row).
+template <typename Act>
+struct Quad;
+template <>
+struct Quad<uint16_t> {
+    using raw = uint2;
+    __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ static void store(uint16_t* p, raw v) { *reinterpret_cast<uint2*>(p) = v; }
+    __device__ static void to_float(raw v, float f[4]) {
+        f[0] = __uint_as_float(v.x << 16);
+        f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        f[2] = __uint_as_float(v.y << 16);
+        f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+    // shift left by one element and append `in` (raw bits)
+    __device__ static raw push(raw v, uint16_t in) {
+        raw r;
+        r.x = (v.x >> 16) | (v.y << 16);
+        r.y = (v.y >> 16) | (static_cast<uint32_t>(in) << 16);
+        return r;
+    }
+    __device__ static uint16_t elem(raw v, int j) {
+        uint32_t w = (j < 2) ? v.x : v.y;
+        return static_cast<uint16_t>((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+};
+template <>
+struct Quad<float> {
+    using raw = float4;
+    __device__ static raw load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ static void store(float* p, raw v) { *reinterpret_cast<float4*>(p) = v; }
+    __device__ static void to_float(raw v, float f[4]) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+    __device__ static raw push(raw v, float in) { return make_float4(v.y, v.z, v.w, in); }
+    __device__ static float elem(raw v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+};
+
+// ------------------------------------------------------------ scalar pieces
+
+// y = SiLU(sum_j w[j] * win[j]) with the taps summed oldest first.
+__device__ __forceinline__ float conv_silu(const float w[4], const float win[4]) {
+    float acc = w[0] * win[0];
+    acc = __builtin_fmaf(w[1], win[1], acc);
+    acc = __builtin_fmaf(w[2], win[2], acc);
+    acc = __builtin_fmaf(w[3], win[3], acc);
+    return acc / (1.0f + expf(-acc));
+}
+
+// alpha = exp(-softplus(a)) = 1 / (1 + e^a);  beta = sigmoid(b) = 1 / (1 + e^-b).
+__device__ __forceinline__ void gates(float a, float b, float& alpha, float& beta) {
+    alpha = 1.0f / (1.0f + expf(a));
+    beta = 1.0f / (1.0f + expf(-b));
+}
+
+// ------------------------------------------------------------ wave reductions
+
+// Butterfly sum over aligned groups of `Width` lanes.  Every lane of a group
+// ends with the same bits: at each step lane i adds the partner's value to its
+// own, and the partner adds the same two numbers the other way round.
+template <int Width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < Width; m <<= 1)
+        v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// ------------------------------------------------------------ q/k preparation
+
+// One wave normalises one token's q~ and k~ of one q/k head.  Lane l holds
+// elements l + 64*j (j < J); lanes past D hold zeros.  On return they hold q^,
+// k^ and every lane holds kq = k^.q^.
+template <int D>
+struct Prep {
+    static constexpr int J = D >= kWave ? D / kWave : 1;
+};
+
+template <int D>
+__device__ __forceinline__ void prep_qk(float (&q)[Prep<D>::J], float (&k)[Prep<D>::J], float& kq) {
+    constexpr int J = Prep<D>::J;
+    float nq = 0.0f, nk = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        nq = __builtin_fmaf(q[j], q[j], nq);
+        nk = __builtin_fmaf(k[j], k[j], nk);
+    }
+    nq = group_sum<kWave>(nq);
+    nk = group_sum<kWave>(nk);
+    const float rq = 1.0f / sqrtf(nq + kEps);
+    const float rk = 1.0f / sqrtf(nk + kEps);
+    float d = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        q[j] = q[j] * rq;
+        k[j] = k[j] * rk;
+        d = __builtin_fmaf(q[j], k[j], d);
+    }
+    kq = group_sum<kWave>(d);
+}
+
+// ------------------------------------------------------------ the row update
+
+// A state row of D keys is spread over LPR consecutive lanes; lane r of the
+// group holds the float4 vectors at keys j*4*LPR + 4*r .. +3 for j < NV.
+template <int D>
+struct Row {
+    static constexpr int LPR = (D == 128) ? 16 : 8;
+    static constexpr int NV = D / (4 * LPR);
+    static constexpr int RPW = kWave / LPR;  // rows per wave
+    __device__ static int key(int j, int r) { return j * 4 * LPR + 4 * r; }
+};
+
+__device__ __forceinline__ float dot4(float4 s, float4 k, float acc) {
+    acc = __builtin_fmaf(s.x, k.x, acc);
+    acc = __builtin_fmaf(s.y, k.y, acc);
+    acc = __builtin_fmaf(s.z, k.z, acc);
+    acc = __builtin_fmaf(s.w, k.w, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float4 axpby4(float u, float4 k, float alpha, float4 s) {
+    return make_float4(__builtin_fmaf(u, k.x, alpha * s.x), __builtin_fmaf(u, k.y, alpha * s.y),
+                       __builtin_fmaf(u, k.z, alpha * s.z), __builtin_fmaf(u, k.w, alpha * s.w));
+}
+
+// One token on one row S[i,:] (this lane's slice in s):
+//   p = alpha (S.k);  u = beta (v_i - p);  S <- alpha S + u k;
+//   o_i = scale (alpha (S_old.q) + u (k.q))   [= scale (S_new.q)]
+// Both dot products come from one pass over the old row.  Returns o_i on every
+// lane of the row group.
+template <int D>
+__device__ __forceinline__ float row_update(float4 (&s)[Row<D>::NV], const float4 (&k)[Row<D>::NV],
+                                            const float4 (&q)[Row<D>::NV], float alpha, float beta,
+                                            float v, float kq) {
+    constexpr int NV = Row<D>::NV;
+    float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        pk = dot4(s[j], k[j], pk);
+        pq = dot4(s[j], q[j], pq);
+    }
+    pk = group_sum<Row<D>::LPR>(pk);
+    pq = group_sum<Row<D>::LPR>(pq);
+    const float u = beta * (v - alpha * pk);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        s[j] = axpby4(u, k[j], alpha, s[j]);
+    return Scale<D>::value * __builtin_fmaf(u, kq, alpha * pq);
+}
+
+}  // namespace gdn

@@ -1,0 +1,30 @@
+// gdn_launch.hpp -- host-side launchers of the kernels, called by the C ABI
+// after it has validated every argument.  Each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct Geo {
+    int B, Hk, Hv, D, C;
+    bool bf16;
+};
+
+hipError_t launch_conv_update(const Geo& g, const void* x, void* tail, const void* w, float* y, hipStream_t s);
+hipError_t launch_decode(const Geo& g, float* S, const float* y, const float* a, const float* b, float* o,
+                         hipStream_t s);
+hipError_t launch_tree_tables(int n, const int32_t* parent, int32_t* depth, int32_t* order, int32_t* status,
+                              hipStream_t s);
+hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
+                              const int32_t* parent, const void* x, const float* a, const float* b, float* o,
+                              int32_t* status, hipStream_t s);
+hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
+                         const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
+                         int32_t* status, hipStream_t s);
+size_t prefill_workspace_bytes(const Geo& g, int T);
+hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int T, const void* x, const float* a,
+                          const float* b, float* o, void* ws, hipStream_t s);
+
+}  // namespace gdn

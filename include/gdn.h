@@ -1,0 +1,188 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet recurrent-mixer library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The serving-engine pages describe the problem this library solves
+ * ("Architecture", section 8.1 and its table; repository "Architecture" page,
+ * "The decode loop" and its sequence diagram): each recurrent layer keeps, per
+ * sequence, a fixed-size fp32 state of Hv heads of dv x dk plus a 4-wide
+ * convolution tail; the engine advances it one token at a time, branches it
+ * over a draft tree of up to 32 nodes in one verify pass, and then commits the
+ * accepted path, or undoes the round by not committing.  Long prompts are
+ * prefilled in chunks; the CPU page ("Serving a research architecture on
+ * CPU", exactness section) notes that the chunked and the token-by-token
+ * forms are the same algebra with different rounding.
+ *
+ * Per token and sequence, with C = 2*Hk*dk + Hv*dv conv channels (q | k | v):
+ *   tail   shifts left by one and takes the raw input x[c] as its newest entry
+ *   conv   y[c] = SiLU(sum_{j<4} w[c][j] * tail[c][j])
+ *   norm   q^ = q~ / sqrt(|q~|^2 + 1e-6), k^ likewise, per q/k head
+ *   gates  alpha = exp(-softplus(a)), beta = sigmoid(b), per value head
+ *   state  S <- alpha*S + beta*(v - alpha*S k^) k^T      (rank-1, in place)
+ *   output o = (S q^) / sqrt(dk)                         (from the new state)
+ * Value head h reads q/k head h / (Hv/Hk).
+ *
+ * Conventions for every call below.
+ *   Memory: every array pointer is caller-owned DEVICE memory on the current
+ *     HIP device, 16-byte aligned, dense, in the layout stated.  The library
+ *     allocates nothing, keeps no mutable global state, never synchronises,
+ *     and enqueues all work on `stream` (a hipStream_t passed as void*; NULL
+ *     is the null stream).  Calls are graph-capturable.
+ *   Errors: argument errors the host can see are returned before anything is
+ *     enqueued, with nothing written.  A failed launch returns GDN_ERR_HIP.
+ *     Errors only the device can see (a malformed parent or path array) are
+ *     reported through an optional device status word; then the checkpoint
+ *     state and tail are left as they were.
+ *   Types: state, y, a, b and o are fp32.  x, the conv tail and the conv
+ *     weights share the activation type (GDN_BF16 or GDN_F32).
+ *   Supported shapes: head_k_dim == head_v_dim in {32, 128};
+ *     num_v_heads % num_k_heads == 0; conv_width == 4; batch >= 1.
+ *   Concurrency: calls on different streams with disjoint buffers are
+ *     independent; calls that share an in/out buffer must be ordered by the
+ *     caller.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_MAX_TREE_NODES 32 /* draft trees of up to 32 nodes (decode-loop diagram) */
+#define GDN_MAX_TREE_DEPTH 8  /* nodes on a root-to-leaf path, root counted */
+#define GDN_PREFILL_CHUNK 64
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,       /* unsupported or inconsistent dims, or a size out of range */
+    GDN_ERR_DTYPE = 3,       /* act_dtype is not GDN_F32 or GDN_BF16 */
+    GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    GDN_ERR_TREE = 5,        /* malformed tree or path (also the device status value) */
+    GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+    GDN_ERR_HIP = 7          /* the HIP runtime refused a launch */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+    int32_t batch;        /* B: independent sequences */
+    int32_t num_k_heads;  /* Hk: q/k heads */
+    int32_t num_v_heads;  /* Hv: value heads = state heads */
+    int32_t head_k_dim;   /* dk */
+    int32_t head_v_dim;   /* dv */
+    int32_t conv_width;   /* W: must be 4 */
+    int32_t act_dtype;    /* gdn_dtype of x, conv tail and conv weights */
+} gdn_dims;
+
+/* Library version and a static message for a status code. */
+int gdn_abi_version(void);
+const char* gdn_status_str(int status);
+
+/* Sizes, computable before any model exists; none depends on the number of
+ * tokens.  0 for dims the library does not support. */
+size_t gdn_conv_channels(const gdn_dims* d);   /* C = 2*Hk*dk + Hv*dv */
+size_t gdn_state_bytes(const gdn_dims* d);     /* B*Hv*dv*dk*4 */
+size_t gdn_conv_tail_bytes(const gdn_dims* d); /* B*C*W*sizeof(act) */
+
+/*
+ * gdn_conv_update -- one token of the causal depthwise conv (section 8.1
+ * table's 4-wide tail; the CPU page's convolution rings).
+ *   x         act  [B][C]     raw q|k|v activations of this token (read)
+ *   conv_tail act  [B][C][4]  last four raw inputs, oldest first (in/out)
+ *   conv_w    act  [C][4]     taps, tap 3 multiplies the newest input (read)
+ *   y         f32  [B][C]     SiLU(conv) (written)
+ */
+gdn_status gdn_conv_update(const gdn_dims* d, const void* x, void* conv_tail,
+                           const void* conv_w, float* y, void* stream);
+
+/*
+ * gdn_decode_step -- one token of the recurrence for every sequence
+ * (section 8.1: a fixed-size state advanced per token; CPU page: a rank-1
+ * update written in place).
+ *   state f32 [B][Hv][dv][dk]  rows over the value index, contiguous over keys (in/out)
+ *   y     f32 [B][C]           output of gdn_conv_update for this token (read)
+ *   a, b  f32 [B][Hv]          gate inputs (read)
+ *   o     f32 [B][Hv][dv]      output (written)
+ */
+gdn_status gdn_decode_step(const gdn_dims* d, float* state, const float* y,
+                           const float* a, const float* b, float* o, void* stream);
+
+/*
+ * gdn_tree_verify -- one read-only pass over a draft tree of n_nodes tokens
+ * (decode-loop diagram: a tree of up to 32 nodes verified in one pass;
+ * section 8.1: the state must be branched for a tree of guesses).  Node 0 is
+ * the root, the last committed token, whose parent is the checkpoint; every
+ * other node's state is branched from its parent's.  Node n's output equals,
+ * bit for bit, the output of gdn_conv_update + gdn_decode_step run over the
+ * root-first path to n from the checkpoint.  batch must be 1.
+ *   state_ckpt f32 [Hv][dv][dk]    checkpoint (read only)
+ *   conv_tail  act [C][4]          checkpoint tail (read only)
+ *   conv_w     act [C][4]
+ *   n_nodes    1..32
+ *   parent     i32 [n_nodes]       parent[0] == -1, 0 <= parent[i] < i, depth <= 8
+ *   x          act [n_nodes][C];  a, b f32 [n_nodes][Hv]
+ *   o          f32 [n_nodes][Hv][dv]  (written)
+ *   tree_status i32 [1] or NULL: set to GDN_OK, or GDN_ERR_TREE when parent[]
+ *              is malformed (o is then undefined).
+ */
+gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
+                           const void* conv_w, int32_t n_nodes, const int32_t* parent,
+                           const void* x, const float* a, const float* b, float* o,
+                           int32_t* tree_status, void* stream);
+
+/*
+ * gdn_commit_path -- commit the accepted root-first path of a verified tree
+ * (decode-loop diagram: commit the accepted path's recurrent state; section
+ * 8.1: exact undo).  The new (state, tail) is bit-identical to path_len calls
+ * of gdn_conv_update + gdn_decode_step over the path's tokens.  Undo is not
+ * calling this.  batch must be 1.
+ *   state      f32 [Hv][dv][dk]  in: checkpoint, out: committed (in/out)
+ *   conv_tail  act [C][4]        in/out
+ *   conv_w, n_nodes, parent, x, a, b: as for gdn_tree_verify
+ *   path_len   1..min(n_nodes, 8);  path i32 [path_len]: path[0] == 0,
+ *              parent[path[j]] == path[j-1]
+ *   o          f32 [path_len][Hv][dv] or NULL: per-token outputs
+ *   tree_status i32 [1] or NULL: GDN_OK, or GDN_ERR_TREE for a malformed
+ *              tree or path, in which case state and tail are untouched.
+ */
+gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w,
+                           int32_t n_nodes, const int32_t* parent, const void* x,
+                           const float* a, const float* b, int32_t path_len,
+                           const int32_t* path, float* o, int32_t* tree_status, void* stream);
+
+/*
+ * gdn_tree_tables -- the device-side tree analysis the two calls above use,
+ * exposed so its integer results can be checked exactly.
+ *   depth  i32 [n_nodes] root = 1;  order i32 [n_nodes]: depth-first pre-order
+ *   visiting children by increasing index;  tree_status i32 [1] (required).
+ */
+gdn_status gdn_tree_tables(int32_t n_nodes, const int32_t* parent, int32_t* depth,
+                           int32_t* order, int32_t* tree_status, void* stream);
+
+/*
+ * gdn_prefill_chunked -- T tokens per sequence from (state, tail), in chunks
+ * of 64 (repository "Architecture" page: the prompt is prefilled before the
+ * decode loop; CPU page: the chunked form is the same algebra as the
+ * token-by-token one).  Results match the token-by-token calls up to
+ * rounding; state and tail afterwards continue exactly like decode.
+ *   state     f32 [B][Hv][dv][dk]  in/out
+ *   conv_tail act [B][C][4]        in/out
+ *   x act [B][T][C];  a, b f32 [B][T][Hv];  o f32 [B][T][Hv][dv] (written)
+ *   workspace device bytes >= gdn_prefill_workspace_bytes(d, T) (may be NULL
+ *             when that size is 0).
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_dims* d, int32_t T);
+gdn_status gdn_prefill_chunked(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w,
+                               int32_t T, const void* x, const float* a, const float* b, float* o,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,107 @@
+"""The C-ABI library, on the CPU: it loads, exports every function include/gdn.h
+declares, and refuses bad arguments before it touches a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "gated_deltanet_decode_amd", "libgdn.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libgdn.so is not built (python -m gated_deltanet_decode_amd.build)")
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for f in ("gdn_conv_update", "gdn_decode_step", "gdn_tree_verify", "gdn_commit_path", "gdn_prefill_chunked"):
+        assert f in names
+
+
+def test_library_exports_every_declared_function(lib):
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, f"not exported: {missing}"
+
+
+class Dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("batch", "num_k_heads", "num_v_heads", "head_k_dim",
+                                         "head_v_dim", "conv_width", "act_dtype")]
+
+
+GOOD = dict(batch=1, num_k_heads=16, num_v_heads=48, head_k_dim=128, head_v_dim=128, conv_width=4, act_dtype=1)
+
+
+def mk(**kw):
+    d = dict(GOOD)
+    d.update(kw)
+    return Dims(**d)
+
+
+def test_size_queries_match_the_pages(lib):
+    """The 27B-class layer: 3.15 MB of fp32 state and an 80 KB bf16 conv tail per
+    sequence ("Architecture" section 8.1 table), 151 MB over 48 layers (8.2)."""
+    for f in ("gdn_state_bytes", "gdn_conv_tail_bytes", "gdn_conv_channels"):
+        getattr(lib, f).restype = C.c_size_t
+    d = mk()
+    assert lib.gdn_conv_channels(C.byref(d)) == 10240
+    assert lib.gdn_state_bytes(C.byref(d)) == 48 * 128 * 128 * 4 == 3_145_728
+    assert lib.gdn_conv_tail_bytes(C.byref(d)) == 4 * 10240 * 2 == 81_920
+    assert 48 * lib.gdn_state_bytes(C.byref(d)) == 150_994_944  # the pages' 151 MB
+    assert lib.gdn_state_bytes(C.byref(mk(batch=64))) == 64 * 3_145_728
+    assert lib.gdn_state_bytes(C.byref(mk(head_k_dim=64, head_v_dim=64))) == 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_k_dim=64, head_v_dim=64), 2), (dict(head_v_dim=32), 2), (dict(num_v_heads=40), 2),
+    (dict(conv_width=3), 2), (dict(batch=0), 2), (dict(act_dtype=7), 3),
+])
+def test_bad_dims_are_refused_before_launch(lib, bad, status):
+    """Non-null, aligned fake pointers: the call must return before using them."""
+    fake = C.c_void_p(0x1000)
+    d = mk(**bad)
+    assert lib.gdn_decode_step(C.byref(d), fake, fake, fake, fake, fake, None) == status
+    assert lib.gdn_conv_update(C.byref(d), fake, fake, fake, fake, None) == status
+
+
+def test_null_and_misaligned_pointers_are_refused(lib):
+    d = mk()
+    fake = C.c_void_p(0x1000)
+    odd = C.c_void_p(0x1004)
+    assert lib.gdn_decode_step(C.byref(d), None, fake, fake, fake, fake, None) == 1
+    assert lib.gdn_decode_step(C.byref(d), odd, fake, fake, fake, fake, None) == 4
+    assert lib.gdn_decode_step(None, fake, fake, fake, fake, fake, None) == 1
+
+
+def test_tree_sizes_are_refused_before_launch(lib):
+    fake = C.c_void_p(0x1000)
+    d = mk()
+    args = [fake] * 3
+    # n_nodes out of range
+    for n in (0, 33):
+        assert lib.gdn_tree_verify(C.byref(d), *args, n, fake, fake, fake, fake, fake, None, None) == 5
+    # batch must be 1 for trees
+    d2 = mk(batch=2)
+    assert lib.gdn_tree_verify(C.byref(d2), *args, 4, fake, fake, fake, fake, fake, None, None) == 2
+    # path longer than the depth limit, than the tree, or empty
+    for n, L in ((32, 9), (4, 5), (4, 0)):
+        assert lib.gdn_commit_path(C.byref(d), *args, n, fake, fake, fake, fake, L, fake, None, None, None) == 5
+    assert lib.gdn_tree_tables(0, fake, fake, fake, fake, None) == 5
+
+
+def test_status_strings(lib):
+    lib.gdn_status_str.restype = C.c_char_p
+    for s in range(8):
+        assert lib.gdn_status_str(s)
+    assert lib.gdn_abi_version() == 1
