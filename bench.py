@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Throughput of the Gated DeltaNet mixer library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows ...]
+
+The headline line is one decode step of one 27B-class recurrent layer at
+batch 1 (16 q/k heads and 48 value heads of 128, fp32 state of 3.15 MB, bf16
+activations and conv tail), repeated for K chained steps: a step is
+gdn_conv_update + gdn_decode_step.  Each step advances the next of R
+independent states (R * 3.15 MB > the 256 MB Infinity Cache), so every step
+reads its state from HBM, as it would in a model with 48 such layers and
+weights streaming in between.  The value is algorithmic state-traffic GB/s:
+bytes the step must move (state read + write, its vectors) over the time.
+
+Extra rows, each with its own roofline fraction: the same step under a hip
+graph, the state step alone (the dominant kernel), batch-64 decode (ping-pong
+over two batches), 32-node tree verify, path commit, chunked prefill at
+T = 32,768; and the CPU oracle on a bounded sample as the host baseline.
+Inputs are seeded synthetic tensors of the workload's shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+MFMA_FP16_TFLOPS = 2500.0  # dense fp16/bf16 MFMA, published
+
+SHAPE_DESC = {"num_k_heads": 16, "num_v_heads": 48, "head_k_dim": 128, "head_v_dim": 128, "conv_width": 4}
+
+
+def step_bytes(B, shape):
+    """Algorithmic bytes of one decode step (state step + conv update) for B sequences."""
+    Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
+    state = 2 * Hv * D * D * 4
+    dec_vec = C * 4 + 2 * Hv * 4 + Hv * D * 4          # y, a, b in; o out
+    conv = C * 2 + 2 * C * 4 * 2 + C * 4               # x in, tail in+out, y out (bf16 tail)
+    conv_w = C * 4 * 2                                  # weights, read once per launch
+    return B * (state + dec_vec), B * conv + conv_w
+
+
+def tree_bytes(n, shape):
+    Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
+    return (Hv * D * D * 4 + n * C * 2 + C * 4 * 2 + C * 4 * 2 + 2 * n * Hv * 4 + n * Hv * D * 4 + n * 4)
+
+
+def commit_bytes(L, shape):
+    Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
+    return (2 * Hv * D * D * 4 + L * C * 2 + 2 * C * 4 * 2 + C * 4 * 2 + 2 * L * Hv * 4 + L * Hv * D * 4)
+
+
+class Timer:
+    """HIP events on the stream the work is launched on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.s.record(self.torch.cuda.current_stream())
+        return self
+
+    def __exit__(self, *a):
+        self.e.record(self.torch.cuda.current_stream())
+        self.torch.cuda.synchronize()
+        self.ms = self.s.elapsed_time(self.e)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4096)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--buffers", type=int, default=160, help="independent states rotated through (cold runs)")
+    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,prefill,hot,cpu or all/none")
+    ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 512 MiB device copy (for byte counters)")
+    ap.add_argument("--details", default=None, help="write the full results JSON here")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (the mixer shards by q/k head "
+              "groups with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_deltanet_decode_amd as gdn
+    import gdn_inputs as gi
+
+    rows = set(["graph", "kernel", "b64", "tree", "commit", "prefill", "hot", "cpu"]) if args.rows == "all" else \
+        set() if args.rows == "none" else set(args.rows.split(","))
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    shape = gi.QWEN27B_LAYER
+    K, W, R = args.steps, args.warmup, args.buffers
+    C, Hv, D = shape.conv_channels, shape.num_v_heads, shape.head_k_dim
+
+    def act(arr):
+        arr = np.ascontiguousarray(arr)
+        return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    steps_total = K + W
+    inp = gi.decode_inputs(1, shape, 1, steps_total, state_sigma=0.1, tail_random=True)
+    pool = gi.decode_inputs(101, shape, R, 1, state_sigma=0.1, tail_random=True)  # R independent states
+    x = act(inp.x[:, 0])
+    a = f32(inp.a[:, 0])
+    b = f32(inp.b[:, 0])
+    w = act(inp.w)
+    S_pool = f32(pool.state)
+    tail_pool = act(pool.tail)
+    del pool
+    d1 = gdn.dims(1, 16, 48, 128, 128, 4, "bf16")
+    y = torch.empty(1, C, device=dev)
+    o = torch.empty(1, Hv, D, device=dev)
+    gen_s = time.time() - t0
+
+    def step(t, S, tail):
+        gdn.conv_update(d1, x[t], tail, w, y)
+        gdn.decode_step(d1, S, y, a[t], b[t], o)
+
+    res = {}
+    dec_b, conv_b = step_bytes(1, shape)
+    per_step = dec_b + conv_b
+
+    # ---------------------------------------------------------------- headline: cold, eager launches
+    for t in range(W):
+        step(t, S_pool[t % R], tail_pool[t % R])
+    with Timer(torch) as tm:
+        for t in range(W, W + K):
+            step(t, S_pool[t % R], tail_pool[t % R])
+    cold_ms = tm.ms
+    res["decode_b1_cold_eager"] = {"ms_per_step": cold_ms / K, "GBps": per_step * K / cold_ms / 1e6,
+                                   "tokens_per_s": K / cold_ms * 1e3}
+
+    # ---------------------------------------------------------------- same steps under a hip graph
+    graph_ms = None
+    if "graph" in rows:
+        chunk = min(K, 512)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for t in range(3):  # warm the capture stream
+                step(t, S_pool[t % R], tail_pool[t % R])
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            for t in range(chunk):
+                step(W + t, S_pool[t % R], tail_pool[t % R])
+        g.replay()
+        reps = max(1, K // chunk)
+        with Timer(torch) as tm:
+            for _ in range(reps):
+                g.replay()
+        graph_ms = tm.ms / (reps * chunk) * K
+        res["decode_b1_cold_graph"] = {"ms_per_step": graph_ms / K, "GBps": per_step * K / graph_ms / 1e6,
+                                       "tokens_per_s": K / graph_ms * 1e3, "graph_steps": chunk, "replays": reps}
+        del g
+
+    # ---------------------------------------------------------------- the state-step kernel alone
+    kern = None
+    if "kernel" in rows:
+        yk = torch.empty(R, 1, C, device=dev)
+        for r in range(R):
+            gdn.conv_update(d1, x[r % steps_total], tail_pool[r], w, yk[r])
+        nk = K
+        for t in range(64):
+            gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t], b[t], o)
+        with Timer(torch) as tm:
+            for t in range(nk):
+                gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t % steps_total], b[t % steps_total], o)
+        eager_us = tm.ms * 1e3 / nk
+        chunk = 512
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(chunk):
+                gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t], b[t], o)
+        g.replay()
+        reps = max(1, nk // chunk)
+        with Timer(torch) as tm:
+            for _ in range(reps):
+                g.replay()
+        graph_us = tm.ms * 1e3 / (reps * chunk)
+        kern = {"kernel": "decode_kernel<128,1>", "bytes_per_launch": dec_b, "us_per_launch_eager": eager_us,
+                "us_per_launch_graph": graph_us, "GBps_graph": dec_b / graph_us / 1e3,
+                "GBps_eager": dec_b / eager_us / 1e3}
+        res["decode_b1_kernel_cold"] = kern
+        del g, yk
+
+    # ---------------------------------------------------------------- hot: one state buffer
+    if "hot" in rows:
+        S1 = S_pool[0].clone()
+        t1 = tail_pool[0].clone()
+        for t in range(W):
+            step(t, S1, t1)
+        with Timer(torch) as tm:
+            for t in range(W, W + K):
+                step(t, S1, t1)
+        res["decode_b1_hot_eager"] = {"ms_per_step": tm.ms / K, "GBps": per_step * K / tm.ms / 1e6,
+                                      "note": "one 3.15 MB state: served from cache, not HBM"}
+
+    # ---------------------------------------------------------------- batch 64, ping-pong over two batches
+    if "b64" in rows:
+        B = 64
+        steps64 = 256
+        del S_pool  # make room; tree/commit use their own pool below
+        S_pool = None
+        inp64 = gi.decode_inputs(2, shape, 2 * B, 1, state_sigma=0.1, tail_random=True)
+        S64 = f32(inp64.state).view(2, B, Hv, D, D)
+        T64 = act(inp64.tail).view(2, B, C, 4)
+        w64 = act(inp64.w)
+        del inp64
+        xs = gi.decode_inputs(3, shape, B, steps64 + 16, state_sigma=0.0, tail_random=False)
+        x64, a64, b64 = act(xs.x), f32(xs.a), f32(xs.b)
+        del xs
+        d64 = gdn.dims(B, 16, 48, 128, 128, 4, "bf16")
+        y64 = torch.empty(B, C, device=dev)
+        o64 = torch.empty(B, Hv, D, device=dev)
+
+        def step64(t):
+            gdn.conv_update(d64, x64[t], T64[t % 2], w64, y64)
+            gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
+
+        for t in range(16):
+            step64(t)
+        with Timer(torch) as tm:
+            for t in range(16, 16 + steps64):
+                step64(t)
+        db, cb = step_bytes(B, shape)
+        res["decode_b64"] = {"ms_per_step": tm.ms / steps64, "GBps": (db + cb) * steps64 / tm.ms / 1e6,
+                             "tokens_per_s": B * steps64 / tm.ms * 1e3, "frac_hbm": (db + cb) * steps64 / tm.ms / 1e6 / HBM_PEAK_GBS}
+        # the state-step kernel alone at batch 64
+        for t in range(8):
+            gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
+        with Timer(torch) as tm:
+            for t in range(steps64):
+                gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
+        us = tm.ms * 1e3 / steps64
+        res["decode_b64"]["kernel_us"] = us
+        res["decode_b64"]["kernel_GBps"] = db / us / 1e3
+        res["decode_b64"]["kernel_frac_hbm"] = db / us / 1e3 / HBM_PEAK_GBS
+        del S64, T64, x64, a64, b64, y64, o64
+
+    # ---------------------------------------------------------------- tree verify + commit
+    if "tree" in rows or "commit" in rows:
+        tin = gi.tree_inputs(3, shape, n_nodes=32, max_depth=8)
+        pool = gi.decode_inputs(103, shape, R, 1, state_sigma=0.1, tail_random=True)
+        Sp = f32(pool.state)
+        Tp = act(pool.tail)
+        del pool
+        parent = torch.from_numpy(tin.extra["parent"]).to(dev)
+        path = torch.from_numpy(tin.extra["path"]).to(dev)
+        L = int(path.numel())
+        xt, at, bt, wt = act(tin.x[:, 0]), f32(tin.a[:, 0]), f32(tin.b[:, 0]), act(tin.w)
+        ot = torch.empty(32, Hv, D, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        nrep = 1024
+        if "tree" in rows:
+            for r in range(16):
+                gdn.tree_verify(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, ot, st)
+            with Timer(torch) as tm:
+                for r in range(nrep):
+                    gdn.tree_verify(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, ot, st)
+            us = tm.ms * 1e3 / nrep
+            tb = tree_bytes(32, shape)
+            res["tree_verify_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
+                                      "nodes_per_s": 32 / us * 1e6, "bytes": tb}
+        if "commit" in rows:
+            for r in range(16):
+                gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, path, None, st)
+            with Timer(torch) as tm:
+                for r in range(nrep):
+                    gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, path, None, st)
+            us = tm.ms * 1e3 / nrep
+            cbt = commit_bytes(L, shape)
+            res["commit_path"] = {"us": us, "path_len": L, "GBps": cbt / us / 1e3,
+                                  "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt}
+            if "tree_verify_n32" in res:
+                res["commit_path"]["committed_tokens_per_s"] = L / (us + res["tree_verify_n32"]["us"]) * 1e6
+        assert st.item() == 0
+        del Sp, Tp
+
+    # ---------------------------------------------------------------- chunked prefill
+    if "prefill" in rows:
+        try:
+            T = 32768
+            pin = gi.prefill_inputs(4, shape, T)
+            dP = gdn.dims(1, 16, 48, 128, 128, 4, "bf16")
+            Sx = f32(pin.state)
+            Tx = act(pin.tail)
+            xP, aP, bP, wP = act(pin.x), f32(pin.a), f32(pin.b), act(pin.w)
+            oP = torch.empty(1, T, Hv, D, device=dev)
+            ws_n = gdn.prefill_workspace_bytes(dP, T)
+            ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+            gdn.prefill_chunked(dP, Sx, Tx, wP, xP, aP, bP, oP, ws)
+            reps = 5
+            with Timer(torch) as tm:
+                for _ in range(reps):
+                    gdn.prefill_chunked(dP, Sx, Tx, wP, xP, aP, bP, oP, ws)
+            us = tm.ms * 1e3 / reps
+            flop = prefill_flops(T, shape)
+            res["prefill_t32768"] = {"us": us, "tokens_per_s": T / us * 1e6, "TFLOPs": flop / us / 1e6,
+                                     "frac_mfma_fp16": flop / us / 1e6 / MFMA_FP16_TFLOPS}
+        except Exception as e:  # reported, not hidden
+            res["prefill_t32768"] = {"error": str(e)}
+
+    # ---------------------------------------------------------------- copy calibration for byte counters
+    if args.copy_calibration:
+        n = 512 * 1024 * 1024 // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4, "launches": 4}
+        del src, dst
+
+    # ---------------------------------------------------------------- CPU oracle on a bounded sample
+    cpu = None
+    if "cpu" in rows:
+        import oracle
+        oracle.build(force=False)
+        budget_s = 12.0
+        tok = 0
+        S0 = inp.state[0]
+        tail0 = inp.tail[0]
+        t0 = time.time()
+        chunk = 8
+        while time.time() - t0 < budget_s and tok + chunk <= steps_total:
+            _, S0, tail0 = oracle.run(shape, S0, tail0, inp.w, inp.x[tok:tok + chunk, 0], inp.a[tok:tok + chunk, 0],
+                                      inp.b[tok:tok + chunk, 0])
+            tok += chunk
+        el = time.time() - t0
+        cpu = {"value": per_step * tok / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{tok} chained decode steps of the same batch-1 27B-class layer (all 48 heads, fp64 "
+                         f"scalar C), {el:.1f} s on one host core; tokens/s {tok / el:.1f}"}
+
+    # ---------------------------------------------------------------- the line
+    best_ms = cold_ms if graph_ms is None else min(cold_ms, graph_ms)
+    launch = "eager" if graph_ms is None or cold_ms <= graph_ms else "hipGraph"
+    value = per_step * K / best_ms / 1e6
+    roof = None
+    if kern is not None:
+        us = min(kern["us_per_launch_graph"], kern["us_per_launch_eager"])
+        ach = dec_b / us / 1e3
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_kernel<128,1>",
+                "bytes_per_launch": dec_b, "us_per_launch": round(us, 3)}
+    line = {
+        "metric": "GDN state GB/s & tokens/s per layer (decode, 32-node tree, prefill); % roofline",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(best_ms / K, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "tokens_per_s_per_layer": round(K / best_ms * 1e3, 1),
+        "config": {"workload": "decode_b1_27b_layer_4096_steps", "batch": 1, **SHAPE_DESC,
+                   "state_bytes": 3_145_728, "act": "bf16", "state_buffers_rotated": R, "launch": launch,
+                   "bytes_per_step": per_step},
+        "roofline": roof, "cpu_baseline": cpu, "rows": {k: _round(v) for k, v in res.items()},
+        "input_gen_s": round(gen_s, 1),
+    }
+    if args.details:
+        with open(args.details, "w") as f:
+            json.dump(line, f, indent=1)
+    print(json.dumps(line))
+
+
+def prefill_flops(T, shape):
+    """Algorithmic flops of the chunked form at chunk 64 (per chunk: K.K^T and Q.K^T per
+    q/k head; T.bV, T.bgK, P.W, Wk.S0^T, gQ.S0^T, W^T.K~ and the triangular solve per value head)."""
+    Cc, D = 64, shape.head_k_dim
+    nchunks = (T + Cc - 1) // Cc
+    per_qk = 2 * (2 * Cc * Cc * D)
+    per_v = 3 * (2 * Cc * Cc * D) + 3 * (2 * Cc * D * D) + Cc ** 3 // 3
+    return nchunks * (shape.num_k_heads * per_qk + shape.num_v_heads * per_v)
+
+
+def _round(v):
+    if isinstance(v, dict):
+        return {k: _round(x) for k, x in v.items()}
+    if isinstance(v, float):
+        return round(v, 4)
+    return v
+
+
+if __name__ == "__main__":
+    main()
