@@ -176,7 +176,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, float* state, void* conv_tail,
     gdn_status st = check_dims(d, g);
     if (st == GDN_OK)
         st = ptrs_ok({state, conv_tail, conv_w, x, a, b, o});
-    if (st == GDN_OK && T < 1)
+    if (st == GDN_OK && (T < 1 || g.D != 128 || g.Hv / g.Hk > 8))
         st = GDN_ERR_SHAPE;
     if (st == GDN_OK && static_cast<int64_t>(g.B) * T * g.C >= (1ll << 40))
         st = GDN_ERR_SHAPE;

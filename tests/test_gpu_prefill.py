@@ -1,0 +1,180 @@
+"""GPU chunked prefill against the sequential CPU oracle.
+
+Tolerance: the benchmark spec's bound for bf16-input chunked prefill, max relative
+error 2e-3, normwise per tensor (o over the checked tokens, final state).  The
+conv tail is data movement and must match exactly.  A prefill split at a chunk
+boundary must equal the unsplit prefill bit for bit (the CPU page's bitwise
+streaming state carry), and decode must continue from a prefilled state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from gdn_inputs import QWEN27B_LAYER, LayerShape
+from tests.conftest import normwise
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+SMALL = LayerShape(2, 6, 128, 128, 4, "bf16")
+
+
+def gpu_prefill(inp, T=None, S=None, tail=None, x_off=0):
+    """Run the library's prefill over tokens [x_off, x_off + T) of inp; returns (o, S, tail) on device."""
+    import gated_deltanet_decode_amd as gdn
+    from tests.gpu_util import act_to_dev, dims_of, f32_to_dev
+    shape, B = inp.shape, inp.batch
+    T = inp.steps - x_off if T is None else T
+    d = dims_of(shape, B)
+    S = f32_to_dev(inp.state) if S is None else S
+    tail = act_to_dev(inp.tail) if tail is None else tail
+    # the generator lays tokens out [T][B]; the call wants [B][T]
+    x = act_to_dev(np.ascontiguousarray(np.swapaxes(inp.x[x_off:x_off + T], 0, 1)))
+    a = f32_to_dev(np.swapaxes(inp.a[x_off:x_off + T], 0, 1))
+    b = f32_to_dev(np.swapaxes(inp.b[x_off:x_off + T], 0, 1))
+    w = act_to_dev(inp.w)
+    o = torch.full((B, T, shape.num_v_heads, shape.head_v_dim), float("nan"), device="cuda")
+    ws = torch.empty(max(gdn.prefill_workspace_bytes(d, T), 16), dtype=torch.uint8, device="cuda")
+    gdn.prefill_chunked(d, S, tail, w, x, a, b, o, ws)
+    torch.cuda.synchronize()
+    return o, S, tail
+
+
+def check_against_oracle(inp, o, S, tail, seqs=(0,), h_range=None, t_check=None):
+    from tests.gpu_util import act_to_host
+    shape = inp.shape
+    lo, hi = (0, shape.num_v_heads) if h_range is None else h_range
+    og, Sg, tg = o.cpu().numpy(), S.cpu().numpy(), act_to_host(tail)
+    for s in seqs:
+        o_r, S_r, t_r = oracle.run(shape, inp.state[s], inp.tail[s], inp.w, inp.x[:, s], inp.a[:, s], inp.b[:, s],
+                                   h_range=h_range)
+        tc = o_r.shape[0] if t_check is None else t_check
+        err_o = normwise(og[s, :tc, lo:hi], o_r[:tc, lo:hi])
+        err_s = normwise(Sg[s, lo:hi], S_r[lo:hi])
+        assert err_o < TOL, f"seq {s}: o error {err_o:.3e}"
+        assert err_s < TOL, f"seq {s}: state error {err_s:.3e}"
+        assert np.array_equal(oracle.f64(tg[s]), t_r), f"seq {s}: conv tail differs"
+        assert np.all(np.isfinite(og[s, :tc, lo:hi]))
+    return err_o, err_s
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 300])
+def test_small_shape_fresh_prompt(T):
+    inp = gi.prefill_inputs(70 + T, SMALL, T)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail)
+
+
+@pytest.mark.parametrize("T", [3, 200])
+def test_small_shape_continuation_from_random_state(T):
+    inp = gi.prefill_inputs(90 + T, SMALL, T, state_sigma=0.1, tail_random=True)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail)
+
+
+def test_27b_layer_all_heads():
+    inp = gi.prefill_inputs(4, QWEN27B_LAYER, 333, state_sigma=0.1, tail_random=True)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail)
+
+
+def test_batched_prompts():
+    inp = gi.prefill_inputs(5, SMALL, 150, batch=3, state_sigma=0.1, tail_random=True)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail, seqs=(0, 1, 2))
+
+
+def test_crosses_segment_boundary():
+    """2,048-token segments: a prompt of 2,200 tokens spans two launches pairs."""
+    inp = gi.prefill_inputs(6, SMALL, 2200, state_sigma=0.1, tail_random=True)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail)
+
+
+def test_27b_layer_32768_tokens():
+    """The long-prompt workload: T = 32,768 from a fresh state.  o is checked on the
+    first 2,048 tokens for every head; the final state for q/k heads 0 and 9
+    (value heads 0-2 and 27-29) against the oracle over all 32,768 tokens."""
+    from tests.gpu_util import act_to_host
+    T = 32768
+    inp = gi.prefill_inputs(4, QWEN27B_LAYER, T)
+    o, S, tail = gpu_prefill(inp)
+    og = o[0, :2048].cpu().numpy()
+    Sg = S.cpu().numpy()[0]
+    tg = act_to_host(tail)[0]
+    o_r, _, _ = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:2048, 0], inp.a[:2048, 0],
+                           inp.b[:2048, 0])
+    err = normwise(og, o_r)
+    assert err < TOL, f"o[0:2048] error {err:.3e}"
+    for hr in ((0, 3), (27, 30)):
+        _, S_r, t_r = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:, 0], inp.a[:, 0],
+                                 inp.b[:, 0], h_range=hr, want_o=False)
+        err = normwise(Sg[hr[0]:hr[1]], S_r[hr[0]:hr[1]])
+        assert err < TOL, f"final state heads {hr}: error {err:.3e}"
+        assert np.array_equal(oracle.f64(tg), t_r)
+    assert torch.isfinite(o).all()
+
+
+@pytest.mark.parametrize("split", [64, 128, 2048])
+def test_split_at_chunk_boundary_is_bitwise(split):
+    inp = gi.prefill_inputs(7, SMALL, 2200, state_sigma=0.1, tail_random=True)
+    o1, S1, t1 = gpu_prefill(inp)
+    oa, Sa, ta = gpu_prefill(inp, T=split)
+    ob, Sb, tb = gpu_prefill(inp, T=2200 - split, S=Sa, tail=ta, x_off=split)
+    assert torch.equal(S1.view(torch.int32), Sb.view(torch.int32))
+    assert torch.equal(t1, tb)
+    assert torch.equal(o1[:, :split].view(torch.int32), oa.view(torch.int32))
+    assert torch.equal(o1[:, split:].view(torch.int32), ob.view(torch.int32))
+
+
+def test_decode_continues_from_prefill():
+    import gated_deltanet_decode_amd as gdn
+    from tests.gpu_util import act_to_dev, dims_of, f32_to_dev
+    T, steps = 200, 8
+    inp = gi.prefill_inputs(8, SMALL, T + steps, state_sigma=0.1, tail_random=True)
+    _, S, tail = gpu_prefill(inp, T=T)
+    d = dims_of(SMALL, 1)
+    w = act_to_dev(inp.w)
+    y = torch.empty(1, SMALL.conv_channels, device="cuda")
+    o = torch.empty(steps, 1, 6, 128, device="cuda")
+    for j in range(steps):
+        t = T + j
+        gdn.conv_update(d, act_to_dev(inp.x[t]), tail, w, y)
+        gdn.decode_step(d, S, y, f32_to_dev(inp.a[t]), f32_to_dev(inp.b[t]), o[j])
+    torch.cuda.synchronize()
+    o_r, S_r, _ = oracle.run(SMALL, inp.state[0], inp.tail[0], inp.w, inp.x[:, 0], inp.a[:, 0], inp.b[:, 0])
+    assert normwise(o.cpu().numpy()[:, 0], o_r[T:]) < TOL
+    assert normwise(S.cpu().numpy()[0], S_r) < TOL
+
+
+def test_deterministic():
+    inp = gi.prefill_inputs(9, SMALL, 500, state_sigma=0.1, tail_random=True)
+    r1 = gpu_prefill(inp)
+    r2 = gpu_prefill(inp)
+    for u, v in zip(r1, r2):
+        assert torch.equal(u.view(torch.int32) if u.dtype == torch.float32 else u, v.view(torch.int32) if v.dtype == torch.float32 else v)
+
+
+def test_refusals():
+    import gated_deltanet_decode_amd as gdn
+    from tests.gpu_util import dims_of
+    d = dims_of(SMALL, 1)
+    T = 100
+    S = torch.zeros(6, 128, 128, device="cuda")
+    tail = torch.zeros(SMALL.conv_channels, 4, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(SMALL.conv_channels, 4, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(T, SMALL.conv_channels, dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros(T, 6, device="cuda")
+    o = torch.zeros(T, 6, 128, device="cuda")
+    small_ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        gdn.prefill_chunked(d, S, tail, w, x, a, a, o, small_ws)
+    with pytest.raises(gdn.GdnError) as e:
+        gdn._check(gdn._lib.gdn_prefill_chunked(gdn.C.byref(d), S.data_ptr(), tail.data_ptr(), w.data_ptr(), T,
+                                                x.data_ptr(), a.data_ptr(), a.data_ptr(), o.data_ptr(),
+                                                small_ws.data_ptr(), 1024, None), "prefill")
+    assert e.value.status == 6
+    d32 = gdn.dims(1, 4, 4, 32, 32, 4, "f32")
+    assert gdn.prefill_workspace_bytes(d32, T) == 0
