@@ -7,24 +7,30 @@
 // G_t the inclusive cumulative log-decay inside the chunk (G_t = sum log
 // alpha), the recurrence folds into (derivation: the chunk-form test)
 //   A    = strict-lower( beta_i e^{G_i - G_j} k_i.k_j ),   T = (I + A)^-1
-//   U    = T (beta (.) (V - e^G (.) K S0^T))
+//   U    = T (beta (.) V) - T (beta e^G (.) K) S0^T  =  U~ - W~ S0^T
 //   O    = s ( e^G (.) Q S0^T + P U ),   P = lower-incl( e^{G_i - G_j} q_i.k_j )
 //   S_n  = e^{G_n} S0 + U^T (e^{G_n - G} (.) K)
-// Only differences G_i - G_j with i >= j are exponentiated.
+// Only differences G_i - G_j with i >= j are exponentiated, so nothing
+// overflows however strong the decay.
 //
-// Work split for MI355X:
-//   prep (fully parallel, one workgroup per (sequence, q/k head, chunk)):
-//     conv + SiLU of the head's q, k and its G value heads' channels, q/k L2
-//     norm, gates and G; K K^T and Q K^T on MFMA (fp16 in, fp32 out), then per
-//     value head A, the blocked inverse T in fp32 and P; operands are written
-//     as fp16 to a workspace that holds one segment of the prompt.
-//   scan (sequential over chunks, one workgroup per (sequence, value head,
-//     16-row slice of the state)): the state-dependent products only, all on
-//     MFMA 16x16x32 fp16 with fp32 accumulation; the state slice stays in
-//     registers in fp32 across chunks.  Workgroups of one q/k group sit on one
-//     XCD so they share its L2 for the group's q/k operands.
-// Segments of 2,048 tokens bound the workspace (a few tens of MB, independent
-// of the prompt length) and keep it small enough for the Infinity Cache.
+// Work split for MI355X, per segment of at most 2,048 tokens:
+//   conv  (parallel over 16-token blocks x q/k heads): conv + SiLU of the
+//         q/k head's channels and of its value heads' channels, q/k L2 norm;
+//         writes fp16 q^, k^, k^ transposed per chunk and v transposed per
+//         chunk.  Small LDS, many waves per CU.
+//   tri   (parallel over value heads x chunks): gates and G, K K^T and Q K^T
+//         on MFMA, A, the blocked inverse T in fp32 (16x16 diagonal blocks by
+//         substitution, off-diagonal blocks by block products), then
+//         U~ = T (beta V) and W~ = T (beta e^G K) on MFMA, and P.
+//   scan  (sequential over chunks; one workgroup per (sequence, value head,
+//         16-row slice of the state)): Z = W~ S0^T and Y = Q S0^T, U = U~ - Z,
+//         O = s (e^G Y + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K): fourteen
+//         16x16x32 fp16 MFMAs and two barriers per chunk, with the next
+//         chunk's operands loaded while the current one computes.  The state
+//         slice stays in registers in fp32.  Workgroups of one q/k head sit on
+//         one XCD and share its L2.
+// The workspace holds one segment (about 114 MB at the 27B-class shape),
+// whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
 
 #include "gdn_core.hpp"
@@ -39,146 +45,207 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int D = 128;       // head width handled by the prefill kernels
 constexpr int CH = 64;       // chunk length
 constexpr int SEG = 2048;    // tokens per segment
+constexpr int TB = 16;       // tokens per conv workgroup
 constexpr int DS = 16;       // state rows per scan workgroup
 constexpr int NS = D / DS;   // scan workgroups per value head
-constexpr int QKP = D + 8;   // fp16 pitch of a q^/k^ row in LDS
 constexpr int MP = CH + 1;   // fp32 pitch of a 64x64 matrix row in LDS
-constexpr int MAXG = 8;      // value heads per q/k head handled by one prep workgroup
+constexpr int HP = CH + 8;   // fp16 pitch of a 64-token row in LDS
 constexpr float kScale = Scale<D>::value;
 
-// Workspace of one segment; SP = token pitch (segment length rounded to 64).
-//   q, k  fp16 [B][Hk][SP][D]      normalised q^, k^ (zero past the prompt)
-//   kt    fp16 [B][Hk][SP/64][D][64]  k^ transposed per chunk
-//   v     fp16 [B][Hv][SP][D]
-//   G     f32  [B][Hv][SP]          inclusive cumulative log-decay within the chunk
-//   beta  f32  [B][Hv][SP]
-//   T, P  fp16 [B][Hv][SP/64][64][64]
+// Workspace of one segment; SP = token pitch (segment length rounded to 64),
+// NC = SP / 64 chunks.
+//   q, k  fp16 [B][Hk][SP][D]        normalised q^, k^ (zero past the prompt)
+//   kt    fp16 [B][Hk][NC][D][64]    k^ transposed per chunk
+//   vt    fp16 [B][Hv][NC][D][64]    v transposed per chunk
+//   ut    fp16 [B][Hv][NC][D][64]    U~ = T (beta V), transposed per chunk
+//   wt    fp16 [B][Hv][SP][D]        W~ = T (beta e^G K)
+//   P     fp16 [B][Hv][NC][64][64]
+//   eg    f32  [B][Hv][SP]           e^{G_t}
+//   egd   f32  [B][Hv][SP]           e^{G_last - G_t}
 struct Ws {
-    _Float16 *q, *k, *kt, *v;
-    float *G, *beta;
-    _Float16 *T, *P;
+    _Float16 *q, *k, *kt, *vt, *ut, *wt, *P;
+    float *eg, *egd;
 };
 
 inline size_t seg_pitch(int T) { return static_cast<size_t>(T >= SEG ? SEG : (T + CH - 1) / CH * CH); }
 
 inline size_t ws_bytes(int B, int Hk, int Hv, size_t SP) {
-    const size_t per_tok = 3ull * Hk * D * 2 + static_cast<size_t>(Hv) * D * 2 + Hv * 8ull + Hv * 2ull * CH * 2;
-    return static_cast<size_t>(B) * SP * per_tok + 256 * 8;
+    const size_t per_tok = 3ull * Hk * D * 2 + 3ull * Hv * D * 2 + Hv * CH * 2ull + Hv * 8ull;
+    return static_cast<size_t>(B) * SP * per_tok + 256 * 10;
 }
 
 inline Ws carve(void* base, int B, int Hk, int Hv, size_t SP) {
     auto align = [](uintptr_t p) { return (p + 255) & ~static_cast<uintptr_t>(255); };
     uintptr_t p = align(reinterpret_cast<uintptr_t>(base));
+    const size_t nk = static_cast<size_t>(B) * Hk * SP * D, nv = static_cast<size_t>(B) * Hv * SP * D;
+    const size_t nm = static_cast<size_t>(B) * Hv * SP * CH, ng = static_cast<size_t>(B) * Hv * SP;
     Ws w;
-    const size_t nqk = static_cast<size_t>(B) * Hk * SP * D, nv = static_cast<size_t>(B) * Hv * SP * D;
-    const size_t ng = static_cast<size_t>(B) * Hv * SP, nm = static_cast<size_t>(B) * Hv * SP * CH;
-    w.q = reinterpret_cast<_Float16*>(p); p = align(p + nqk * 2);
-    w.k = reinterpret_cast<_Float16*>(p); p = align(p + nqk * 2);
-    w.kt = reinterpret_cast<_Float16*>(p); p = align(p + nqk * 2);
-    w.v = reinterpret_cast<_Float16*>(p); p = align(p + nv * 2);
-    w.G = reinterpret_cast<float*>(p); p = align(p + ng * 4);
-    w.beta = reinterpret_cast<float*>(p); p = align(p + ng * 4);
-    w.T = reinterpret_cast<_Float16*>(p); p = align(p + nm * 2);
-    w.P = reinterpret_cast<_Float16*>(p);
+    auto take16 = [&](size_t n) { _Float16* r = reinterpret_cast<_Float16*>(p); p = align(p + n * 2); return r; };
+    auto take32 = [&](size_t n) { float* r = reinterpret_cast<float*>(p); p = align(p + n * 4); return r; };
+    w.q = take16(nk);
+    w.k = take16(nk);
+    w.kt = take16(nk);
+    w.vt = take16(nv);
+    w.ut = take16(nv);
+    w.wt = take16(nv);
+    w.P = take16(nm);
+    w.eg = take32(ng);
+    w.egd = take32(ng);
     return w;
 }
 
 __device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ h8 ld8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
+__device__ __forceinline__ f4 zero4() { return f4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// ------------------------------------------------------------ prep
-
-struct alignas(16) PrepSmem {
-    float yqk[CH / 2][2 * D];      // conv output of q|k for half a chunk (fp32, before the norm)
-    _Float16 qh[CH][QKP];          // q^ (fp16)
-    _Float16 kh[CH][QKP];          // k^ (fp16)
-    float kk[CH][MP];              // K K^T (lower tiles)
-    float qk[CH][MP];              // Q K^T (lower tiles)
-    float A[CH][MP];               // A of one value head
-    float T[CH][MP];               // its inverse (I + A)^-1
-    float tmp[3][16][17];          // block products
-    float G[MAXG][CH];
-    float beta[MAXG][CH];
-};
+// ------------------------------------------------------------ conv + norm
 
 template <typename Act>
-__global__ __launch_bounds__(256) void prep_kernel(const Act* __restrict__ x, const Act* __restrict__ tail,
-                                                   const Act* __restrict__ w, const float* __restrict__ a,
-                                                   const float* __restrict__ bg, Ws ws, int T, int seg0, int SP,
-                                                   int nch, int Hk, int Hv, int C) {
-    __shared__ PrepSmem sm;
-    const int cl = blockIdx.x % nch;
-    const int g = (blockIdx.x / nch) % Hk;
-    const int bq = blockIdx.x / (nch * Hk);
+__global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, const Act* __restrict__ tail,
+                                                   const Act* __restrict__ w, Ws ws, int T, int seg0, int SP,
+                                                   int nblk, int Hk, int Hv, int C) {
+    __shared__ float ys[TB][2 * D];                  // q~ | k~ of the block, fp32
+    __shared__ __align__(16) _Float16 khs[TB][D];    // k^ of the block, fp16
+    const int tb = blockIdx.x % nblk;
+    const int g = (blockIdx.x / nblk) % Hk;
+    const int bq = blockIdx.x / (nblk * Hk);
     const int G = Hv / Hk;
-    const int t_base = seg0 + cl * CH;           // first token of the chunk (prompt index)
-    const int n = min(CH, T - t_base);           // valid tokens in the chunk
-    const int s0 = cl * CH;                      // first token of the chunk (segment index)
+    const int NC = SP / CH;
+    const int t0 = seg0 + tb * TB;                   // prompt index of the block's first token
+    const int sl = tb * TB;                          // segment index of the same token
+    const int cl = sl / CH, co = sl % CH;            // its chunk and offset in the chunk
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const size_t xrow = static_cast<size_t>(C);
-    const Act* xb = x + static_cast<size_t>(bq) * T * xrow;
-    const Act* tb = tail + static_cast<size_t>(bq) * C * 4;
+    const Act* xb = x + static_cast<size_t>(bq) * T * C;
+    const Act* tbq = tail + static_cast<size_t>(bq) * C * 4;
     const int per_group = (2 + G) * D;
 
-    for (int half = 0; half < 2; ++half) {
-        // conv + SiLU: item = (channel of this group, 8 consecutive tokens)
-        for (int item = threadIdx.x; item < per_group * 4; item += blockDim.x) {
-            const int ch = item % per_group;
-            const int tg = item / per_group;
-            const int c = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
-            float wf[4];
-            Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
-            const int tau0 = half * (CH / 2) + tg * 8;  // chunk-local token of the first output
-            float hist[11];
+    for (int ch = threadIdx.x; ch < per_group; ch += blockDim.x) {
+        const int c = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
+        float wf[4];
+        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
+        float hist[TB + 3];
+        // unconditional loads from selected addresses: all of them in flight at once
 #pragma unroll
-            for (int m = 0; m < 11; ++m) {
-                const int t = t_base + tau0 + m - 3;
-                hist[m] = t < 0 ? widen(tb[static_cast<size_t>(c) * 4 + 4 + t])
-                                : (t < T ? widen(xb[static_cast<size_t>(t) * xrow + c]) : 0.0f);
-            }
+        for (int m = 0; m < TB + 3; ++m) {
+            const int t = t0 + m - 3;
+            const int tc = t < T ? t : T - 1;
+            const Act* src = t < 0 ? tbq + static_cast<size_t>(c) * 4 + 4 + t : xb + static_cast<size_t>(tc) * C + c;
+            const float v = widen(*src);
+            hist[m] = t < T ? v : 0.0f;
+        }
+        float yv[TB];
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+            yv[j] = (t0 + j < T) ? conv_silu(wf, &hist[j]) : 0.0f;
+        if (ch < 2 * D) {
+#pragma unroll
+            for (int j = 0; j < TB; ++j)
+                ys[j][ch] = yv[j];
+        } else {
+            const int h = G * g + (ch - 2 * D) / D;
+            const int d = (ch - 2 * D) % D;
+            h8 lo, hi;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int tau = tau0 + j;
-                const float yv = (tau < n) ? conv_silu(wf, &hist[j]) : 0.0f;
-                if (ch < 2 * D) {
-                    sm.yqk[tau - half * (CH / 2)][ch] = yv;
-                } else {
-                    const int h = G * g + (ch - 2 * D) / D;
-                    const int d = (ch - 2 * D) % D;
-                    ws.v[((static_cast<size_t>(bq) * Hv + h) * SP + s0 + tau) * D + d] = static_cast<_Float16>(yv);
-                }
+                lo[j] = static_cast<_Float16>(yv[j]);
+                hi[j] = static_cast<_Float16>(yv[8 + j]);
             }
+            _Float16* dst = ws.vt + (((static_cast<size_t>(bq) * Hv + h) * NC + cl) * D + d) * CH + co;
+            *reinterpret_cast<h8*>(dst) = lo;
+            *reinterpret_cast<h8*>(dst + 8) = hi;
         }
-        __syncthreads();
-        // L2 norm of each token's q and k (one wave per vector)
-        for (int vec = wave; vec < CH; vec += 4) {
-            const int tl = vec >> 1, which = vec & 1;
-            const float e0 = sm.yqk[tl][which * D + lane];
-            const float e1 = sm.yqk[tl][which * D + lane + kWave];
-            float ss = __builtin_fmaf(e1, e1, e0 * e0);
-            ss = group_sum<kWave>(ss);
-            const float r = 1.0f / sqrtf(ss + kEps);
-            const _Float16 h0 = static_cast<_Float16>(e0 * r), h1 = static_cast<_Float16>(e1 * r);
-            const int tau = half * (CH / 2) + tl;
-            _Float16* dst = which ? &sm.kh[tau][0] : &sm.qh[tau][0];
-            dst[lane] = h0;
-            dst[lane + kWave] = h1;
-            _Float16* gdst = (which ? ws.k : ws.q) + ((static_cast<size_t>(bq) * Hk + g) * SP + s0 + tau) * D;
-            gdst[lane] = h0;
-            gdst[lane + kWave] = h1;
-        }
-        __syncthreads();
     }
+    __syncthreads();
+    for (int vec = wave; vec < 2 * TB; vec += 4) {
+        const int tl = vec >> 1, which = vec & 1;
+        const float e0 = ys[tl][which * D + lane];
+        const float e1 = ys[tl][which * D + lane + kWave];
+        const float ss = group_sum<kWave>(__builtin_fmaf(e1, e1, e0 * e0));
+        const float r = 1.0f / sqrtf(ss + kEps);
+        const _Float16 h0 = static_cast<_Float16>(e0 * r), h1 = static_cast<_Float16>(e1 * r);
+        _Float16* gdst = (which ? ws.k : ws.q) + ((static_cast<size_t>(bq) * Hk + g) * SP + sl + tl) * D;
+        gdst[lane] = h0;
+        gdst[lane + kWave] = h1;
+        if (which) {
+            khs[tl][lane] = h0;
+            khs[tl][lane + kWave] = h1;
+        }
+    }
+    __syncthreads();
+    {
+        const int d = threadIdx.x >> 1, half = threadIdx.x & 1;
+        h8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = khs[8 * half + j][d];
+        *reinterpret_cast<h8*>(ws.kt + (((static_cast<size_t>(bq) * Hk + g) * NC + cl) * D + d) * CH + co + 8 * half) = v;
+    }
+}
 
-    // gates: one wave per value head, one lane per token; inclusive scan of log alpha
-    for (int hh = wave; hh < G; hh += 4) {
-        const int h = G * g + hh;
-        const bool valid = lane < n;
+// ------------------------------------------------------------ tri
+
+struct alignas(16) TriSmem {
+    float A[CH][MP];
+    float T[CH][MP];
+    float tmp[3][16][17];
+    float G[CH];
+    float beta[CH];
+    float bv[CH];    // beta_t            (scales V in U~)
+    float bk[CH];    // beta_t e^{G_t}    (scales K in W~)
+};
+
+__global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, const float* __restrict__ bg, Ws ws,
+                                                  int T, int seg0, int SP, int nch, int Hk, int Hv) {
+    __shared__ TriSmem sm;
+    const int cl = blockIdx.x % nch;
+    const int h = (blockIdx.x / nch) % Hv;
+    const int bq = blockIdx.x / (nch * Hv);
+    const int g = h / (Hv / Hk);
+    const int NC = SP / CH;
+    const int t_base = seg0 + cl * CH;
+    const int n = min(CH, T - t_base);
+    const int s0 = cl * CH;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane & 15, lq = lane >> 4;
+    const size_t hs = (static_cast<size_t>(bq) * Hv + h) * SP + s0;   // this head's token row base
+
+    // Gate inputs first, then every operand fragment this wave needs, so that
+    // waiting for the gates does not wait for the fragments.
+    float av = 0.0f, bv = 0.0f;
+    if (wave == 0 && lane < n) {
+        const size_t idx = (static_cast<size_t>(bq) * T + t_base + lane) * Hv + h;
+        av = a[idx];
+        bv = bg[idx];
+    }
+    // Every operand fragment this wave needs is requested up front.
+    //   K K^T / Q K^T: wave w computes row block w (tiles (w, J), J <= w).
+    //   U~ / W~: wave w computes column tiles 2w and 2w+1 for all token rows.
+    const _Float16* qg = ws.q + ((static_cast<size_t>(bq) * Hk + g) * SP + s0) * D;
+    const _Float16* kg = ws.k + ((static_cast<size_t>(bq) * Hk + g) * SP + s0) * D;
+    const _Float16* vth = ws.vt + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * D * CH;
+    const _Float16* ktg = ws.kt + ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * D * CH;
+    h8 qa[4], ka[4], kb[3][4], vb[2][2], kt[2][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        qa[s] = ld8(qg + static_cast<size_t>(16 * wave + lr) * D + 32 * s + 8 * lq);
+        ka[s] = ld8(kg + static_cast<size_t>(16 * wave + lr) * D + 32 * s + 8 * lq);
+#pragma unroll
+        for (int J = 0; J < 3; ++J)
+            kb[J][s] = ld8(kg + static_cast<size_t>(16 * (J < wave ? J : wave) + lr) * D + 32 * s + 8 * lq);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            vb[tt][s] = ld8(vth + static_cast<size_t>(16 * (2 * wave + tt) + lr) * CH + 32 * s + 8 * lq);
+            kt[tt][s] = ld8(ktg + static_cast<size_t>(16 * (2 * wave + tt) + lr) * CH + 32 * s + 8 * lq);
+        }
+
+    if (wave == 0) {
         float la = 0.0f, be = 0.0f;
-        if (valid) {
-            const size_t idx = (static_cast<size_t>(bq) * T + t_base + lane) * Hv + h;
-            const float av = a[idx], bv = bg[idx];
+        if (lane < n) {
             la = -(fmaxf(av, 0.0f) + log1pf(expf(-fabsf(av))));
             be = 1.0f / (1.0f + expf(-bv));
         }
@@ -188,109 +255,232 @@ __global__ __launch_bounds__(256) void prep_kernel(const Act* __restrict__ x, co
             if (lane >= off)
                 la += up;
         }
-        sm.G[hh][lane] = la;
-        sm.beta[hh][lane] = be;
-        const size_t gi = (static_cast<size_t>(bq) * Hv + h) * SP + s0 + lane;
-        ws.G[gi] = la;
-        ws.beta[gi] = be;
+        const float glast = __shfl(la, kWave - 1, kWave);
+        const float eg = expf(la);
+        sm.G[lane] = la;
+        sm.beta[lane] = be;
+        sm.bv[lane] = be;
+        sm.bk[lane] = be * eg;
+        ws.eg[hs + lane] = eg;
+        ws.egd[hs + lane] = expf(glast - la);
     }
+    __syncthreads();
 
-    // K K^T and Q K^T, lower 16x16 tiles, on MFMA
-    {
-        constexpr int ti[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-        constexpr int tj[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-        for (int job = wave; job < 20; job += 4) {
-            const int which = job / 10, I = ti[job % 10], J = tj[job % 10];
-            const _Float16(*arow)[QKP] = which ? sm.qh : sm.kh;
-            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // K K^T -> A and Q K^T -> P for row block w; the blocks right of the
+    // diagonal are zero in P and in T.
+    _Float16* Pm = ws.P + (((static_cast<size_t>(bq) * Hv + h) * NC + cl) * CH) * CH;
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s)
-                acc = mma(ld8(&arow[16 * I + (lane & 15)][32 * s + 8 * (lane >> 4)]),
-                          ld8(&sm.kh[16 * J + (lane & 15)][32 * s + 8 * (lane >> 4)]), acc);
-            float(*out)[MP] = which ? sm.qk : sm.kk;
+    for (int J = 0; J < 4; ++J) {
+        const int i0 = 16 * wave + 4 * lq, j = 16 * J + lr;
+        if (J <= wave) {
+            f4 kk = zero4(), qk = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out[16 * I + 4 * (lane >> 4) + r][16 * J + (lane & 15)] = acc[r];
-        }
-        // k^ transposed per chunk, for the state update's B operand
-        for (int item = threadIdx.x; item < D * (CH / 8); item += blockDim.x) {
-            const int d = item / (CH / 8), oct = item % (CH / 8);
-            h8 v;
+            for (int s = 0; s < 4; ++s) {
+                const h8 b = (J == wave) ? ka[s] : kb[J < 3 ? J : 0][s];
+                kk = mma(ka[s], b, kk);
+                qk = mma(qa[s], b, qk);
+            }
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = sm.kh[8 * oct + j][d];
-            *reinterpret_cast<h8*>(ws.kt + (((static_cast<size_t>(bq) * Hk + g) * (SP / CH) + cl) * D + d) * CH +
-                                   8 * oct) = v;
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + r;
+                const float dg = (i >= j) ? expf(sm.G[i] - sm.G[j]) : 0.0f;
+                Pm[i * CH + j] = static_cast<_Float16>(dg * qk[r]);
+                sm.A[i][j] = (i > j) ? sm.beta[i] * dg * kk[r] : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Pm[(i0 + r) * CH + j] = static_cast<_Float16>(0.0f);
+                sm.T[i0 + r][j] = 0.0f;
+            }
         }
     }
     __syncthreads();
 
-    const int nchp = SP / CH;
-    for (int hh = 0; hh < G; ++hh) {
-        const int h = G * g + hh;
-        const size_t mbase = ((static_cast<size_t>(bq) * Hv + h) * nchp + cl) * CH * CH;
-        for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) {
-            const int i = e / CH, j = e % CH;
-            const float dg = (i >= j) ? expf(sm.G[hh][i] - sm.G[hh][j]) : 0.0f;
-            sm.A[i][j] = (i > j) ? sm.beta[hh][i] * dg * sm.kk[i][j] : 0.0f;
-            ws.P[mbase + e] = static_cast<_Float16>((i >= j) ? dg * sm.qk[i][j] : 0.0f);
-        }
-        __syncthreads();
-        // diagonal 16x16 blocks of (I + A)^-1 by forward substitution, lane = column
-        if (lane < 16) {
-            const int o = 16 * wave, j = lane;
-            float X[16];
+    // diagonal 16x16 blocks of (I + A)^-1: wave 0, lane = (block, column)
+    if (wave == 0) {
+        const int o = 16 * lq, j = lr;
+        float X[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == j) ? 1.0f : 0.0f;
+        for (int i = 0; i < 16; ++i) {
+            float s = (i == j) ? 1.0f : 0.0f;
 #pragma unroll
-                for (int k = 0; k < i; ++k)
-                    s = __builtin_fmaf(-sm.A[o + i][o + k], X[k], s);
-                X[i] = s;
-                sm.T[o + i][o + j] = s;
-            }
+            for (int k = 0; k < i; ++k)
+                s = __builtin_fmaf(-sm.A[o + i][o + k], X[k], s);
+            X[i] = s;
+            sm.T[o + i][o + j] = s;
         }
-        __syncthreads();
-        // off-diagonal blocks, one block diagonal at a time:
-        //   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
-        for (int lvl = 1; lvl < 4; ++lvl) {
-            const int nb = 4 - lvl;  // blocks on this diagonal: (lvl + q, q)
-            for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) {
-                const int q = e / 256, r = (e / 16) % 16, c = e % 16;
-                const int I = lvl + q, J = q;
-                float s = 0.0f;
-                for (int K = J; K < I; ++K)
-                    for (int k = 0; k < 16; ++k)
-                        s = __builtin_fmaf(sm.A[16 * I + r][16 * K + k], sm.T[16 * K + k][16 * J + c], s);
-                sm.tmp[q][r][c] = s;
-            }
-            __syncthreads();
-            for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) {
-                const int q = e / 256, r = (e / 16) % 16, c = e % 16;
-                const int I = lvl + q, J = q;
-                float s = 0.0f;
+    }
+    __syncthreads();
+    // off-diagonal blocks, one block diagonal at a time: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
+    for (int lvl = 1; lvl < 4; ++lvl) {
+        const int nb = 4 - lvl;
+        for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) {
+            const int q = e / 256, r = (e / 16) % 16, c = e % 16;
+            const int I = lvl + q, J = q;
+            float s = 0.0f;
+            for (int K = J; K < I; ++K)
+#pragma unroll
                 for (int k = 0; k < 16; ++k)
-                    s = __builtin_fmaf(sm.T[16 * I + r][16 * I + k], sm.tmp[q][k][c], s);
-                sm.T[16 * I + r][16 * J + c] = -s;
-            }
-            __syncthreads();
-        }
-        for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) {
-            const int i = e / CH, j = e % CH;
-            ws.T[mbase + e] = static_cast<_Float16>((j / 16 <= i / 16) ? sm.T[i][j] : 0.0f);
+                    s = __builtin_fmaf(sm.A[16 * I + r][16 * K + k], sm.T[16 * K + k][16 * J + c], s);
+            sm.tmp[q][r][c] = s;
         }
         __syncthreads();
+        for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) {
+            const int q = e / 256, r = (e / 16) % 16, c = e % 16;
+            const int I = lvl + q, J = q;
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                s = __builtin_fmaf(sm.T[16 * I + r][16 * I + k], sm.tmp[q][k][c], s);
+            sm.T[16 * I + r][16 * J + c] = -s;
+        }
+        __syncthreads();
+    }
+
+    // U~ = T (beta V) and W~ = T (beta e^G K): wave w owns column tiles 2w, 2w+1
+    h8 vsc[2][2], ksc[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        float fv[8], fk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            fv[e] = sm.bv[32 * s + 8 * lq + e];
+            fk[e] = sm.bk[32 * s + 8 * lq + e];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                vsc[tt][s][e] = static_cast<_Float16>(static_cast<float>(vb[tt][s][e]) * fv[e]);
+                ksc[tt][s][e] = static_cast<_Float16>(static_cast<float>(kt[tt][s][e]) * fk[e]);
+            }
+    }
+    _Float16* uto = ws.ut + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * D * CH;
+    _Float16* wto = ws.wt + hs * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        h8 tf[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tf[s][e] = static_cast<_Float16>(sm.T[16 * m + lr][32 * s + 8 * lq + e]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            f4 u = zero4(), wv = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u = mma(tf[s], vsc[tt][s], u);
+                wv = mma(tf[s], ksc[tt][s], wv);
+            }
+            const int d = 16 * (2 * wave + tt) + lr;
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            h4 uh;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uh[r] = static_cast<_Float16>(u[r]);
+                wto[static_cast<size_t>(16 * m + 4 * lq + r) * D + d] = static_cast<_Float16>(wv[r]);
+            }
+            *reinterpret_cast<h4*>(uto + static_cast<size_t>(d) * CH + 16 * m + 4 * lq) = uh;
+        }
     }
 }
 
 // ------------------------------------------------------------ scan
 
 struct alignas(16) ScanSmem {
-    _Float16 s0[DS][QKP];   // S0 slice, fp16, [row][key]
-    _Float16 rhsT[DS][CH + 8];
-    _Float16 ut[DS][CH + 8];
-    _Float16 utd[DS][CH + 8];
+    _Float16 s0[DS][D + 8];   // S0 slice, fp16, [row][key]
+    _Float16 ut[DS][HP];      // U^T
+    _Float16 utd[DS][HP];     // U^T scaled by e^{G_last - G}
 };
+
+// Operands of one chunk for one lane.  Kept in their storage types until used,
+// so that waiting for one chunk's loads never waits for the next chunk's.
+struct ScanOps {
+    h8 wf[4], qf[4], pf[2], kf[2][2];
+    uint2 u;       // four fp16 U~ values
+    f4 eg, egd;
+    float eglast;
+};
+
+struct ScanCtx {
+    size_t gbase, hbase, pbase, ktbase, utbase;
+    int wave, lr, lq, row0;
+};
+
+__device__ __forceinline__ void scan_load(ScanOps& op, const Ws& ws, const ScanCtx& c, int cl) {
+    const int s0 = cl * CH;
+    const size_t trow = static_cast<size_t>(s0 + 16 * c.wave + c.lr);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        op.wf[s] = ld8(ws.wt + (c.hbase + trow) * D + 32 * s + 8 * c.lq);
+        op.qf[s] = ld8(ws.q + (c.gbase + trow) * D + 32 * s + 8 * c.lq);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        op.pf[s] = ld8(ws.P + ((c.pbase + cl) * CH + 16 * c.wave + c.lr) * CH + 32 * s + 8 * c.lq);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+            op.kf[tt][s] = ld8(ws.kt + ((c.ktbase + cl) * D + 16 * (2 * c.wave + tt) + c.lr) * CH + 32 * s + 8 * c.lq);
+    }
+    op.u = *reinterpret_cast<const uint2*>(ws.ut + ((c.utbase + cl) * D + c.row0 + c.lr) * CH + 16 * c.wave + 4 * c.lq);
+    op.eg = *reinterpret_cast<const f4*>(ws.eg + c.hbase + s0 + 16 * c.wave + 4 * c.lq);
+    op.egd = *reinterpret_cast<const f4*>(ws.egd + c.hbase + s0 + 16 * c.wave + 4 * c.lq);
+    op.eglast = ws.eg[c.hbase + s0 + CH - 1];
+}
+
+// One chunk: orow points at the chunk's first token row of o for this head and
+// slice; n is the number of valid tokens (only a final partial chunk is MASKED).
+template <bool MASKED>
+__device__ __forceinline__ void scan_step(const ScanOps& op, ScanSmem& sm, f4 (&sacc)[2], const ScanCtx& c,
+                                          float* __restrict__ orow, int n, size_t ostride) {
+    const int wave = c.wave, lr = c.lr, lq = c.lq;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sm.s0[4 * lq + r][16 * (2 * wave + tt) + lr] = static_cast<_Float16>(sacc[tt][r]);
+    __syncthreads();
+
+    f4 Z = zero4(), Y = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const h8 bs = ld8(&sm.s0[lr][32 * s + 8 * lq]);
+        Z = mma(op.wf[s], bs, Z);
+        Y = mma(op.qf[s], bs, Y);
+    }
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 uh = __builtin_bit_cast(h4, op.u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lq + r;
+        const float U = static_cast<float>(uh[r]) - Z[r];
+        sm.ut[lr][t] = static_cast<_Float16>(U);
+        sm.utd[lr][t] = static_cast<_Float16>(U * op.egd[r]);
+    }
+    __syncthreads();
+
+    f4 PU = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        PU = mma(op.pf[s], ld8(&sm.ut[lr][32 * s + 8 * lq]), PU);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lq + r;
+        if (!MASKED || t < n)
+            orow[static_cast<size_t>(t) * ostride + lr] = kScale * __builtin_fmaf(op.eg[r], Y[r], PU[r]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sacc[tt][r] *= op.eglast;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            sacc[tt] = mma(ld8(&sm.utd[lr][32 * s + 8 * lq]), op.kf[tt][s], sacc[tt]);
+    }
+}
 
 __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
                                                    int seg0, int SP, int nch, int B, int Hk, int Hv) {
@@ -304,9 +494,17 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
     const int rem = r8 % (G * NS);
     const int bq = gu / Hk, g = gu % Hk, h = G * g + rem / NS, row0 = (rem % NS) * DS;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int lr = lane & 15, lq = lane >> 4;
-    const int nchp = SP / CH;
+    const int NC = SP / CH;
+    ScanCtx c;
+    c.wave = threadIdx.x / kWave;
+    c.lr = lane & 15;
+    c.lq = lane >> 4;
+    c.row0 = row0;
+    c.gbase = (static_cast<size_t>(bq) * Hk + g) * SP;   // token rows of q/k head g
+    c.hbase = (static_cast<size_t>(bq) * Hv + h) * SP;   // token rows of value head h
+    c.pbase = (static_cast<size_t>(bq) * Hv + h) * NC;
+    c.utbase = c.pbase;
+    c.ktbase = (static_cast<size_t>(bq) * Hk + g) * NC;
 
     float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0) * D;
     f4 sacc[2];
@@ -314,115 +512,38 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            sacc[tt][r] = Sh[(4 * lq + r) * D + 16 * (2 * wave + tt) + lr];
+            sacc[tt][r] = Sh[(4 * c.lq + r) * D + 16 * (2 * c.wave + tt) + c.lr];
 
-    const _Float16* qg = ws.q + (static_cast<size_t>(bq) * Hk + g) * SP * D;
-    const _Float16* kg = ws.k + (static_cast<size_t>(bq) * Hk + g) * SP * D;
-    const _Float16* ktg = ws.kt + (static_cast<size_t>(bq) * Hk + g) * nchp * D * CH;
-    const _Float16* vh = ws.v + (static_cast<size_t>(bq) * Hv + h) * SP * D;
-    const float* Gh = ws.G + (static_cast<size_t>(bq) * Hv + h) * SP;
-    const float* bh = ws.beta + (static_cast<size_t>(bq) * Hv + h) * SP;
-    const _Float16* Th = ws.T + (static_cast<size_t>(bq) * Hv + h) * nchp * CH * CH;
-    const _Float16* Ph = ws.P + (static_cast<size_t>(bq) * Hv + h) * nchp * CH * CH;
-
-    for (int cl = 0; cl < nch; ++cl) {
-        const int t_base = seg0 + cl * CH;
-        const int n = min(CH, T - t_base);
-        const int s0 = cl * CH;
-        const int trow = s0 + 16 * wave + lr;  // token row of this lane's A fragments
-        h8 kf[4], qf[4], tf[2], pf[2], ktf[2][2];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            kf[s] = ld8(kg + static_cast<size_t>(trow) * D + 32 * s + 8 * lq);
-            qf[s] = ld8(qg + static_cast<size_t>(trow) * D + 32 * s + 8 * lq);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            tf[s] = ld8(Th + (static_cast<size_t>(cl) * CH + 16 * wave + lr) * CH + 32 * s + 8 * lq);
-            pf[s] = ld8(Ph + (static_cast<size_t>(cl) * CH + 16 * wave + lr) * CH + 32 * s + 8 * lq);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-                ktf[tt][s] = ld8(ktg + (static_cast<size_t>(cl) * D + 16 * (2 * wave + tt) + lr) * CH + 32 * s + 8 * lq);
-        }
-        float vv[4], gv[4], bv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = s0 + 16 * wave + 4 * lq + r;
-            vv[r] = static_cast<float>(vh[static_cast<size_t>(t) * D + row0 + lr]);
-            gv[r] = Gh[t];
-            bv[r] = bh[t];
-        }
-        const float glast = Gh[s0 + CH - 1];
-
-        // S0 slice to LDS as fp16 [row][key]
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm.s0[4 * lq + r][16 * (2 * wave + tt) + lr] = static_cast<_Float16>(sacc[tt][r]);
-        __syncthreads();
-
-        // X = K S0^T and Y = Q S0^T for tokens 16*wave .. +15
-        f4 X = {0.0f, 0.0f, 0.0f, 0.0f}, Y = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const h8 bs = ld8(&sm.s0[lr][32 * s + 8 * lq]);
-            X = mma(kf[s], bs, X);
-            Y = mma(qf[s], bs, Y);
-        }
-        float eg[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            eg[r] = expf(gv[r]);
-            const float rhs = bv[r] * (vv[r] - eg[r] * X[r]);
-            sm.rhsT[lr][16 * wave + 4 * lq + r] = static_cast<_Float16>(rhs);
-        }
-        __syncthreads();
-
-        // U = T rhs
-        f4 U = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            U = mma(tf[s], ld8(&sm.rhsT[lr][32 * s + 8 * lq]), U);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + 4 * lq + r;
-            sm.ut[lr][t] = static_cast<_Float16>(U[r]);
-            sm.utd[lr][t] = static_cast<_Float16>(U[r] * expf(glast - gv[r]));
-        }
-        __syncthreads();
-
-        // O = s (e^G Y + P U)
-        f4 PU = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            PU = mma(pf[s], ld8(&sm.ut[lr][32 * s + 8 * lq]), PU);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + 4 * lq + r;
-            if (t < n)
-                o[((static_cast<size_t>(bq) * T + t_base + t) * Hv + h) * D + row0 + lr] =
-                    kScale * __builtin_fmaf(eg[r], Y[r], PU[r]);
-        }
-
-        // S <- e^{G_n} S + U^T (e^{G_n - G} K)
-        const float gl = expf(glast);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[tt][r] *= gl;
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                sacc[tt] = mma(ld8(&sm.utd[lr][32 * s + 8 * lq]), ktf[tt][s], sacc[tt]);
-        }
+    const size_t ostride = static_cast<size_t>(Hv) * D;
+    float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
+    // Full chunks run with two register stages: chunk cl computes from one while
+    // chunk cl+1 loads into the other.  Loads and stores in this loop are
+    // unconditional (the look-ahead index is clamped), so the compiler can wait
+    // for exactly the stage it needs.  A final partial chunk runs masked.
+    const int len = min(SEG, T - seg0);
+    const int nfull = len / CH, tailn = len % CH;
+    ScanOps opA, opB;
+    if (nfull > 0)
+        scan_load(opA, ws, c, 0);
+    int cl = 0;
+    for (; cl + 1 < nfull; cl += 2) {
+        scan_load(opB, ws, c, cl + 1);
+        scan_step<false>(opA, sm, sacc, c, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
+        scan_load(opA, ws, c, min(cl + 2, nch - 1));
+        scan_step<false>(opB, sm, sacc, c, obase + static_cast<size_t>(cl + 1) * CH * ostride, CH, ostride);
+    }
+    if (cl < nfull)
+        scan_step<false>(opA, sm, sacc, c, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
+    if (tailn > 0) {
+        scan_load(opA, ws, c, nfull);
+        scan_step<true>(opA, sm, sacc, c, obase + static_cast<size_t>(nfull) * CH * ostride, tailn, ostride);
     }
 
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            Sh[(4 * lq + r) * D + 16 * (2 * wave + tt) + lr] = sacc[tt][r];
+            Sh[(4 * c.lq + r) * D + 16 * (2 * c.wave + tt) + c.lr] = sacc[tt][r];
 }
 
 // ------------------------------------------------------------ tail
@@ -447,43 +568,48 @@ __global__ __launch_bounds__(256) void tail_kernel(const Act* __restrict__ x, Ac
 }  // namespace pf
 
 size_t prefill_workspace_bytes(const Geo& g, int T) {
-    if (g.D != pf::D || g.Hv / g.Hk > pf::MAXG)
+    if (g.D != pf::D || g.Hv / g.Hk > 8)
         return 0;
     return pf::ws_bytes(g.B, g.Hk, g.Hv, pf::seg_pitch(T));
 }
 
 hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int T, const void* x, const float* a,
                           const float* b, float* o, void* ws, hipStream_t s) {
-    if (g.D != pf::D || g.Hv / g.Hk > pf::MAXG)
+    if (g.D != pf::D || g.Hv / g.Hk > 8)
         return hipErrorNotSupported;
-    const size_t SP = pf::seg_pitch(T);
+    const int SP = static_cast<int>(pf::seg_pitch(T));
     const pf::Ws W = pf::carve(ws, g.B, g.Hk, g.Hv, SP);
     const int G = g.Hv / g.Hk;
     const int units = g.B * g.Hk;
     const int scan_grid = 8 * ((units + 7) / 8) * G * pf::NS;
+    const dim3 block(256);
     for (int seg0 = 0; seg0 < T; seg0 += pf::SEG) {
         const int len = std::min(pf::SEG, T - seg0);
         const int nch = (len + pf::CH - 1) / pf::CH;
-        const dim3 pgrid(static_cast<unsigned>(g.B * g.Hk * nch)), block(256);
+        const int nblk = nch * (pf::CH / pf::TB);
+        const dim3 cgrid(static_cast<unsigned>(g.B * g.Hk * nblk));
         if (g.bf16)
-            hipLaunchKernelGGL(pf::prep_kernel<uint16_t>, pgrid, block, 0, s, static_cast<const uint16_t*>(x),
-                               static_cast<const uint16_t*>(tail), static_cast<const uint16_t*>(w), a, b, W, T, seg0,
-                               static_cast<int>(SP), nch, g.Hk, g.Hv, g.C);
+            hipLaunchKernelGGL(pf::conv_kernel<uint16_t>, cgrid, block, 0, s, static_cast<const uint16_t*>(x),
+                               static_cast<const uint16_t*>(tail), static_cast<const uint16_t*>(w), W, T, seg0, SP,
+                               nblk, g.Hk, g.Hv, g.C);
         else
-            hipLaunchKernelGGL(pf::prep_kernel<float>, pgrid, block, 0, s, static_cast<const float*>(x),
-                               static_cast<const float*>(tail), static_cast<const float*>(w), a, b, W, T, seg0,
-                               static_cast<int>(SP), nch, g.Hk, g.Hv, g.C);
+            hipLaunchKernelGGL(pf::conv_kernel<float>, cgrid, block, 0, s, static_cast<const float*>(x),
+                               static_cast<const float*>(tail), static_cast<const float*>(w), W, T, seg0, SP, nblk,
+                               g.Hk, g.Hv, g.C);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
+        hipLaunchKernelGGL(pf::tri_kernel, dim3(static_cast<unsigned>(g.B * g.Hv * nch)), block, 0, s, a, b, W, T,
+                           seg0, SP, nch, g.Hk, g.Hv);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
         hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), block, 0, s, S, o, W, T, seg0,
-                           static_cast<int>(SP), nch, g.B, g.Hk, g.Hv);
-        e = hipGetLastError();
-        if (e != hipSuccess)
+                           SP, nch, g.B, g.Hk, g.Hv);
+        if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
     const int64_t total = static_cast<int64_t>(g.B) * g.C;
-    const dim3 tgrid(static_cast<unsigned>((total + 255) / 256)), block(256);
+    const dim3 tgrid(static_cast<unsigned>((total + 255) / 256));
     if (g.bf16)
         hipLaunchKernelGGL(pf::tail_kernel<uint16_t>, tgrid, block, 0, s, static_cast<const uint16_t*>(x),
                            static_cast<uint16_t*>(tail), T, g.C, total);

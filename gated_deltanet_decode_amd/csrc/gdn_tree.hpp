@@ -78,11 +78,14 @@ __device__ inline bool path_check_wave(int n, const int32_t* __restrict__ parent
 template <typename Act>
 __device__ __forceinline__ void node_window(const Act* __restrict__ x, const Act* __restrict__ tail, int C, int c,
                                             int node, int d, const int anc[3], float win[4]) {
+    // One unconditional load per tap, from a selected address, so all four
+    // loads are in flight together.
     win[3] = widen(x[static_cast<size_t>(node) * C + c]);
 #pragma unroll
     for (int k = 1; k <= 3; ++k) {
-        win[3 - k] = (k <= d - 1) ? widen(x[static_cast<size_t>(anc[k - 1]) * C + c])
-                                  : widen(tail[static_cast<size_t>(c) * 4 + (3 + d - k)]);
+        const Act* src = (k <= d - 1) ? x + static_cast<size_t>(anc[k - 1]) * C + c
+                                      : tail + static_cast<size_t>(c) * 4 + (3 + d - k);
+        win[3 - k] = widen(*src);
     }
 }
 

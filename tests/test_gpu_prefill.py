@@ -53,6 +53,7 @@ def check_against_oracle(inp, o, S, tail, seqs=(0,), h_range=None, t_check=None)
         tc = o_r.shape[0] if t_check is None else t_check
         err_o = normwise(og[s, :tc, lo:hi], o_r[:tc, lo:hi])
         err_s = normwise(Sg[s, lo:hi], S_r[lo:hi])
+        print(f"[prefill parity] T={o_r.shape[0]} seq {s}: o error {err_o:.3e}, state error {err_s:.3e}")
         assert err_o < TOL, f"seq {s}: o error {err_o:.3e}"
         assert err_s < TOL, f"seq {s}: state error {err_s:.3e}"
         assert np.array_equal(oracle.f64(tg[s]), t_r), f"seq {s}: conv tail differs"
@@ -107,11 +108,13 @@ def test_27b_layer_32768_tokens():
     o_r, _, _ = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:2048, 0], inp.a[:2048, 0],
                            inp.b[:2048, 0])
     err = normwise(og, o_r)
+    print(f"[prefill parity] T=32768: o[0:2048] error {err:.3e}")
     assert err < TOL, f"o[0:2048] error {err:.3e}"
     for hr in ((0, 3), (27, 30)):
         _, S_r, t_r = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:, 0], inp.a[:, 0],
                                  inp.b[:, 0], h_range=hr, want_o=False)
         err = normwise(Sg[hr[0]:hr[1]], S_r[hr[0]:hr[1]])
+        print(f"[prefill parity] T=32768: final state heads {hr} error {err:.3e}")
         assert err < TOL, f"final state heads {hr}: error {err:.3e}"
         assert np.array_equal(oracle.f64(tg), t_r)
     assert torch.isfinite(o).all()
