@@ -88,14 +88,34 @@ __device__ __forceinline__ void gates(float a, float b, float& alpha, float& bet
 
 // ------------------------------------------------------------ wave reductions
 
-// Butterfly sum over aligned groups of `Width` lanes.  Every lane of a group
-// ends with the same bits: at each step lane i adds the partner's value to its
-// own, and the partner adds the same two numbers the other way round.
+// Sum over aligned groups of `Width` lanes (4, 8, 16 or 64) with DPP lane
+// moves, which read a neighbour's register without going through LDS:
+//   xor 1 and xor 2 inside a quad, then the half-row mirror (quad q with quad
+//   q^1), then the row mirror (the two halves of a 16-lane row).
+// Each step adds two numbers that the partner lane adds in the other order,
+// so every lane of a group ends with the same bits.  For 64 lanes the four row
+// sums are read into scalar registers and added in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 template <int Width>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < Width; m <<= 1)
-        v += __shfl_xor(v, m, kWave);
+    static_assert(Width == 4 || Width == 8 || Width == 16 || Width == 64, "unsupported group width");
+    v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (Width >= 8)
+        v += dpp_move<0x141>(v);  // row_half_mirror
+    if constexpr (Width >= 16)
+        v += dpp_move<0x140>(v);  // row_mirror
+    if constexpr (Width == 64) {
+        const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+        const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+        v = (r0 + r1) + (r2 + r3);
+    }
     return v;
 }
 

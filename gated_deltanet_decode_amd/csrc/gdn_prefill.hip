@@ -24,11 +24,12 @@
 //         U~ = T (beta V) and W~ = T (beta e^G K) on MFMA, and P.
 //   scan  (sequential over chunks; one workgroup per (sequence, value head,
 //         16-row slice of the state)): Z = W~ S0^T and Y = Q S0^T, U = U~ - Z,
-//         O = s (e^G Y + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K): fourteen
-//         16x16x32 fp16 MFMAs and two barriers per chunk, with the next
-//         chunk's operands loaded while the current one computes.  The state
-//         slice stays in registers in fp32.  Workgroups of one q/k head sit on
-//         one XCD and share its L2.
+//         O = s (e^G Y + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K), all on
+//         16x16x32 fp16 MFMAs, two barriers per chunk.  Four waves carry the
+//         state (fp32, in registers across chunks); four more compute and store
+//         o off the state's critical path.  The next chunk's operands load while
+//         the current one computes.  Workgroups of one q/k head sit on one XCD
+//         and share its L2.
 // The workspace holds one segment (about 114 MB at the 27B-class shape),
 // whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
@@ -389,88 +390,93 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 
 // ------------------------------------------------------------ scan
 
+// The scan workgroup has two roles of four waves each.  State waves carry the
+// recurrence: Z = W~ S0^T, U = U~ - Z, S <- e^{G_n} S + U^T (e^{G_n - G} K).
+// Output waves compute Y = Q S0^T and P U and store o, in the state waves'
+// shadow: their stores never sit in front of a state wave's loads in the
+// in-order memory counter.  The roles meet at two barriers per chunk; S0 and
+// U^T live in LDS double-buffered by chunk parity.
 struct alignas(16) ScanSmem {
-    _Float16 s0[DS][D + 8];   // S0 slice, fp16, [row][key]
-    _Float16 ut[DS][HP];      // U^T
-    _Float16 utd[DS][HP];     // U^T scaled by e^{G_last - G}
+    _Float16 s0[2][DS][D + 8];   // S0 slice, fp16, [row][key]
+    _Float16 ut[2][DS][HP];      // U^T
+    _Float16 utd[DS][HP];        // U^T scaled by e^{G_last - G} (state waves only)
 };
 
-// Operands of one chunk for one lane.  Kept in their storage types until used,
-// so that waiting for one chunk's loads never waits for the next chunk's.
-struct ScanOps {
-    h8 wf[4], qf[4], pf[2], kf[2][2];
+struct StateOps {
+    h8 wf[4], kf[2][2];
     uint2 u;       // four fp16 U~ values
-    f4 eg, egd;
+    f4 egd;
     float eglast;
+};
+
+struct OutOps {
+    h8 qf[4], pf[2];
+    f4 eg;
 };
 
 struct ScanCtx {
     size_t gbase, hbase, pbase, ktbase, utbase;
-    int wave, lr, lq, row0;
+    int w, lr, lq, row0;   // w: this wave's index within its role
 };
 
-__device__ __forceinline__ void scan_load(ScanOps& op, const Ws& ws, const ScanCtx& c, int cl) {
+__device__ __forceinline__ void load_state(StateOps& op, const Ws& ws, const ScanCtx& c, int cl) {
     const int s0 = cl * CH;
-    const size_t trow = static_cast<size_t>(s0 + 16 * c.wave + c.lr);
+    const size_t trow = static_cast<size_t>(s0 + 16 * c.w + c.lr);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 4; ++s)
         op.wf[s] = ld8(ws.wt + (c.hbase + trow) * D + 32 * s + 8 * c.lq);
-        op.qf[s] = ld8(ws.q + (c.gbase + trow) * D + 32 * s + 8 * c.lq);
-    }
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        op.pf[s] = ld8(ws.P + ((c.pbase + cl) * CH + 16 * c.wave + c.lr) * CH + 32 * s + 8 * c.lq);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-            op.kf[tt][s] = ld8(ws.kt + ((c.ktbase + cl) * D + 16 * (2 * c.wave + tt) + c.lr) * CH + 32 * s + 8 * c.lq);
-    }
-    op.u = *reinterpret_cast<const uint2*>(ws.ut + ((c.utbase + cl) * D + c.row0 + c.lr) * CH + 16 * c.wave + 4 * c.lq);
-    op.eg = *reinterpret_cast<const f4*>(ws.eg + c.hbase + s0 + 16 * c.wave + 4 * c.lq);
-    op.egd = *reinterpret_cast<const f4*>(ws.egd + c.hbase + s0 + 16 * c.wave + 4 * c.lq);
+            op.kf[tt][s] = ld8(ws.kt + ((c.ktbase + cl) * D + 16 * (2 * c.w + tt) + c.lr) * CH + 32 * s + 8 * c.lq);
+    op.u = *reinterpret_cast<const uint2*>(ws.ut + ((c.utbase + cl) * D + c.row0 + c.lr) * CH + 16 * c.w + 4 * c.lq);
+    op.egd = *reinterpret_cast<const f4*>(ws.egd + c.hbase + s0 + 16 * c.w + 4 * c.lq);
     op.eglast = ws.eg[c.hbase + s0 + CH - 1];
 }
 
-// One chunk: orow points at the chunk's first token row of o for this head and
-// slice; n is the number of valid tokens (only a final partial chunk is MASKED).
-template <bool MASKED>
-__device__ __forceinline__ void scan_step(const ScanOps& op, ScanSmem& sm, f4 (&sacc)[2], const ScanCtx& c,
-                                          float* __restrict__ orow, int n, size_t ostride) {
-    const int wave = c.wave, lr = c.lr, lq = c.lq;
+__device__ __forceinline__ void load_out(OutOps& op, const Ws& ws, const ScanCtx& c, int cl) {
+    const int s0 = cl * CH;
+    const size_t trow = static_cast<size_t>(s0 + 16 * c.w + c.lr);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        op.qf[s] = ld8(ws.q + (c.gbase + trow) * D + 32 * s + 8 * c.lq);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        op.pf[s] = ld8(ws.P + ((c.pbase + cl) * CH + 16 * c.w + c.lr) * CH + 32 * s + 8 * c.lq);
+    op.eg = *reinterpret_cast<const f4*>(ws.eg + c.hbase + s0 + 16 * c.w + 4 * c.lq);
+}
+
+// x S0^T for one 16-token tile, keys split into two independent chains.
+__device__ __forceinline__ f4 times_s0(const h8 (&a)[4], const _Float16 (*s0)[D + 8], int lr, int lq) {
+    f4 z0 = zero4(), z1 = zero4();
+    z0 = mma(a[0], ld8(&s0[lr][8 * lq]), z0);
+    z1 = mma(a[2], ld8(&s0[lr][64 + 8 * lq]), z1);
+    z0 = mma(a[1], ld8(&s0[lr][32 + 8 * lq]), z0);
+    z1 = mma(a[3], ld8(&s0[lr][96 + 8 * lq]), z1);
+    return z0 + z1;
+}
+
+__device__ __forceinline__ void state_chunk(const StateOps& op, ScanSmem& sm, f4 (&sacc)[2], const ScanCtx& c,
+                                            int par) {
+    const int w = c.w, lr = c.lr, lq = c.lq;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            sm.s0[4 * lq + r][16 * (2 * wave + tt) + lr] = static_cast<_Float16>(sacc[tt][r]);
+            sm.s0[par][4 * lq + r][16 * (2 * w + tt) + lr] = static_cast<_Float16>(sacc[tt][r]);
     __syncthreads();
-
-    f4 Z = zero4(), Y = zero4();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const h8 bs = ld8(&sm.s0[lr][32 * s + 8 * lq]);
-        Z = mma(op.wf[s], bs, Z);
-        Y = mma(op.qf[s], bs, Y);
-    }
+    const f4 Z = times_s0(op.wf, sm.s0[par], lr, lq);
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     const h4 uh = __builtin_bit_cast(h4, op.u);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wave + 4 * lq + r;
+        const int t = 16 * w + 4 * lq + r;
         const float U = static_cast<float>(uh[r]) - Z[r];
-        sm.ut[lr][t] = static_cast<_Float16>(U);
+        sm.ut[par][lr][t] = static_cast<_Float16>(U);
         sm.utd[lr][t] = static_cast<_Float16>(U * op.egd[r]);
     }
     __syncthreads();
-
-    f4 PU = zero4();
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        PU = mma(op.pf[s], ld8(&sm.ut[lr][32 * s + 8 * lq]), PU);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wave + 4 * lq + r;
-        if (!MASKED || t < n)
-            orow[static_cast<size_t>(t) * ostride + lr] = kScale * __builtin_fmaf(op.eg[r], Y[r], PU[r]);
-    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -482,7 +488,28 @@ __device__ __forceinline__ void scan_step(const ScanOps& op, ScanSmem& sm, f4 (&
     }
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
+// orow points at the chunk's first token row of o for this head and slice; only
+// a final partial chunk is MASKED to its n valid tokens.
+template <bool MASKED>
+__device__ __forceinline__ void out_chunk(const OutOps& op, ScanSmem& sm, const ScanCtx& c, int par,
+                                          float* __restrict__ orow, int n, size_t ostride) {
+    const int w = c.w, lr = c.lr, lq = c.lq;
+    __syncthreads();
+    const f4 Y = times_s0(op.qf, sm.s0[par], lr, lq);
+    __syncthreads();
+    f4 PU = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        PU = mma(op.pf[s], ld8(&sm.ut[par][lr][32 * s + 8 * lq]), PU);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * lq + r;
+        if (!MASKED || t < n)
+            orow[static_cast<size_t>(t) * ostride + lr] = kScale * __builtin_fmaf(op.eg[r], Y[r], PU[r]);
+    }
+}
+
+__global__ __launch_bounds__(512, 4) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
                                                    int seg0, int SP, int nch, int B, int Hk, int Hv) {
     __shared__ ScanSmem sm;
     const int G = Hv / Hk;
@@ -494,9 +521,11 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
     const int rem = r8 % (G * NS);
     const int bq = gu / Hk, g = gu % Hk, h = G * g + rem / NS, row0 = (rem % NS) * DS;
     const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const bool state_role = wave < 4;
     const int NC = SP / CH;
     ScanCtx c;
-    c.wave = threadIdx.x / kWave;
+    c.w = wave & 3;
     c.lr = lane & 15;
     c.lq = lane >> 4;
     c.row0 = row0;
@@ -505,45 +534,66 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
     c.pbase = (static_cast<size_t>(bq) * Hv + h) * NC;
     c.utbase = c.pbase;
     c.ktbase = (static_cast<size_t>(bq) * Hk + g) * NC;
-
-    float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0) * D;
-    f4 sacc[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sacc[tt][r] = Sh[(4 * c.lq + r) * D + 16 * (2 * c.wave + tt) + c.lr];
-
-    const size_t ostride = static_cast<size_t>(Hv) * D;
-    float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
-    // Full chunks run with two register stages: chunk cl computes from one while
-    // chunk cl+1 loads into the other.  Loads and stores in this loop are
-    // unconditional (the look-ahead index is clamped), so the compiler can wait
-    // for exactly the stage it needs.  A final partial chunk runs masked.
     const int len = min(SEG, T - seg0);
     const int nfull = len / CH, tailn = len % CH;
-    ScanOps opA, opB;
-    if (nfull > 0)
-        scan_load(opA, ws, c, 0);
-    int cl = 0;
-    for (; cl + 1 < nfull; cl += 2) {
-        scan_load(opB, ws, c, cl + 1);
-        scan_step<false>(opA, sm, sacc, c, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
-        scan_load(opA, ws, c, min(cl + 2, nch - 1));
-        scan_step<false>(opB, sm, sacc, c, obase + static_cast<size_t>(cl + 1) * CH * ostride, CH, ostride);
-    }
-    if (cl < nfull)
-        scan_step<false>(opA, sm, sacc, c, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
-    if (tailn > 0) {
-        scan_load(opA, ws, c, nfull);
-        scan_step<true>(opA, sm, sacc, c, obase + static_cast<size_t>(nfull) * CH * ostride, tailn, ostride);
-    }
 
+    // Full chunks run with two register stages: chunk cl computes from one while
+    // chunk cl+1 loads into the other.  Loads and stores in these loops are
+    // unconditional (the look-ahead index is clamped), so each wait is for
+    // exactly the stage needed.  A final partial chunk runs masked.
+    if (state_role) {
+        float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0) * D;
+        f4 sacc[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Sh[(4 * c.lq + r) * D + 16 * (2 * c.wave + tt) + c.lr] = sacc[tt][r];
+            for (int r = 0; r < 4; ++r)
+                sacc[tt][r] = Sh[(4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr];
+        StateOps opA, opB;
+        if (nfull > 0)
+            load_state(opA, ws, c, 0);
+        int cl = 0;
+        for (; cl + 1 < nfull; cl += 2) {
+            load_state(opB, ws, c, cl + 1);
+            state_chunk(opA, sm, sacc, c, 0);
+            load_state(opA, ws, c, min(cl + 2, nch - 1));
+            state_chunk(opB, sm, sacc, c, 1);
+        }
+        if (cl < nfull) {
+            state_chunk(opA, sm, sacc, c, cl & 1);
+            ++cl;
+        }
+        if (tailn > 0) {
+            load_state(opA, ws, c, nfull);
+            state_chunk(opA, sm, sacc, c, cl & 1);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sh[(4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr] = sacc[tt][r];
+    } else {
+        const size_t ostride = static_cast<size_t>(Hv) * D;
+        float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
+        OutOps opA, opB;
+        if (nfull > 0)
+            load_out(opA, ws, c, 0);
+        int cl = 0;
+        for (; cl + 1 < nfull; cl += 2) {
+            load_out(opB, ws, c, cl + 1);
+            out_chunk<false>(opA, sm, c, 0, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
+            load_out(opA, ws, c, min(cl + 2, nch - 1));
+            out_chunk<false>(opB, sm, c, 1, obase + static_cast<size_t>(cl + 1) * CH * ostride, CH, ostride);
+        }
+        if (cl < nfull) {
+            out_chunk<false>(opA, sm, c, cl & 1, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
+            ++cl;
+        }
+        if (tailn > 0) {
+            load_out(opA, ws, c, nfull);
+            out_chunk<true>(opA, sm, c, cl & 1, obase + static_cast<size_t>(nfull) * CH * ostride, tailn, ostride);
+        }
+    }
 }
 
 // ------------------------------------------------------------ tail
@@ -603,8 +653,8 @@ hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int
                            seg0, SP, nch, g.Hk, g.Hv);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), block, 0, s, S, o, W, T, seg0,
-                           SP, nch, g.B, g.Hk, g.Hv);
+        hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), dim3(512), 0, s, S, o, W, T,
+                           seg0, SP, nch, g.B, g.Hk, g.Hv);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
