@@ -77,6 +77,27 @@ class Timer:
         self.ms = self.s.elapsed_time(self.e)
 
 
+def graph_time_us(torch, fn, n, reps=4):
+    """Capture fn(0..n-1) into one hip graph, replay it `reps` times; microseconds per call.
+    Replays skip the host-side cost of each call, so this is the device-side rate."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    with Timer(torch) as tm:
+        for _ in range(reps):
+            g.replay()
+    del g
+    return tm.ms * 1e3 / (reps * n)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,21 +257,13 @@ def main():
             gdn.conv_update(d64, x64[t], T64[t % 2], w64, y64)
             gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
 
-        for t in range(16):
-            step64(t)
-        with Timer(torch) as tm:
-            for t in range(16, 16 + steps64):
-                step64(t)
         db, cb = step_bytes(B, shape)
-        res["decode_b64"] = {"ms_per_step": tm.ms / steps64, "GBps": (db + cb) * steps64 / tm.ms / 1e6,
-                             "tokens_per_s": B * steps64 / tm.ms * 1e3, "frac_hbm": (db + cb) * steps64 / tm.ms / 1e6 / HBM_PEAK_GBS}
-        # the state-step kernel alone at batch 64
-        for t in range(8):
-            gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
-        with Timer(torch) as tm:
-            for t in range(steps64):
-                gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
-        us = tm.ms * 1e3 / steps64
+        us = graph_time_us(torch, lambda t: step64(16 + t), steps64, reps=2)
+        res["decode_b64"] = {"ms_per_step": us / 1e3, "GBps": (db + cb) / us / 1e3,
+                             "tokens_per_s": B / us * 1e6, "frac_hbm": (db + cb) / us / 1e3 / HBM_PEAK_GBS,
+                             "launch": "hipGraph", "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
+        us = graph_time_us(torch, lambda t: gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64), steps64,
+                           reps=2)
         res["decode_b64"]["kernel_us"] = us
         res["decode_b64"]["kernel_GBps"] = db / us / 1e3
         res["decode_b64"]["kernel_frac_hbm"] = db / us / 1e3 / HBM_PEAK_GBS
@@ -269,27 +282,20 @@ def main():
         xt, at, bt, wt = act(tin.x[:, 0]), f32(tin.a[:, 0]), f32(tin.b[:, 0]), act(tin.w)
         ot = torch.empty(32, Hv, D, device=dev)
         st = torch.zeros(1, dtype=torch.int32, device=dev)
-        nrep = 1024
+        tws = torch.empty(gdn.tree_workspace_bytes(d1, 32), dtype=torch.uint8, device=dev)
+        nrep = 512
         if "tree" in rows:
-            for r in range(16):
-                gdn.tree_verify(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, ot, st)
-            with Timer(torch) as tm:
-                for r in range(nrep):
-                    gdn.tree_verify(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, ot, st)
-            us = tm.ms * 1e3 / nrep
+            us = graph_time_us(torch, lambda r: gdn.tree_verify(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt,
+                                                                 ot, st, tws), nrep)
             tb = tree_bytes(32, shape)
             res["tree_verify_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
-                                      "nodes_per_s": 32 / us * 1e6, "bytes": tb}
+                                      "nodes_per_s": 32 / us * 1e6, "bytes": tb, "launch": "hipGraph"}
         if "commit" in rows:
-            for r in range(16):
-                gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, path, None, st)
-            with Timer(torch) as tm:
-                for r in range(nrep):
-                    gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt, path, None, st)
-            us = tm.ms * 1e3 / nrep
+            us = graph_time_us(torch, lambda r: gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt,
+                                                                 path, None, st), nrep)
             cbt = commit_bytes(L, shape)
             res["commit_path"] = {"us": us, "path_len": L, "GBps": cbt / us / 1e3,
-                                  "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt}
+                                  "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt, "launch": "hipGraph"}
             if "tree_verify_n32" in res:
                 res["commit_path"]["committed_tokens_per_s"] = L / (us + res["tree_verify_n32"]["us"]) * 1e6
         assert st.item() == 0

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
-    "prefill_workspace_bytes", "conv_update", "decode_step", "tree_verify", "commit_path",
+    "prefill_workspace_bytes", "tree_workspace_bytes", "conv_update", "decode_step", "tree_verify", "commit_path",
     "tree_tables", "prefill_chunked", "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH",
     "PREFILL_CHUNK", "F32", "BF16",
 ]
@@ -30,7 +30,7 @@ F32, BF16 = 0, 1
 _STATUS_TREE = 5
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m gated_deltanet_decode_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python gated_deltanet_decode_amd/build.py`")
 
 _lib = C.CDLL(LIB_PATH)
 
@@ -65,7 +65,8 @@ _sig = {
     "gdn_prefill_workspace_bytes": ([_D, _I], C.c_size_t),
     "gdn_conv_update": ([_D, _P, _P, _P, _P, _P], C.c_int),
     "gdn_decode_step": ([_D, _P, _P, _P, _P, _P, _P], C.c_int),
-    "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_tree_workspace_bytes": ([_D, _I], C.c_size_t),
+    "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
     "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
     "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
@@ -143,15 +144,26 @@ def decode_step(d: Dims, state, y, a, b, o, stream=None) -> None:
                                 _stream(stream)), "gdn_decode_step")
 
 
-def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, stream=None) -> None:
+def tree_workspace_bytes(d: Dims, n_nodes: int) -> int:
+    return _lib.gdn_tree_workspace_bytes(C.byref(d), n_nodes)
+
+
+def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, workspace=None, stream=None) -> None:
+    """workspace: a device byte tensor of at least tree_workspace_bytes(d, n) bytes."""
     n = parent.numel()
     Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    need = tree_workspace_bytes(d, n)
+    if workspace is None or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("tree_verify needs a contiguous device workspace tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace of {ws_bytes} bytes, need {need}")
     _check(_lib.gdn_tree_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, Hv * dv * dk),
                                 _t(tail, "conv_tail", d.act_torch, Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
                                 n, _t(parent, "parent", torch.int32, n), _t(x, "x", d.act_torch, n * Cc),
                                 _t(a, "a", torch.float32, n * Hv), _t(b, "b", torch.float32, n * Hv),
                                 _t(o, "o", torch.float32, n * Hv * dv), _opt(status, "tree_status", torch.int32, 1),
-                                _stream(stream)), "gdn_tree_verify")
+                                workspace.data_ptr(), ws_bytes, _stream(stream)), "gdn_tree_verify")
 
 
 def commit_path(d: Dims, state, tail, w, parent, x, a, b, path, o=None, status=None, stream=None) -> None:

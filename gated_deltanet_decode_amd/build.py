@@ -1,6 +1,9 @@
 """Build libgdn.so (the HIP library) in-tree for gfx950.
 
-    python -m gated_deltanet_decode_amd.build
+    python gated_deltanet_decode_amd/build.py
+
+Run it as a file (or load it by path): importing the package itself loads the
+library this script produces.
 
 Every HIP source compiles with -ffp-contract=off (the per-token arithmetic
 spells out each fused multiply-add, so decode, tree verify and commit round

@@ -123,9 +123,16 @@ gdn_status gdn_tree_tables(int32_t n_nodes, const int32_t* parent, int32_t* dept
     return launched(gdn::launch_tree_tables(n_nodes, parent, depth, order, tree_status, as_stream(stream)));
 }
 
+size_t gdn_tree_workspace_bytes(const gdn_dims* d, int32_t n_nodes) {
+    gdn::Geo g;
+    if (check_dims(d, g) != GDN_OK || n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES)
+        return 0;
+    return gdn::tree_ws_bytes(n_nodes, g.Hk, g.Hv, g.D);
+}
+
 gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
                            int32_t n_nodes, const int32_t* parent, const void* x, const float* a, const float* b,
-                           float* o, int32_t* tree_status, void* stream) {
+                           float* o, int32_t* tree_status, void* workspace, size_t workspace_bytes, void* stream) {
     gdn::Geo g;
     gdn_status st = check_dims(d, g);
     if (st == GDN_OK && g.B != 1)
@@ -138,8 +145,12 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
         st = GDN_ERR_TREE;
     if (st != GDN_OK)
         return st;
+    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(n_nodes, g.Hk, g.Hv, g.D))
+        return GDN_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return GDN_ERR_ALIGN;
     return launched(gdn::launch_tree_verify(g, state_ckpt, conv_tail, conv_w, n_nodes, parent, x, a, b, o,
-                                            tree_status, as_stream(stream)));
+                                            tree_status, workspace, as_stream(stream)));
 }
 
 gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w, int32_t n_nodes,

@@ -17,9 +17,10 @@ hipError_t launch_decode(const Geo& g, float* S, const float* y, const float* a,
                          hipStream_t s);
 hipError_t launch_tree_tables(int n, const int32_t* parent, int32_t* depth, int32_t* order, int32_t* status,
                               hipStream_t s);
+size_t tree_ws_bytes(int n, int Hk, int Hv, int D);
 hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
                               const int32_t* parent, const void* x, const float* a, const float* b, float* o,
-                              int32_t* status, hipStream_t s);
+                              int32_t* status, void* ws, hipStream_t s);
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
                          int32_t* status, hipStream_t s);

@@ -47,43 +47,74 @@ hipError_t launch_tree_tables(int n, const int32_t* parent, int32_t* depth, int3
     return hipGetLastError();
 }
 
-// Shared-memory image of up to kMaxNodes tokens for one workgroup.
-template <int D, int ROWS>
-struct NodeSmem {
-    float qk[kMaxNodes][2 * D];  // q~|k~ of the workgroup's q/k head, normalised in place
-    float v[kMaxNodes][ROWS];    // v of the workgroup's rows
-    float kq[kMaxNodes];
-    float alpha[kMaxNodes];
-    float beta[kMaxNodes];
-    int32_t depth[kMaxNodes];
-    int32_t order[kMaxNodes];
-    int32_t parent[kMaxNodes];
+// Shared-memory image of up to MAXN tokens (tree nodes or path positions) for
+// one workgroup: the workgroup's channels are its q/k head's q and k channels
+// and the v channels of its rows.
+template <int D, int ROWS, int MAXN, typename Act>
+struct alignas(16) NodeSmem {
+    static constexpr int PER = 2 * D + ROWS;
+    float qk[MAXN][2 * D];      // q~|k~ of each token, normalised in place
+    float v[MAXN][ROWS];        // v of the workgroup's rows
+    float wl[PER][4];           // conv weights of the workgroup's channels
+    float kq[MAXN], alpha[MAXN], beta[MAXN];
+    float ga[MAXN], gb[MAXN];   // raw gate inputs of the value head
+    Act xr[MAXN][PER];          // raw inputs of the workgroup's channels
+    Act tl[PER][4];             // checkpoint conv tail of those channels
+    int32_t node[MAXN];         // node id of token i
+    int32_t depth[MAXN];        // depth of token i (root = 1)
+    int32_t anc[MAXN][3];       // token index of the ancestor 1..3 steps up, -1 past the root
+    int32_t order[MAXN];        // depth-first pre-order of the tokens (verify)
     int32_t ok;
 };
 
-// Fill conv outputs, normalised q/k, kq and gates for tokens 0..count-1.
-// Token i is node id_of(i) at depth depth_of(i); anc_of(i, k) is its ancestor
-// k steps up (only asked for k < depth).
-template <int D, int ROWS, typename Act, typename IdOf, typename DepthOf, typename AncOf>
-__device__ void fill_nodes(NodeSmem<D, ROWS>& sm, int count, IdOf id_of, DepthOf depth_of, AncOf anc_of,
-                           const Act* __restrict__ x, const Act* __restrict__ tail, const Act* __restrict__ w,
-                           const float* __restrict__ a, const float* __restrict__ b, int Hk, int Hv, int C, int grp,
-                           int h, int row0) {
-    constexpr int PER = 2 * D + ROWS;
+// Fill conv outputs, normalised q/k, k.q and gates for tokens 0..count-1 from
+// sm.node, sm.depth and sm.anc.  Every global load is issued before any is
+// used: each thread requests its channel's raw input at every token at once.
+template <int D, int ROWS, int MAXN, typename Act>
+__device__ void fill_nodes(NodeSmem<D, ROWS, MAXN, Act>& sm, int count, const Act* __restrict__ x,
+                           const Act* __restrict__ tail, const Act* __restrict__ w, const float* __restrict__ a,
+                           const float* __restrict__ b, int Hk, int Hv, int C, int grp, int h, int row0) {
+    constexpr int PER = NodeSmem<D, ROWS, MAXN, Act>::PER;
+    if (threadIdx.x < MAXN) {
+        const int i = threadIdx.x < count ? threadIdx.x : count - 1;
+        const size_t gi = static_cast<size_t>(sm.node[i]) * Hv + h;
+        sm.ga[threadIdx.x] = a[gi];
+        sm.gb[threadIdx.x] = b[gi];
+    }
+    for (int ch = threadIdx.x; ch < PER; ch += blockDim.x) {
+        const int c = ch < D ? grp * D + ch : ch < 2 * D ? Hk * D + grp * D + (ch - D) : 2 * Hk * D + h * D + row0 + (ch - 2 * D);
+        Act r[MAXN];
+#pragma unroll
+        for (int i = 0; i < MAXN; ++i)
+            r[i] = x[static_cast<size_t>(sm.node[i < count ? i : count - 1]) * C + c];
+        const typename Quad<Act>::raw tq = Quad<Act>::load(tail + static_cast<size_t>(c) * 4);
+        float wf[4];
+        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sm.tl[ch][j] = Quad<Act>::elem(tq, j);
+            sm.wl[ch][j] = wf[j];
+        }
+#pragma unroll
+        for (int i = 0; i < MAXN; ++i)
+            if (i < count)
+                sm.xr[i][ch] = r[i];
+    }
+    __syncthreads();
+    // conv + SiLU per (token, channel), from LDS only
     for (int idx = threadIdx.x; idx < count * PER; idx += blockDim.x) {
         const int i = idx / PER;
         const int ch = idx % PER;
-        const int c = ch < D ? grp * D + ch : ch < 2 * D ? Hk * D + grp * D + (ch - D) : 2 * Hk * D + h * D + row0 + (ch - 2 * D);
-        const int node = id_of(i);
-        const int d = depth_of(i);
-        int anc[3];
+        const int d = sm.depth[i];
+        float win[4];
+        win[3] = widen(sm.xr[i][ch]);
 #pragma unroll
-        for (int k = 1; k <= 3; ++k)
-            anc[k - 1] = (k <= d - 1) ? anc_of(i, k) : 0;
-        float win[4], wf[4];
-        node_window<Act>(x, tail, C, c, node, d, anc, win);
-        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
-        const float yv = conv_silu(wf, win);
+        for (int k = 1; k <= 3; ++k) {
+            const int an = sm.anc[i][k - 1];
+            const Act* src = an >= 0 ? &sm.xr[an][ch] : &sm.tl[ch][3 + d - k];
+            win[3 - k] = widen(*src);
+        }
+        const float yv = conv_silu(sm.wl[ch], win);
         if (ch < 2 * D)
             sm.qk[i][ch] = yv;
         else
@@ -113,9 +144,8 @@ __device__ void fill_nodes(NodeSmem<D, ROWS>& sm, int count, IdOf id_of, DepthOf
             }
         }
         if (lane == 0) {
-            const int node = id_of(i);
             float al, be;
-            gates(a[static_cast<size_t>(node) * Hv + h], b[static_cast<size_t>(node) * Hv + h], al, be);
+            gates(sm.ga[i], sm.gb[i], al, be);
             sm.kq[i] = kq;
             sm.alpha[i] = al;
             sm.beta[i] = be;
@@ -124,20 +154,175 @@ __device__ void fill_nodes(NodeSmem<D, ROWS>& sm, int count, IdOf id_of, DepthOf
     __syncthreads();
 }
 
+// One token's operands for a lane's row slice.
+template <int D>
+struct TokOps {
+    float4 k[Row<D>::NV], q[Row<D>::NV];
+    float v, alpha, beta, kq;
+};
+
+template <int D, int ROWS, int MAXN, typename Act>
+__device__ __forceinline__ void tok_load(TokOps<D>& t, const NodeSmem<D, ROWS, MAXN, Act>& sm, int i, int r,
+                                         int lrow) {
+#pragma unroll
+    for (int j = 0; j < Row<D>::NV; ++j) {
+        t.k[j] = *reinterpret_cast<const float4*>(&sm.qk[i][D + Row<D>::key(j, r)]);
+        t.q[j] = *reinterpret_cast<const float4*>(&sm.qk[i][Row<D>::key(j, r)]);
+    }
+    t.v = sm.v[i][lrow];
+    t.alpha = sm.alpha[i];
+    t.beta = sm.beta[i];
+    t.kq = sm.kq[i];
+}
+
 // ------------------------------------------------------------ verify
 
+// Per-node operands of a tree, prepared once by tree_prep_kernel:
+//   qk  f32 [n][Hk][2*D]  q^ | k^ of each q/k head (normalised)
+//   kq  f32 [n][Hk]       k^.q^
+//   v   f32 [n][Hv][D]    conv output of each value head's v channels
+//   ab  f32 [n][Hv][2]    alpha, beta
+struct TreeWs {
+    float *qk, *kq, *v, *ab;
+};
+
+size_t tree_ws_bytes(int n, int Hk, int Hv, int D) {
+    return static_cast<size_t>(n) * (2ull * Hk * D + Hk + static_cast<size_t>(Hv) * D + 2ull * Hv) * 4 + 4 * 256;
+}
+
+static TreeWs tree_ws_carve(void* base, int n, int Hk, int Hv, int D) {
+    auto align = [](uintptr_t p) { return (p + 255) & ~static_cast<uintptr_t>(255); };
+    uintptr_t p = align(reinterpret_cast<uintptr_t>(base));
+    TreeWs w;
+    auto take = [&](size_t cnt) { float* r = reinterpret_cast<float*>(p); p = align(p + cnt * 4); return r; };
+    w.qk = take(static_cast<size_t>(n) * Hk * 2 * D);
+    w.kq = take(static_cast<size_t>(n) * Hk);
+    w.v = take(static_cast<size_t>(n) * Hv * D);
+    w.ab = take(static_cast<size_t>(n) * Hv * 2);
+    return w;
+}
+
+// One workgroup per (node, q/k head): the node's conv window over its q/k
+// head's channels and its value heads' channels, the q/k norm and the gates.
+// The ancestor chain is followed at most three links and every link is
+// checked, so a malformed parent array stays in bounds (the verify kernel
+// reports it and writes nothing).
 template <int D, typename Act>
-__global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, const Act* __restrict__ tail,
-                                                          const Act* __restrict__ w, int n,
-                                                          const int32_t* __restrict__ parent,
-                                                          const Act* __restrict__ x, const float* __restrict__ a,
-                                                          const float* __restrict__ b, float* __restrict__ o,
-                                                          int32_t* __restrict__ status, int Hk, int Hv, int C,
-                                                          int blocks_per_head) {
+__global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
+                                                        int n, const int32_t* __restrict__ parent,
+                                                        const Act* __restrict__ x, const float* __restrict__ a,
+                                                        const float* __restrict__ b, TreeWs ws, int Hk, int Hv,
+                                                        int C) {
+    __shared__ float yqk[2 * D];
+    __shared__ int32_t anc_s[4];
+    const int i = blockIdx.x % n;
+    const int g = blockIdx.x / n;
+    const int G = Hv / Hk;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (threadIdx.x < kWave) {
+        const int p = lane < n ? parent[lane] : -1;
+        int cur = i, m = 0;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int up = __shfl(p, cur >= 0 ? cur : 0, kWave);
+            const bool link = cur >= 0 && up >= 0 && up < cur;
+            if (lane == 0)
+                anc_s[k] = link ? up : -1;
+            m += link ? 1 : 0;
+            cur = link ? up : -1;
+        }
+        if (lane == 0)
+            anc_s[3] = m;   // ancestors found (at most 3)
+    }
+    __syncthreads();
+    const int m = anc_s[3];
+    for (int ch = threadIdx.x; ch < (2 + G) * D; ch += blockDim.x) {
+        const int c = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
+        float win[4], wf[4];
+        win[3] = widen(x[static_cast<size_t>(i) * C + c]);
+#pragma unroll
+        for (int k = 1; k <= 3; ++k) {
+            const Act* src = (k <= m) ? x + static_cast<size_t>(anc_s[k - 1]) * C + c
+                                      : tail + static_cast<size_t>(c) * 4 + (4 + m - k);
+            win[3 - k] = widen(*src);
+        }
+        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
+        const float yv = conv_silu(wf, win);
+        if (ch < 2 * D)
+            yqk[ch] = yv;
+        else
+            ws.v[(static_cast<size_t>(i) * Hv + G * g) * D + (ch - 2 * D)] = yv;
+    }
+    if (threadIdx.x < G) {
+        const int h = G * g + threadIdx.x;
+        float al, be;
+        gates(a[static_cast<size_t>(i) * Hv + h], b[static_cast<size_t>(i) * Hv + h], al, be);
+        ws.ab[(static_cast<size_t>(i) * Hv + h) * 2] = al;
+        ws.ab[(static_cast<size_t>(i) * Hv + h) * 2 + 1] = be;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        constexpr int J = Prep<D>::J;
+        float qv[J], kv[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + kWave * j;
+            qv[j] = e < D ? yqk[e] : 0.0f;
+            kv[j] = e < D ? yqk[D + e] : 0.0f;
+        }
+        float kq;
+        prep_qk<D>(qv, kv, kq);
+        float* dst = ws.qk + (static_cast<size_t>(i) * Hk + g) * 2 * D;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + kWave * j;
+            if (e < D) {
+                dst[e] = qv[j];
+                dst[D + e] = kv[j];
+            }
+        }
+        if (lane == 0)
+            ws.kq[static_cast<size_t>(i) * Hk + g] = kq;
+    }
+}
+
+template <int D, int ROWS>
+struct alignas(16) VerifySmem {
+    float qk[kMaxNodes][2 * D];
+    float v[kMaxNodes][ROWS];
+    float kq[kMaxNodes], alpha[kMaxNodes], beta[kMaxNodes];
+    int32_t depth[kMaxNodes];
+    int32_t order[kMaxNodes];
+    int32_t ok;
+};
+
+// One node of the pre-order walk whose result goes to stack level L (depth
+// L + 1); its parent's row is base (L == 0) or stack level L - 1.  Static
+// levels keep the stack in registers.
+template <int D, int L>
+__device__ __forceinline__ float walk_step(float4 (&stack)[kMaxDepth][Row<D>::NV], const float4 (&base)[Row<D>::NV],
+                                           const TokOps<D>& t) {
+    constexpr int NV = Row<D>::NV;
+    float4 s[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        s[j] = (L == 0) ? base[j] : stack[L > 0 ? L - 1 : 0][j];
+    const float out = row_update<D>(s, t.k, t.q, t.alpha, t.beta, t.v, t.kq);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        stack[L][j] = s[j];
+    return out;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, int n,
+                                                          const int32_t* __restrict__ parent, TreeWs ws,
+                                                          float* __restrict__ o, int32_t* __restrict__ status,
+                                                          int Hk, int Hv, int blocks_per_head) {
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
     constexpr int ROWS = 4 * RPW;
-    __shared__ NodeSmem<D, ROWS> sm;
+    __shared__ VerifySmem<D, ROWS> sm;
 
     const int blk = blockIdx.x % blocks_per_head;
     const int h = blockIdx.x / blocks_per_head;
@@ -155,10 +340,25 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     for (int j = 0; j < NV; ++j)
         base[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
 
+    // prepared operands of every node for this workgroup's head and rows
+    constexpr int Q4 = 2 * D / 4;
+    for (int idx = threadIdx.x; idx < n * Q4; idx += blockDim.x) {
+        const int i = idx / Q4, e = idx % Q4;
+        *reinterpret_cast<float4*>(&sm.qk[i][4 * e]) =
+            *reinterpret_cast<const float4*>(ws.qk + (static_cast<size_t>(i) * Hk + grp) * 2 * D + 4 * e);
+    }
+    for (int idx = threadIdx.x; idx < n * ROWS; idx += blockDim.x) {
+        const int i = idx / ROWS, rr = idx % ROWS;
+        sm.v[i][rr] = ws.v[(static_cast<size_t>(i) * Hv + h) * D + row0 + rr];
+    }
+    if (threadIdx.x < n) {
+        const int i = threadIdx.x;
+        sm.kq[i] = ws.kq[static_cast<size_t>(i) * Hk + grp];
+        sm.alpha[i] = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2];
+        sm.beta[i] = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2 + 1];
+    }
     if (wave == 0) {
         const bool ok = tree_tables_wave(n, parent, sm.depth, sm.order);
-        if (lane < n)
-            sm.parent[lane] = ok ? parent[lane] : -1;
         if (lane == 0) {
             sm.ok = ok ? 1 : 0;
             if (status && blockIdx.x == 0)
@@ -169,51 +369,49 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     if (!sm.ok)
         return;
 
-    const int32_t* par = sm.parent;
-    fill_nodes<D, ROWS, Act>(
-        sm, n, [](int i) { return i; }, [&](int i) { return sm.depth[i]; },
-        [&](int i, int k) {
-            int m = i;
-            for (int s = 0; s < k; ++s)
-                m = par[m];
-            return m;
-        },
-        x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
-
+    // Pre-order walk.  Lane l holds the l-th node of the walk and its depth, so
+    // the loop reads them with readlane; the next node's operands load from LDS
+    // while the current one computes.
+    const int ord_l = lane < n ? sm.order[lane] : 0;
+    const int dep_l = lane < n ? sm.depth[ord_l] : 1;
     float4 stack[kMaxDepth][NV];
 #pragma unroll
     for (int l = 0; l < kMaxDepth; ++l)
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             stack[l][j] = base[j];
-
-    float4 kk[NV], qq[NV], cur[NV];
-    for (int it = 0; it < n; ++it) {
-        const int node = sm.order[it];
-        const int d = sm.depth[node];
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            cur[j] = base[j];
-#pragma unroll
-        for (int l = 0; l < kMaxDepth - 1; ++l)
-            if (l == d - 2)
-#pragma unroll
-                for (int j = 0; j < NV; ++j)
-                    cur[j] = stack[l][j];
+    TokOps<D> cur, nxt;
+    auto load_tok = [&](TokOps<D>& t, int i) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            kk[j] = *reinterpret_cast<const float4*>(&sm.qk[node][D + R::key(j, r)]);
-            qq[j] = *reinterpret_cast<const float4*>(&sm.qk[node][R::key(j, r)]);
+            t.k[j] = *reinterpret_cast<const float4*>(&sm.qk[i][D + R::key(j, r)]);
+            t.q[j] = *reinterpret_cast<const float4*>(&sm.qk[i][R::key(j, r)]);
         }
-        const float out = row_update<D>(cur, kk, qq, sm.alpha[node], sm.beta[node], sm.v[node][lrow], sm.kq[node]);
-#pragma unroll
-        for (int l = 0; l < kMaxDepth; ++l)
-            if (l == d - 1)
-#pragma unroll
-                for (int j = 0; j < NV; ++j)
-                    stack[l][j] = cur[j];
+        t.v = sm.v[i][lrow];
+        t.alpha = sm.alpha[i];
+        t.beta = sm.beta[i];
+        t.kq = sm.kq[i];
+    };
+    load_tok(cur, __builtin_amdgcn_readlane(ord_l, 0));
+    float* oh = o + static_cast<size_t>(h) * D + row;
+    for (int it = 0; it < n; ++it) {
+        const int node = __builtin_amdgcn_readlane(ord_l, it);
+        const int d = __builtin_amdgcn_readlane(dep_l, it);
+        load_tok(nxt, __builtin_amdgcn_readlane(ord_l, it + 1 < n ? it + 1 : it));
+        float out;
+        switch (d) {
+            case 1: out = walk_step<D, 0>(stack, base, cur); break;
+            case 2: out = walk_step<D, 1>(stack, base, cur); break;
+            case 3: out = walk_step<D, 2>(stack, base, cur); break;
+            case 4: out = walk_step<D, 3>(stack, base, cur); break;
+            case 5: out = walk_step<D, 4>(stack, base, cur); break;
+            case 6: out = walk_step<D, 5>(stack, base, cur); break;
+            case 7: out = walk_step<D, 6>(stack, base, cur); break;
+            default: out = walk_step<D, 7>(stack, base, cur); break;
+        }
         if (r == 0)
-            o[(static_cast<size_t>(node) * Hv + h) * D + row] = out;
+            oh[static_cast<size_t>(node) * Hv * D] = out;
+        cur = nxt;
     }
 }
 
@@ -236,14 +434,22 @@ static hipError_t dispatch(const Geo& g, F&& f) {
 
 hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
                               const int32_t* parent, const void* x, const float* a, const float* b, float* o,
-                              int32_t* status, hipStream_t s) {
-    return dispatch(g, [&](auto dtag, auto atag) {
+                              int32_t* status, void* ws, hipStream_t s) {
+    const TreeWs W = tree_ws_carve(ws, n, g.Hk, g.Hv, g.D);
+    hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
+        hipLaunchKernelGGL((tree_prep_kernel<D, Act>), dim3(static_cast<unsigned>(n * g.Hk)), dim3(256), 0, s,
+                           static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                           static_cast<const Act*>(x), a, b, W, g.Hk, g.Hv, g.C);
+    });
+    if (e != hipSuccess)
+        return e;
+    return dispatch(g, [&](auto dtag, auto) {
+        constexpr int D = decltype(dtag)::value;
         const int bph = D / (4 * Row<D>::RPW);
-        hipLaunchKernelGGL((tree_verify_kernel<D, Act>), dim3(static_cast<unsigned>(g.Hv * bph)), dim3(256), 0, s,
-                           S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                           static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C, bph);
+        hipLaunchKernelGGL((tree_verify_kernel<D>), dim3(static_cast<unsigned>(g.Hv * bph)), dim3(256), 0, s, S, n,
+                           parent, W, o, status, g.Hk, g.Hv, bph);
     });
 }
 
@@ -261,7 +467,7 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
     constexpr int ROWS = 4 * RPW;
-    __shared__ NodeSmem<D, ROWS> sm;
+    __shared__ NodeSmem<D, ROWS, kMaxDepth, Act> sm;
 
     const int blk = blockIdx.x % blocks_per_head;
     const int h = blockIdx.x / blocks_per_head;
@@ -274,16 +480,22 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     const int row = row0 + lrow;
 
     float* Sh = S + static_cast<size_t>(h) * D * D;
-    float4 cur[NV];
+    float4 s[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        cur[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
+        s[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
 
     if (wave == 0) {
         bool ok = tree_tables_wave(n, parent, nullptr, nullptr);
         ok = ok && path_check_wave(n, parent, L, path);
-        if (lane < L)
-            sm.order[lane] = ok ? path[lane] : 0;
+        if (lane < L) {
+            // token i of the commit is path position i: its ancestors are the positions before it
+            sm.node[lane] = ok ? path[lane] : 0;
+            sm.depth[lane] = lane + 1;
+#pragma unroll
+            for (int k = 1; k <= 3; ++k)
+                sm.anc[lane][k - 1] = lane - k;
+        }
         if (lane == 0) {
             sm.ok = ok ? 1 : 0;
             if (status && blockIdx.x == 0)
@@ -294,24 +506,20 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     if (!sm.ok)
         return;
 
-    fill_nodes<D, ROWS, Act>(
-        sm, L, [&](int i) { return sm.order[i]; }, [](int i) { return i + 1; },
-        [&](int i, int k) { return sm.order[i - k]; }, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
+    fill_nodes<D, ROWS, kMaxDepth, Act>(sm, L, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
 
-    float4 kk[NV], qq[NV];
+    TokOps<D> cur, nxt;
+    tok_load(cur, sm, 0, r, lrow);
     for (int i = 0; i < L; ++i) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            kk[j] = *reinterpret_cast<const float4*>(&sm.qk[i][D + R::key(j, r)]);
-            qq[j] = *reinterpret_cast<const float4*>(&sm.qk[i][R::key(j, r)]);
-        }
-        const float out = row_update<D>(cur, kk, qq, sm.alpha[i], sm.beta[i], sm.v[i][lrow], sm.kq[i]);
+        tok_load(nxt, sm, i + 1 < L ? i + 1 : i, r, lrow);
+        const float out = row_update<D>(s, cur.k, cur.q, cur.alpha, cur.beta, cur.v, cur.kq);
         if (o && r == 0)
             o[(static_cast<size_t>(i) * Hv + h) * D + row] = out;
+        cur = nxt;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        *reinterpret_cast<float4*>(Sh + row * D + R::key(j, r)) = cur[j];
+        *reinterpret_cast<float4*>(Sh + row * D + R::key(j, r)) = s[j];
 }
 
 // The tail after a commit holds the last four raw inputs of (old tail ++ path).

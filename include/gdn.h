@@ -129,11 +129,17 @@ gdn_status gdn_decode_step(const gdn_dims* d, float* state, const float* y,
  *   o          f32 [n_nodes][Hv][dv]  (written)
  *   tree_status i32 [1] or NULL: set to GDN_OK, or GDN_ERR_TREE when parent[]
  *              is malformed (o is then undefined).
+ *   workspace  device bytes >= gdn_tree_workspace_bytes(d, n_nodes), 16-byte
+ *              aligned, caller-owned: each node's normalised q/k, v and gates
+ *              are prepared there once and shared by every value head (about
+ *              1.3 MB for 32 nodes at 16 q/k and 48 value heads of 128).
  */
+size_t gdn_tree_workspace_bytes(const gdn_dims* d, int32_t n_nodes);
 gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
                            const void* conv_w, int32_t n_nodes, const int32_t* parent,
                            const void* x, const float* a, const float* b, float* o,
-                           int32_t* tree_status, void* stream);
+                           int32_t* tree_status, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * gdn_commit_path -- commit the accepted root-first path of a verified tree

@@ -49,6 +49,14 @@ def mk(**kw):
     return Dims(**d)
 
 
+def test_tree_workspace_is_bounded(lib):
+    lib.gdn_tree_workspace_bytes.restype = C.c_size_t
+    d = mk()
+    sizes = [lib.gdn_tree_workspace_bytes(C.byref(d), n) for n in (1, 16, 32)]
+    assert 0 < sizes[0] < sizes[1] < sizes[2] < 2 * 1024 * 1024
+    assert lib.gdn_tree_workspace_bytes(C.byref(d), 33) == 0
+
+
 def test_size_queries_match_the_pages(lib):
     """The 27B-class layer: 3.15 MB of fp32 state and an 80 KB bf16 conv tail per
     sequence ("Architecture" section 8.1 table), 151 MB over 48 layers (8.2)."""
@@ -85,15 +93,21 @@ def test_null_and_misaligned_pointers_are_refused(lib):
 
 
 def test_tree_sizes_are_refused_before_launch(lib):
+    P = C.c_void_p
+    lib.gdn_tree_verify.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gdn_commit_path.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, C.c_int32, P, P, P, P]
     fake = C.c_void_p(0x1000)
     d = mk()
     args = [fake] * 3
     # n_nodes out of range
     for n in (0, 33):
-        assert lib.gdn_tree_verify(C.byref(d), *args, n, fake, fake, fake, fake, fake, None, None) == 5
+        assert lib.gdn_tree_verify(C.byref(d), *args, n, fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == 5
     # batch must be 1 for trees
     d2 = mk(batch=2)
-    assert lib.gdn_tree_verify(C.byref(d2), *args, 4, fake, fake, fake, fake, fake, None, None) == 2
+    assert lib.gdn_tree_verify(C.byref(d2), *args, 4, fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == 2
+    # a missing or short workspace is refused before launch
+    assert lib.gdn_tree_verify(C.byref(d), *args, 4, fake, fake, fake, fake, fake, None, None, 0, None) == 6
+    assert lib.gdn_tree_verify(C.byref(d), *args, 4, fake, fake, fake, fake, fake, None, fake, 1024, None) == 6
     # path longer than the depth limit, than the tree, or empty
     for n, L in ((32, 9), (4, 5), (4, 0)):
         assert lib.gdn_commit_path(C.byref(d), *args, n, fake, fake, fake, fake, L, fake, None, None, None) == 5

@@ -31,7 +31,8 @@ def gpu_verify(c, n):
     d = c["d"]
     o = torch.full((n, d.num_v_heads, d.head_v_dim), float("nan"), device="cuda")
     st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
-    gdn.tree_verify(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"], c["b"], o, st)
+    ws = torch.empty(gdn.tree_workspace_bytes(d, n), dtype=torch.uint8, device="cuda")
+    gdn.tree_verify(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"], c["b"], o, st, ws)
     torch.cuda.synchronize()
     return o, int(st.item())
 
