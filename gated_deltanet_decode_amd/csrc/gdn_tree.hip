@@ -3,26 +3,30 @@
 // Verify (repository "Architecture" page, decode-loop diagram: one pass over
 // the whole draft tree of up to 32 nodes; "Architecture" section 8.1: the
 // state must be branched for a tree of guesses) reads the checkpoint state
-// once.  Each workgroup owns a block of rows of one value head; a lane keeps
-// its slice of the checkpoint row plus a stack of up to 8 branched rows, one
-// per tree level, all in registers, and walks the nodes in depth-first
-// pre-order so that a node's parent row is always on the stack.  Nothing is
-// written but the per-node outputs, so rejecting the round costs nothing.
+// once and writes nothing but the per-node outputs, so rejecting the round
+// costs nothing.  Two launches:
+//   tree_prep_kernel    one workgroup per (node, q/k head): conv window over
+//                       the node's ancestors and the tail, q/k norm, gates,
+//                       into a caller-owned workspace;
+//   tree_verify_kernel  each workgroup owns a block of rows of one value head
+//                       and walks the nodes in depth-first pre-order.  A
+//                       lane's slice of the current row stays in registers;
+//                       the row after each node is saved in an LDS slot per
+//                       tree level, from which a later sibling's subtree
+//                       restarts.  Node operands stream from the workspace
+//                       through a register ring several nodes ahead.
 //
 // Commit replays the accepted path from the checkpoint with the same per-token
 // arithmetic as decode (gdn_core.hpp), so the committed state is bit-identical
 // to token-by-token decode of the path; the tail is rewritten by a second,
 // stream-ordered launch after every workgroup of the first has read it.
-//
-// Per-node conv outputs, normalised q/k and gates are computed once per
-// workgroup into LDS: first every thread computes conv outputs for (node,
-// channel) pairs, then each wave normalises whole nodes with the same wave
-// butterfly as the decode kernel.
+// Commit's per-token operands are computed per workgroup into LDS.
 #include "gdn_core.hpp"
 #include "gdn_launch.hpp"
 #include "gdn_tree.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace gdn {
 
@@ -286,33 +290,32 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
     }
 }
 
-template <int D, int ROWS>
+// The branched rows live in LDS, one slot per tree level below the deepest:
+// slot L holds, for every lane, its slice of the row after the most recent
+// node of depth L + 1 on the walk.  A node whose parent is the previous node
+// of the walk takes the rows still in registers; any other node reloads its
+// parent's slot (or the checkpoint rows, for a child of the root).
+template <int D>
 struct alignas(16) VerifySmem {
-    float qk[kMaxNodes][2 * D];
-    float v[kMaxNodes][ROWS];
-    float kq[kMaxNodes], alpha[kMaxNodes], beta[kMaxNodes];
+    float4 stack[kMaxDepth - 1][Row<D>::NV][256];
     int32_t depth[kMaxNodes];
     int32_t order[kMaxNodes];
     int32_t ok;
 };
 
-// One node of the pre-order walk whose result goes to stack level L (depth
-// L + 1); its parent's row is base (L == 0) or stack level L - 1.  Static
-// levels keep the stack in registers.
-template <int D, int L>
-__device__ __forceinline__ float walk_step(float4 (&stack)[kMaxDepth][Row<D>::NV], const float4 (&base)[Row<D>::NV],
-                                           const TokOps<D>& t) {
-    constexpr int NV = Row<D>::NV;
-    float4 s[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        s[j] = (L == 0) ? base[j] : stack[L > 0 ? L - 1 : 0][j];
-    const float out = row_update<D>(s, t.k, t.q, t.alpha, t.beta, t.v, t.kq);
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        stack[L][j] = s[j];
-    return out;
+constexpr int kRing = 6;   // walk steps of operand prefetch
+
+// Calls f(integral_constant<I>) for I = 0, 1, ... until one returns false.
+template <typename F, int... I>
+__device__ __forceinline__ void walk_all(F& f, std::integer_sequence<int, I...>) {
+    (void)(f(std::integral_constant<int, I>{}) && ...);
 }
+
+template <int D>
+struct NodeOps {
+    float4 k[Row<D>::NV], q[Row<D>::NV];
+    float v, alpha, beta, kq;
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, int n,
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
     constexpr int ROWS = 4 * RPW;
-    __shared__ VerifySmem<D, ROWS> sm;
+    __shared__ VerifySmem<D> sm;
 
     const int blk = blockIdx.x % blocks_per_head;
     const int h = blockIdx.x / blocks_per_head;
@@ -330,9 +333,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int r = lane % LPR;
-    const int row0 = blk * ROWS;
-    const int lrow = wave * RPW + lane / LPR;
-    const int row = row0 + lrow;
+    const int row = blk * ROWS + wave * RPW + lane / LPR;
+    const int tid = threadIdx.x;
 
     const float* Sh = Sc + static_cast<size_t>(h) * D * D;
     float4 base[NV];
@@ -340,23 +342,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     for (int j = 0; j < NV; ++j)
         base[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
 
-    // prepared operands of every node for this workgroup's head and rows
-    constexpr int Q4 = 2 * D / 4;
-    for (int idx = threadIdx.x; idx < n * Q4; idx += blockDim.x) {
-        const int i = idx / Q4, e = idx % Q4;
-        *reinterpret_cast<float4*>(&sm.qk[i][4 * e]) =
-            *reinterpret_cast<const float4*>(ws.qk + (static_cast<size_t>(i) * Hk + grp) * 2 * D + 4 * e);
-    }
-    for (int idx = threadIdx.x; idx < n * ROWS; idx += blockDim.x) {
-        const int i = idx / ROWS, rr = idx % ROWS;
-        sm.v[i][rr] = ws.v[(static_cast<size_t>(i) * Hv + h) * D + row0 + rr];
-    }
-    if (threadIdx.x < n) {
-        const int i = threadIdx.x;
-        sm.kq[i] = ws.kq[static_cast<size_t>(i) * Hk + grp];
-        sm.alpha[i] = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2];
-        sm.beta[i] = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2 + 1];
-    }
     if (wave == 0) {
         const bool ok = tree_tables_wave(n, parent, sm.depth, sm.order);
         if (lane == 0) {
@@ -369,50 +354,68 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     if (!sm.ok)
         return;
 
-    // Pre-order walk.  Lane l holds the l-th node of the walk and its depth, so
-    // the loop reads them with readlane; the next node's operands load from LDS
-    // while the current one computes.
+    // Lane l holds the l-th node of the pre-order walk and its depth; the loop
+    // reads them with readlane.  Node operands come from the prepared
+    // workspace through a ring of kRing register slots, unrolled so that each
+    // slot keeps its registers: a slot is refilled with the node kRing steps
+    // ahead as soon as its node is done, which hides the cross-XCD fetch.
     const int ord_l = lane < n ? sm.order[lane] : 0;
     const int dep_l = lane < n ? sm.depth[ord_l] : 1;
-    float4 stack[kMaxDepth][NV];
-#pragma unroll
-    for (int l = 0; l < kMaxDepth; ++l)
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            stack[l][j] = base[j];
-    TokOps<D> cur, nxt;
-    auto load_tok = [&](TokOps<D>& t, int i) {
+    auto load_node = [&](NodeOps<D>& t, int it) {
+        const int i = __builtin_amdgcn_readlane(ord_l, it < n ? it : n - 1);
+        const float* qk = ws.qk + (static_cast<size_t>(i) * Hk + grp) * 2 * D;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            t.k[j] = *reinterpret_cast<const float4*>(&sm.qk[i][D + R::key(j, r)]);
-            t.q[j] = *reinterpret_cast<const float4*>(&sm.qk[i][R::key(j, r)]);
+            t.k[j] = *reinterpret_cast<const float4*>(qk + D + R::key(j, r));
+            t.q[j] = *reinterpret_cast<const float4*>(qk + R::key(j, r));
         }
-        t.v = sm.v[i][lrow];
-        t.alpha = sm.alpha[i];
-        t.beta = sm.beta[i];
-        t.kq = sm.kq[i];
+        t.v = ws.v[(static_cast<size_t>(i) * Hv + h) * D + row];
+        t.alpha = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2];
+        t.beta = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2 + 1];
+        t.kq = ws.kq[static_cast<size_t>(i) * Hk + grp];
     };
-    load_tok(cur, __builtin_amdgcn_readlane(ord_l, 0));
+    NodeOps<D> ring[kRing];
+#pragma unroll
+    for (int p = 0; p < kRing; ++p)
+        load_node(ring[p], p);
+    float4 s[NV];
     float* oh = o + static_cast<size_t>(h) * D + row;
-    for (int it = 0; it < n; ++it) {
+    int dprev = 0;
+    // One walk step per node, expanded at compile time (at most kMaxNodes),
+    // so that ring slots are static registers and every wait on a slot counts
+    // exactly the loads issued after it.
+    auto step = [&](auto itc) -> bool {
+        constexpr int it = decltype(itc)::value;
+        constexpr int p = it % kRing;
+        if (it >= n)
+            return false;
         const int node = __builtin_amdgcn_readlane(ord_l, it);
         const int d = __builtin_amdgcn_readlane(dep_l, it);
-        load_tok(nxt, __builtin_amdgcn_readlane(ord_l, it + 1 < n ? it + 1 : it));
-        float out;
-        switch (d) {
-            case 1: out = walk_step<D, 0>(stack, base, cur); break;
-            case 2: out = walk_step<D, 1>(stack, base, cur); break;
-            case 3: out = walk_step<D, 2>(stack, base, cur); break;
-            case 4: out = walk_step<D, 3>(stack, base, cur); break;
-            case 5: out = walk_step<D, 4>(stack, base, cur); break;
-            case 6: out = walk_step<D, 5>(stack, base, cur); break;
-            case 7: out = walk_step<D, 6>(stack, base, cur); break;
-            default: out = walk_step<D, 7>(stack, base, cur); break;
+        if (d == 1) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                s[j] = base[j];
+        } else if (d != dprev + 1) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                s[j] = sm.stack[d - 2][j][tid];
         }
-        if (r == 0)
-            oh[static_cast<size_t>(node) * Hv * D] = out;
-        cur = nxt;
-    }
+        const NodeOps<D>& t = ring[p];
+        const float out = row_update<D>(s, t.k, t.q, t.alpha, t.beta, t.v, t.kq);
+        if (d < kMaxDepth) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                sm.stack[d - 1][j][tid] = s[j];
+        }
+        // Every lane of the row holds the same sum (the butterfly adds
+        // commuted pairs), so all of them store it: no exec branch.
+        oh[static_cast<size_t>(node) * Hv * D] = out;
+        dprev = d;
+        if (it + kRing < kMaxNodes)
+            load_node(ring[p], it + kRing);
+        return true;
+    };
+    walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
 }
 
 // Runs f(D, Act) for the geometry's head width and activation type.

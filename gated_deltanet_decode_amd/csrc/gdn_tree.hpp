@@ -43,9 +43,11 @@ __device__ inline bool tree_tables_wave(int n, const int32_t* __restrict__ paren
         return false;
     // Root-first key: the root lands in the top slot, shorter chains pad with zeros.
     const uint64_t key = live ? (packed << (6 * (kMaxDepth - depth))) : ~0ull;
+    const uint32_t klo = static_cast<uint32_t>(key), khi = static_cast<uint32_t>(key >> 32);
     int rank = 0;
     for (int j = 0; j < n; ++j) {
-        const uint64_t kj = __shfl(key, j, kWave);
+        const uint64_t kj = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(khi, j))) << 32) |
+                            static_cast<uint32_t>(__builtin_amdgcn_readlane(klo, j));
         rank += (kj < key) ? 1 : 0;
     }
     if (live) {
