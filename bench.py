@@ -5,15 +5,17 @@
 
 The headline line is one decode step of one 27B-class recurrent layer at
 batch 1 (16 q/k heads and 48 value heads of 128, fp32 state of 3.15 MB, bf16
-activations and conv tail), repeated for K chained steps: a step is
-gdn_conv_update + gdn_decode_step.  Each step advances the next of R
-independent states (R * 3.15 MB > the 256 MB Infinity Cache), so every step
-reads its state from HBM, as it would in a model with 48 such layers and
-weights streaming in between.  The value is algorithmic state-traffic GB/s:
-bytes the step must move (state read + write, its vectors) over the time.
+activations and conv tail), repeated for K chained steps: a step is one
+gdn_decode_token call (conv update, q/k norm, gates and state step in one
+launch; bit-identical to gdn_conv_update + gdn_decode_step).  Each step
+advances the next of R independent states (R * 3.15 MB > the 256 MB Infinity
+Cache), so every step reads its state from HBM, as it would in a model with
+48 such layers and weights streaming in between.  The value is algorithmic
+GB/s: bytes the step must move (state read + write, x, conv tail in and out,
+weights, gates, o) over the time.
 
 Extra rows, each with its own roofline fraction: the same step under a hip
-graph, the state step alone (the dominant kernel), batch-64 decode (ping-pong
+graph and as two calls, the state step alone, batch-64 decode (ping-pong
 over two batches), 32-node tree verify, path commit, chunked prefill at
 T = 32,768; and the CPU oracle on a bounded sample as the host baseline.
 Inputs are seeded synthetic tensors of the workload's shapes.
@@ -48,6 +50,14 @@ def step_bytes(B, shape):
     return B * (state + dec_vec), B * conv + conv_w
 
 
+def token_bytes(B, shape):
+    """Algorithmic bytes of one fused token (gdn_decode_token) for B sequences: state read +
+    write, x, conv tail in + out (bf16), a, b, o; the conv weights once per launch."""
+    Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
+    per_seq = 2 * Hv * D * D * 4 + C * 2 + 2 * C * 4 * 2 + 2 * Hv * 4 + Hv * D * 4
+    return B * per_seq + C * 4 * 2
+
+
 def tree_bytes(n, shape):
     Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
     return (Hv * D * D * 4 + n * C * 2 + C * 4 * 2 + C * 4 * 2 + 2 * n * Hv * 4 + n * Hv * D * 4 + n * 4)
@@ -58,19 +68,19 @@ def commit_bytes(L, shape):
     return (2 * Hv * D * D * 4 + L * C * 2 + 2 * C * 4 * 2 + C * 4 * 2 + 2 * L * Hv * 4 + L * Hv * D * 4)
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_b1_27b_layer_counters.md")
-DECODE_SOURCES = [os.path.join(ROOT, "gated_deltanet_decode_amd", "csrc", f) for f in ("gdn_decode.hip", "gdn_core.hpp")]
+COUNTERS = os.path.join(ROOT, "profiles", "token_kernel_b1_27b_layer_counters.md")
+TOKEN_SOURCES = [os.path.join(ROOT, "gated_deltanet_decode_amd", "csrc", f) for f in ("gdn_token.hip", "gdn_core.hpp")]
 
 
 def counter_traffic():
-    """HBM bytes per launch of the batch-1 state step from the committed rocprofv3
+    """HBM bytes per launch of the batch-1 fused token kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when the kernel
     sources no longer hash to what was profiled."""
     import hashlib
     try:
         line = next(l for l in open(COUNTERS) if l.startswith("traffic-json:"))
         rec = json.loads(line.split(":", 1)[1])
-        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in DECODE_SOURCES)).hexdigest()
+        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in TOKEN_SOURCES)).hexdigest()
     except (OSError, StopIteration, ValueError):
         return None
     return rec["bytes_per_launch"] if rec.get("sources_sha256") == sha else None
@@ -163,93 +173,76 @@ def main():
     w = act(inp.w)
     S_pool = f32(pool.state)
     tail_pool = act(pool.tail)
+    tail_pool2 = torch.empty_like(tail_pool)
+    tails = (tail_pool, tail_pool2)
+    cnt = [0] * R   # steps applied to each state: its current tail is tails[cnt % 2]
     del pool
     d1 = gdn.dims(1, 16, 48, 128, 128, 4, "bf16")
     y = torch.empty(1, C, device=dev)
     o = torch.empty(1, Hv, D, device=dev)
     gen_s = time.time() - t0
 
-    def step(t, S, tail):
+    def step(t, r):
+        """One token on state r: the fused call, the tail going from one buffer to the other."""
+        i = cnt[r] % 2
+        gdn.decode_token(d1, S_pool[r], tails[i][r], tails[1 - i][r], w, x[t], a[t], b[t], o)
+        cnt[r] += 1
+
+    def step_two_calls(t, r):
+        """The same token through gdn_conv_update + gdn_decode_step (tail in place)."""
+        tail = tails[cnt[r] % 2][r]
         gdn.conv_update(d1, x[t], tail, w, y)
-        gdn.decode_step(d1, S, y, a[t], b[t], o)
+        gdn.decode_step(d1, S_pool[r], y, a[t], b[t], o)
 
     res = {}
+    per_step = token_bytes(1, shape)
     dec_b, conv_b = step_bytes(1, shape)
-    per_step = dec_b + conv_b
 
     # ---------------------------------------------------------------- headline: cold, eager launches
     for t in range(W):
-        step(t, S_pool[t % R], tail_pool[t % R])
+        step(t, t % R)
     with Timer(torch) as tm:
         for t in range(W, W + K):
-            step(t, S_pool[t % R], tail_pool[t % R])
+            step(t, t % R)
     cold_ms = tm.ms
     res["decode_b1_cold_eager"] = {"ms_per_step": cold_ms / K, "GBps": per_step * K / cold_ms / 1e6,
                                    "tokens_per_s": K / cold_ms * 1e3}
 
     # ---------------------------------------------------------------- same steps under a hip graph
+    # 2R steps per graph: every state advances twice per replay, so its tail
+    # parity is the same at every replay boundary.
     graph_ms = None
     if "graph" in rows:
-        chunk = min(K, 512)
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for t in range(3):  # warm the capture stream
-                step(t, S_pool[t % R], tail_pool[t % R])
-        torch.cuda.current_stream().wait_stream(s)
-        with torch.cuda.graph(g):
-            for t in range(chunk):
-                step(W + t, S_pool[t % R], tail_pool[t % R])
-        g.replay()
-        reps = max(1, K // chunk)
-        with Timer(torch) as tm:
-            for _ in range(reps):
-                g.replay()
-        graph_ms = tm.ms / (reps * chunk) * K
-        res["decode_b1_cold_graph"] = {"ms_per_step": graph_ms / K, "GBps": per_step * K / graph_ms / 1e6,
-                                       "tokens_per_s": K / graph_ms * 1e3, "graph_steps": chunk, "replays": reps}
-        del g
+        chunk = min(K, 2 * R)
+        us = graph_time_us(torch, lambda t: step(W + t % K, t % R), chunk, reps=max(1, K // chunk))
+        graph_ms = us * K / 1e3
+        res["decode_b1_cold_graph"] = {"ms_per_step": us / 1e3, "GBps": per_step / us / 1e3,
+                                       "tokens_per_s": 1e6 / us, "graph_steps": chunk}
+        us2 = graph_time_us(torch, lambda t: step_two_calls(W + t % K, t % R), chunk, reps=max(1, K // chunk))
+        res["decode_b1_two_calls_graph"] = {"ms_per_step": us2 / 1e3, "GBps": (dec_b + conv_b) / us2 / 1e3,
+                                            "tokens_per_s": 1e6 / us2, "calls": "gdn_conv_update + gdn_decode_step"}
 
     # ---------------------------------------------------------------- the state-step kernel alone
-    kern = None
     if "kernel" in rows:
         yk = torch.empty(R, 1, C, device=dev)
         for r in range(R):
-            gdn.conv_update(d1, x[r % steps_total], tail_pool[r], w, yk[r])
-        nk = K
-        for t in range(64):
-            gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t], b[t], o)
-        with Timer(torch) as tm:
-            for t in range(nk):
-                gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t % steps_total], b[t % steps_total], o)
-        eager_us = tm.ms * 1e3 / nk
-        chunk = 512
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for t in range(chunk):
-                gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t], b[t], o)
-        g.replay()
-        reps = max(1, nk // chunk)
-        with Timer(torch) as tm:
-            for _ in range(reps):
-                g.replay()
-        graph_us = tm.ms * 1e3 / (reps * chunk)
-        kern = {"kernel": "decode_kernel<128,1>", "bytes_per_launch": dec_b, "us_per_launch_eager": eager_us,
-                "us_per_launch_graph": graph_us, "GBps_graph": dec_b / graph_us / 1e3,
-                "GBps_eager": dec_b / eager_us / 1e3}
-        res["decode_b1_kernel_cold"] = kern
-        del g, yk
+            gdn.conv_update(d1, x[r % steps_total], tails[cnt[r] % 2][r], w, yk[r])
+        us = graph_time_us(torch, lambda t: gdn.decode_step(d1, S_pool[t % R], yk[t % R], a[t % steps_total],
+                                                             b[t % steps_total], o), 512, reps=max(1, K // 512))
+        res["decode_b1_state_step_kernel"] = {"kernel": "decode_kernel<128,1>", "bytes_per_launch": dec_b,
+                                              "us_per_launch_graph": us, "GBps": dec_b / us / 1e3,
+                                              "frac_hbm": dec_b / us / 1e3 / HBM_PEAK_GBS}
+        del yk
 
     # ---------------------------------------------------------------- hot: one state buffer
     if "hot" in rows:
         S1 = S_pool[0].clone()
-        t1 = tail_pool[0].clone()
+        th = (tails[cnt[0] % 2][0].clone(), tails[cnt[0] % 2][0].clone())
         for t in range(W):
-            step(t, S1, t1)
+            gdn.decode_token(d1, S1, th[t % 2], th[1 - t % 2], w, x[t], a[t], b[t], o)
         with Timer(torch) as tm:
             for t in range(W, W + K):
-                step(t, S1, t1)
+                gdn.decode_token(d1, S1, th[t % 2], th[1 - t % 2], w, x[t], a[t], b[t], o)
         res["decode_b1_hot_eager"] = {"ms_per_step": tm.ms / K, "GBps": per_step * K / tm.ms / 1e6,
                                       "note": "one 3.15 MB state: served from cache, not HBM"}
 
@@ -271,21 +264,28 @@ def main():
         y64 = torch.empty(B, C, device=dev)
         o64 = torch.empty(B, Hv, D, device=dev)
 
+        tails64 = (T64, torch.empty_like(T64))
+        cnt64 = [0, 0]
+
         def step64(t):
-            gdn.conv_update(d64, x64[t], T64[t % 2], w64, y64)
-            gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64)
+            p = t % 2
+            i = cnt64[p] % 2
+            gdn.decode_token(d64, S64[p], tails64[i][p], tails64[1 - i][p], w64, x64[t], a64[t], b64[t], o64)
+            cnt64[p] += 1
 
         db, cb = step_bytes(B, shape)
+        tb = token_bytes(B, shape)
         us = graph_time_us(torch, lambda t: step64(16 + t), steps64, reps=2)
-        res["decode_b64"] = {"ms_per_step": us / 1e3, "GBps": (db + cb) / us / 1e3,
-                             "tokens_per_s": B / us * 1e6, "frac_hbm": (db + cb) / us / 1e3 / HBM_PEAK_GBS,
-                             "launch": "hipGraph", "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
+        res["decode_b64"] = {"ms_per_step": us / 1e3, "GBps": tb / us / 1e3,
+                             "tokens_per_s": B / us * 1e6, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
+                             "launch": "hipGraph", "call": "gdn_decode_token",
+                             "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
         us = graph_time_us(torch, lambda t: gdn.decode_step(d64, S64[t % 2], y64, a64[t], b64[t], o64), steps64,
                            reps=2)
         res["decode_b64"]["kernel_us"] = us
         res["decode_b64"]["kernel_GBps"] = db / us / 1e3
         res["decode_b64"]["kernel_frac_hbm"] = db / us / 1e3 / HBM_PEAK_GBS
-        del S64, T64, x64, a64, b64, y64, o64
+        del S64, T64, tails64, x64, a64, b64, y64, o64
 
     # ---------------------------------------------------------------- tree verify + commit
     if "tree" in rows or "commit" in rows:
@@ -380,13 +380,13 @@ def main():
     best_ms = cold_ms if graph_ms is None else min(cold_ms, graph_ms)
     launch = "eager" if graph_ms is None or cold_ms <= graph_ms else "hipGraph"
     value = per_step * K / best_ms / 1e6
-    roof = None
-    if kern is not None:
-        us = min(kern["us_per_launch_graph"], kern["us_per_launch_eager"])
-        ach = dec_b / us / 1e3
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(), "kernel": "decode_kernel<128,1>",
-                "bytes_per_launch": dec_b, "us_per_launch": round(us, 3)}
+    # The headline step is one launch of the fused token kernel, so its per-step
+    # time (HIP events over the timed region) is that kernel's launch time.
+    us = best_ms * 1e3 / K
+    ach = per_step / us / 1e3
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
+            "kernel": "token_kernel<128,1,bf16>", "bytes_per_launch": per_step, "us_per_launch": round(us, 3)}
     line = {
         "metric": "GDN state GB/s & tokens/s per layer (decode, 32-node tree, prefill); % roofline",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
-    "prefill_workspace_bytes", "tree_workspace_bytes", "conv_update", "decode_step", "tree_verify", "commit_path",
+    "prefill_workspace_bytes", "tree_workspace_bytes", "conv_update", "decode_step", "decode_token", "tree_verify",
+    "commit_path",
     "tree_tables", "prefill_chunked", "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH",
     "PREFILL_CHUNK", "F32", "BF16",
 ]
@@ -65,6 +66,7 @@ _sig = {
     "gdn_prefill_workspace_bytes": ([_D, _I], C.c_size_t),
     "gdn_conv_update": ([_D, _P, _P, _P, _P, _P], C.c_int),
     "gdn_decode_step": ([_D, _P, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_decode_token": ([_D, _P, _P, _P, _P, _P, _P, _P, _P, _P], C.c_int),
     "gdn_tree_workspace_bytes": ([_D, _I], C.c_size_t),
     "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
@@ -142,6 +144,17 @@ def decode_step(d: Dims, state, y, a, b, o, stream=None) -> None:
                                 _t(y, "y", torch.float32, B * Cc), _t(a, "a", torch.float32, B * Hv),
                                 _t(b, "b", torch.float32, B * Hv), _t(o, "o", torch.float32, B * Hv * dv),
                                 _stream(stream)), "gdn_decode_step")
+
+
+def decode_token(d: Dims, state, tail_in, tail_out, w, x, a, b, o, stream=None) -> None:
+    """conv_update + decode_step in one launch; the tail goes from tail_in to tail_out."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_decode_token(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                 _t(tail_in, "conv_tail_in", d.act_torch, B * Cc * 4),
+                                 _t(tail_out, "conv_tail_out", d.act_torch, B * Cc * 4),
+                                 _t(w, "conv_w", d.act_torch, Cc * 4), _t(x, "x", d.act_torch, B * Cc),
+                                 _t(a, "a", torch.float32, B * Hv), _t(b, "b", torch.float32, B * Hv),
+                                 _t(o, "o", torch.float32, B * Hv * dv), _stream(stream)), "gdn_decode_token")
 
 
 def tree_workspace_bytes(d: Dims, n_nodes: int) -> int:

@@ -30,7 +30,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument", "-Wno-unknown-pragmas",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_tree.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_token.hip", "gdn_tree.hip", "gdn_prefill.hip"]
 
 
 def _compile(src: str) -> str:

@@ -15,6 +15,8 @@ struct Geo {
 hipError_t launch_conv_update(const Geo& g, const void* x, void* tail, const void* w, float* y, hipStream_t s);
 hipError_t launch_decode(const Geo& g, float* S, const float* y, const float* a, const float* b, float* o,
                          hipStream_t s);
+hipError_t launch_token(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w, const void* x,
+                        const float* a, const float* b, float* o, hipStream_t s);
 hipError_t launch_tree_tables(int n, const int32_t* parent, int32_t* depth, int32_t* order, int32_t* status,
                               hipStream_t s);
 size_t tree_ws_bytes(int n, int Hk, int Hv, int D);

@@ -64,7 +64,8 @@ typedef enum {
     GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     GDN_ERR_TREE = 5,        /* malformed tree or path (also the device status value) */
     GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
-    GDN_ERR_HIP = 7          /* the HIP runtime refused a launch */
+    GDN_ERR_HIP = 7,         /* the HIP runtime refused a launch */
+    GDN_ERR_ALIAS = 8        /* buffers that must be distinct overlap */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -111,6 +112,23 @@ gdn_status gdn_conv_update(const gdn_dims* d, const void* x, void* conv_tail,
  */
 gdn_status gdn_decode_step(const gdn_dims* d, float* state, const float* y,
                            const float* a, const float* b, float* o, void* stream);
+
+/*
+ * gdn_decode_token -- gdn_conv_update followed by gdn_decode_step, in one
+ * launch (section 8.1: state and 4-wide tail advanced per token; CPU page:
+ * rank-1 update in place, convolution rings).  state and o are bit-identical
+ * to the two calls; conv_tail_out receives exactly what gdn_conv_update would
+ * leave in the tail.  The tail is updated out of place so that no reader of a
+ * channel's window races its writer: the caller alternates two tail buffers.
+ *   state          f32 [B][Hv][dv][dk]  (in/out)
+ *   conv_tail_in   act [B][C][4]        last four raw inputs before this token (read)
+ *   conv_tail_out  act [B][C][4]        the same after this token (written); must not
+ *                                       overlap conv_tail_in (GDN_ERR_ALIAS)
+ *   conv_w act [C][4];  x act [B][C];  a, b f32 [B][Hv];  o f32 [B][Hv][dv] (written)
+ */
+gdn_status gdn_decode_token(const gdn_dims* d, float* state, const void* conv_tail_in, void* conv_tail_out,
+                            const void* conv_w, const void* x, const float* a, const float* b, float* o,
+                            void* stream);
 
 /*
  * gdn_tree_verify -- one read-only pass over a draft tree of n_nodes tokens

@@ -26,7 +26,8 @@ def lib():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for f in ("gdn_conv_update", "gdn_decode_step", "gdn_tree_verify", "gdn_commit_path", "gdn_prefill_chunked"):
+    for f in ("gdn_conv_update", "gdn_decode_step", "gdn_tree_verify", "gdn_commit_path", "gdn_prefill_chunked",
+              "gdn_decode_token"):
         assert f in names
 
 
@@ -114,8 +115,23 @@ def test_tree_sizes_are_refused_before_launch(lib):
     assert lib.gdn_tree_tables(0, fake, fake, fake, fake, None) == 5
 
 
+def test_fused_token_refuses_overlapping_tails(lib):
+    P = C.c_void_p
+    lib.gdn_decode_token.argtypes = [C.POINTER(Dims)] + [P] * 9
+    d = mk()
+    fake = P(0x1000)
+    tail_bytes = 4 * 10240 * 2
+    # same buffer, and a partial overlap
+    assert lib.gdn_decode_token(C.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, None) == 8
+    assert lib.gdn_decode_token(C.byref(d), fake, fake, P(0x1000 + tail_bytes - 16), fake, fake, fake, fake, fake,
+                                None) == 8
+    # bad dims are still refused first
+    assert lib.gdn_decode_token(C.byref(mk(conv_width=3)), fake, fake, P(0x1000000), fake, fake, fake, fake, fake,
+                                None) == 2
+
+
 def test_status_strings(lib):
     lib.gdn_status_str.restype = C.c_char_p
-    for s in range(8):
+    for s in range(9):
         assert lib.gdn_status_str(s)
     assert lib.gdn_abi_version() == 1
