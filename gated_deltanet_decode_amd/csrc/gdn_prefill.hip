@@ -23,16 +23,18 @@
 //         substitution, off-diagonal blocks by block products), then
 //         U~ = T (beta V) and W~ = T (beta e^G K) on MFMA, and P.
 //   scan  (sequential over chunks; one workgroup per (sequence, value head,
-//         16-row slice of the state)): Z = W~ S0^T and Y = Q S0^T, U = U~ - Z,
-//         O = s (e^G Y + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K), all on
-//         16x16x32 fp16 MFMAs, two barriers per chunk.  Four waves carry the
-//         state (fp32, in registers across chunks); four more compute and store
-//         o off the state's critical path.  The next chunk's operands load while
-//         the current one computes.  Workgroups of one q/k head sit on one XCD
-//         and share its L2.
+//         32-row slice of the state), one workgroup per CU): Z = W~ S0^T and
+//         Y = Q S0^T, U = U~ - Z, O = s (e^G Y + P U),
+//         S <- e^{G_n} S + U^T (e^{G_n - G} K), all on 16x16x32 fp16 MFMAs,
+//         two barriers per chunk.  Four waves carry the state (fp32, in
+//         registers across chunks); four more compute and store o off the
+//         state's critical path.  Operands stream through a four-stage
+//         register ring, three chunks ahead.  Workgroups of one q/k head sit
+//         on one XCD and share its L2.
 // The workspace holds one segment (about 114 MB at the 27B-class shape),
 // whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
+#include <utility>
 
 #include "gdn_core.hpp"
 #include "gdn_launch.hpp"
@@ -47,7 +49,7 @@ constexpr int D = 128;       // head width handled by the prefill kernels
 constexpr int CH = 64;       // chunk length
 constexpr int SEG = 2048;    // tokens per segment
 constexpr int TB = 16;       // tokens per conv workgroup
-constexpr int DS = 16;       // state rows per scan workgroup
+constexpr int DS = 32;       // state rows per scan workgroup
 constexpr int NS = D / DS;   // scan workgroups per value head
 constexpr int MP = CH + 1;   // fp32 pitch of a 64x64 matrix row in LDS
 constexpr int HP = CH + 8;   // fp16 pitch of a 64-token row in LDS
@@ -390,21 +392,32 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 
 // ------------------------------------------------------------ scan
 
-// The scan workgroup has two roles of four waves each.  State waves carry the
-// recurrence: Z = W~ S0^T, U = U~ - Z, S <- e^{G_n} S + U^T (e^{G_n - G} K).
-// Output waves compute Y = Q S0^T and P U and store o, in the state waves'
-// shadow: their stores never sit in front of a state wave's loads in the
-// in-order memory counter.  The roles meet at two barriers per chunk; S0 and
-// U^T live in LDS double-buffered by chunk parity.
+// The scan workgroup owns DS rows of one value head's state and has two roles
+// of four waves.  State waves carry the recurrence: Z = W~ S0^T, U = U~ - Z,
+// S <- e^{G_n} S + U^T (e^{G_n - G} K), the state in fp32 registers across
+// chunks.  Output waves compute Y = Q S0^T and P U and store o.  The roles meet
+// at two barriers per chunk; S0 and U^T pass through LDS, double-buffered by
+// chunk parity.
+//
+// The workgroup's operands of a chunk (W~, K^T, Q and P of its head; U~ of its
+// rows) are read once per workgroup, so the chip-wide operand traffic is
+// (value heads x 128 / DS) copies per chunk: DS = 32 keeps it within what the
+// L2 delivers while one workgroup per CU keeps every state slice resident.
+// Each wave streams its operands through a ring of kScanRing register stages,
+// so the chunk it computes was requested kScanRing - 1 chunks earlier.  The
+// chunk loop body holds kScanRing chunks, which keeps every ring slot in fixed
+// registers while the code stays small enough for the instruction cache.
+constexpr int kScanRing = 4;
+
 struct alignas(16) ScanSmem {
     _Float16 s0[2][DS][D + 8];   // S0 slice, fp16, [row][key]
-    _Float16 ut[2][DS][HP];      // U^T
+    _Float16 ut[2][DS][HP];      // U^T [row][t]
     _Float16 utd[DS][HP];        // U^T scaled by e^{G_last - G} (state waves only)
 };
 
 struct StateOps {
     h8 wf[4], kf[2][2];
-    uint2 u;       // four fp16 U~ values
+    uint2 u[DS / 16];   // four fp16 U~ values per row tile
     f4 egd;
     float eglast;
 };
@@ -430,7 +443,10 @@ __device__ __forceinline__ void load_state(StateOps& op, const Ws& ws, const Sca
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
             op.kf[tt][s] = ld8(ws.kt + ((c.ktbase + cl) * D + 16 * (2 * c.w + tt) + c.lr) * CH + 32 * s + 8 * c.lq);
-    op.u = *reinterpret_cast<const uint2*>(ws.ut + ((c.utbase + cl) * D + c.row0 + c.lr) * CH + 16 * c.w + 4 * c.lq);
+#pragma unroll
+    for (int it = 0; it < DS / 16; ++it)
+        op.u[it] = *reinterpret_cast<const uint2*>(ws.ut + ((c.utbase + cl) * D + c.row0 + 16 * it + c.lr) * CH +
+                                                   16 * c.w + 4 * c.lq);
     op.egd = *reinterpret_cast<const f4*>(ws.egd + c.hbase + s0 + 16 * c.w + 4 * c.lq);
     op.eglast = ws.eg[c.hbase + s0 + CH - 1];
 }
@@ -447,7 +463,8 @@ __device__ __forceinline__ void load_out(OutOps& op, const Ws& ws, const ScanCtx
     op.eg = *reinterpret_cast<const f4*>(ws.eg + c.hbase + s0 + 16 * c.w + 4 * c.lq);
 }
 
-// x S0^T for one 16-token tile, keys split into two independent chains.
+// x S0^T for one 16-token tile and the 16 state rows starting at s0, keys
+// split into two independent chains.
 __device__ __forceinline__ f4 times_s0(const h8 (&a)[4], const _Float16 (*s0)[D + 8], int lr, int lq) {
     f4 z0 = zero4(), z1 = zero4();
     z0 = mma(a[0], ld8(&s0[lr][8 * lq]), z0);
@@ -457,60 +474,77 @@ __device__ __forceinline__ f4 times_s0(const h8 (&a)[4], const _Float16 (*s0)[D 
     return z0 + z1;
 }
 
-__device__ __forceinline__ void state_chunk(const StateOps& op, ScanSmem& sm, f4 (&sacc)[2], const ScanCtx& c,
-                                            int par) {
+// sacc[it][tt]: rows 16*it.., keys 16*(2w+tt).. of the slice (C layout: row
+// 4*lq + r, column lr).
+template <int PAR>
+__device__ __forceinline__ void state_chunk(const StateOps& op, ScanSmem& sm, f4 (&sacc)[DS / 16][2],
+                                            const ScanCtx& c) {
     const int w = c.w, lr = c.lr, lq = c.lq;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int it = 0; it < DS / 16; ++it)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sm.s0[par][4 * lq + r][16 * (2 * w + tt) + lr] = static_cast<_Float16>(sacc[tt][r]);
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sm.s0[PAR][16 * it + 4 * lq + r][16 * (2 * w + tt) + lr] = static_cast<_Float16>(sacc[it][tt][r]);
     __syncthreads();
-    const f4 Z = times_s0(op.wf, sm.s0[par], lr, lq);
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const h4 uh = __builtin_bit_cast(h4, op.u);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * lq + r;
-        const float U = static_cast<float>(uh[r]) - Z[r];
-        sm.ut[par][lr][t] = static_cast<_Float16>(U);
-        sm.utd[lr][t] = static_cast<_Float16>(U * op.egd[r]);
+    for (int it = 0; it < DS / 16; ++it) {
+        const f4 Z = times_s0(op.wf, &sm.s0[PAR][16 * it], lr, lq);
+        const h4 uh = __builtin_bit_cast(h4, op.u[it]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * lq + r;
+            const float U = static_cast<float>(uh[r]) - Z[r];
+            sm.ut[PAR][16 * it + lr][t] = static_cast<_Float16>(U);
+            sm.utd[16 * it + lr][t] = static_cast<_Float16>(U * op.egd[r]);
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int it = 0; it < DS / 16; ++it)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sacc[tt][r] *= op.eglast;
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            sacc[tt] = mma(ld8(&sm.utd[lr][32 * s + 8 * lq]), op.kf[tt][s], sacc[tt]);
-    }
+            for (int r = 0; r < 4; ++r)
+                sacc[it][tt][r] *= op.eglast;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                sacc[it][tt] = mma(ld8(&sm.utd[16 * it + lr][32 * s + 8 * lq]), op.kf[tt][s], sacc[it][tt]);
+        }
 }
 
-// orow points at the chunk's first token row of o for this head and slice; only
-// a final partial chunk is MASKED to its n valid tokens.
-template <bool MASKED>
-__device__ __forceinline__ void out_chunk(const OutOps& op, ScanSmem& sm, const ScanCtx& c, int par,
+// orow points at the chunk's first token row of o for this head and slice; a
+// final partial chunk stores only its n valid tokens.
+template <int PAR, bool MASKED>
+__device__ __forceinline__ void out_chunk(const OutOps& op, ScanSmem& sm, const ScanCtx& c,
                                           float* __restrict__ orow, int n, size_t ostride) {
     const int w = c.w, lr = c.lr, lq = c.lq;
     __syncthreads();
-    const f4 Y = times_s0(op.qf, sm.s0[par], lr, lq);
+    f4 Y[DS / 16];
+#pragma unroll
+    for (int it = 0; it < DS / 16; ++it)
+        Y[it] = times_s0(op.qf, &sm.s0[PAR][16 * it], lr, lq);
     __syncthreads();
-    f4 PU = zero4();
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-        PU = mma(op.pf[s], ld8(&sm.ut[par][lr][32 * s + 8 * lq]), PU);
+    for (int it = 0; it < DS / 16; ++it) {
+        f4 PU = zero4();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * lq + r;
-        if (!MASKED || t < n)
-            orow[static_cast<size_t>(t) * ostride + lr] = kScale * __builtin_fmaf(op.eg[r], Y[r], PU[r]);
+        for (int s = 0; s < 2; ++s)
+            PU = mma(op.pf[s], ld8(&sm.ut[PAR][16 * it + lr][32 * s + 8 * lq]), PU);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * lq + r;
+            if (!MASKED || t < n)
+                orow[static_cast<size_t>(t) * ostride + 16 * it + lr] =
+                    kScale * __builtin_fmaf(op.eg[r], Y[it][r], PU[r]);
+        }
     }
 }
 
-__global__ __launch_bounds__(512, 4) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
-                                                   int seg0, int SP, int nch, int B, int Hk, int Hv) {
+__global__ __launch_bounds__(512, 2) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
+                                                      int seg0, int SP, int nch, int B, int Hk, int Hv) {
     __shared__ ScanSmem sm;
     const int G = Hv / Hk;
     // workgroups of one (sequence, q/k head) share an XCD: blockIdx % 8 picks the XCD
@@ -536,67 +570,81 @@ __global__ __launch_bounds__(512, 4) void scan_kernel(float* __restrict__ S, flo
     c.ktbase = (static_cast<size_t>(bq) * Hk + g) * NC;
     const int len = min(SEG, T - seg0);
     const int nfull = len / CH, tailn = len % CH;
+    // Chunk nfull (if tailn > 0) is partial: its workspace rows past the
+    // prompt are zero, so the state waves treat it like any other.
 
-    // Full chunks run with two register stages: chunk cl computes from one while
-    // chunk cl+1 loads into the other.  Loads and stores in these loops are
-    // unconditional (the look-ahead index is clamped), so each wait is for
-    // exactly the stage needed.  A final partial chunk runs masked.
     if (state_role) {
         float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0) * D;
-        f4 sacc[2];
+        f4 sacc[DS / 16][2];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int it = 0; it < DS / 16; ++it)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[tt][r] = Sh[(4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr];
-        StateOps opA, opB;
-        if (nfull > 0)
-            load_state(opA, ws, c, 0);
-        int cl = 0;
-        for (; cl + 1 < nfull; cl += 2) {
-            load_state(opB, ws, c, cl + 1);
-            state_chunk(opA, sm, sacc, c, 0);
-            load_state(opA, ws, c, min(cl + 2, nch - 1));
-            state_chunk(opB, sm, sacc, c, 1);
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sacc[it][tt][r] = Sh[(16 * it + 4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr];
+        StateOps ring[kScanRing];
+#pragma unroll
+        for (int p = 0; p < kScanRing; ++p)
+            load_state(ring[p], ws, c, min(p, nch - 1));
+        // chunk cl uses ring slot cl % kScanRing and LDS parity cl & 1, both
+        // fixed per position in the unrolled body because cl0 % kScanRing == 0
+        auto step = [&](auto pc, int cl) {
+            constexpr int P = decltype(pc)::value;
+            state_chunk<P & 1>(ring[P], sm, sacc, c);
+            load_state(ring[P], ws, c, min(cl + kScanRing, nch - 1));
+        };
+        int cl0 = 0;
+        for (; cl0 + kScanRing <= nch; cl0 += kScanRing) {
+            step(std::integral_constant<int, 0>{}, cl0);
+            step(std::integral_constant<int, 1>{}, cl0 + 1);
+            step(std::integral_constant<int, 2>{}, cl0 + 2);
+            step(std::integral_constant<int, 3>{}, cl0 + 3);
         }
-        if (cl < nfull) {
-            state_chunk(opA, sm, sacc, c, cl & 1);
-            ++cl;
-        }
-        if (tailn > 0) {
-            load_state(opA, ws, c, nfull);
-            state_chunk(opA, sm, sacc, c, cl & 1);
-        }
+        if (cl0 < nch)
+            step(std::integral_constant<int, 0>{}, cl0);
+        if (cl0 + 1 < nch)
+            step(std::integral_constant<int, 1>{}, cl0 + 1);
+        if (cl0 + 2 < nch)
+            step(std::integral_constant<int, 2>{}, cl0 + 2);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int it = 0; it < DS / 16; ++it)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Sh[(4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr] = sacc[tt][r];
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Sh[(16 * it + 4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr] = sacc[it][tt][r];
     } else {
         const size_t ostride = static_cast<size_t>(Hv) * D;
         float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
-        OutOps opA, opB;
-        if (nfull > 0)
-            load_out(opA, ws, c, 0);
-        int cl = 0;
-        for (; cl + 1 < nfull; cl += 2) {
-            load_out(opB, ws, c, cl + 1);
-            out_chunk<false>(opA, sm, c, 0, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
-            load_out(opA, ws, c, min(cl + 2, nch - 1));
-            out_chunk<false>(opB, sm, c, 1, obase + static_cast<size_t>(cl + 1) * CH * ostride, CH, ostride);
+        OutOps ring[kScanRing];
+#pragma unroll
+        for (int p = 0; p < kScanRing; ++p)
+            load_out(ring[p], ws, c, min(p, nch - 1));
+        auto step = [&](auto pc, int cl) {
+            constexpr int P = decltype(pc)::value;
+            float* orow = obase + static_cast<size_t>(cl) * CH * ostride;
+            if (cl < nfull)
+                out_chunk<P & 1, false>(ring[P], sm, c, orow, CH, ostride);
+            else
+                out_chunk<P & 1, true>(ring[P], sm, c, orow, tailn, ostride);
+            load_out(ring[P], ws, c, min(cl + kScanRing, nch - 1));
+        };
+        int cl0 = 0;
+        for (; cl0 + kScanRing <= nch; cl0 += kScanRing) {
+            step(std::integral_constant<int, 0>{}, cl0);
+            step(std::integral_constant<int, 1>{}, cl0 + 1);
+            step(std::integral_constant<int, 2>{}, cl0 + 2);
+            step(std::integral_constant<int, 3>{}, cl0 + 3);
         }
-        if (cl < nfull) {
-            out_chunk<false>(opA, sm, c, cl & 1, obase + static_cast<size_t>(cl) * CH * ostride, CH, ostride);
-            ++cl;
-        }
-        if (tailn > 0) {
-            load_out(opA, ws, c, nfull);
-            out_chunk<true>(opA, sm, c, cl & 1, obase + static_cast<size_t>(nfull) * CH * ostride, tailn, ostride);
-        }
+        if (cl0 < nch)
+            step(std::integral_constant<int, 0>{}, cl0);
+        if (cl0 + 1 < nch)
+            step(std::integral_constant<int, 1>{}, cl0 + 1);
+        if (cl0 + 2 < nch)
+            step(std::integral_constant<int, 2>{}, cl0 + 2);
     }
 }
-
-// ------------------------------------------------------------ tail
 
 // New tail = the last four raw inputs of (old tail ++ the prompt).
 template <typename Act>
