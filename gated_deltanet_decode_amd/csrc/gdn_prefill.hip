@@ -101,6 +101,20 @@ __device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mf
 __device__ __forceinline__ h8 ld8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
 __device__ __forceinline__ f4 zero4() { return f4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// Prefill stores q^, k^ and v as fp16 (relative step 2^-11), so its conv and
+// norm use the hardware exp2, reciprocal and reciprocal square root (about one
+// ulp of fp32 each) instead of the correctly rounded library calls the
+// token-by-token path shares.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float conv_silu_fast(const float w[4], const float win[4]) {
+    float acc = w[0] * win[0];
+    acc = __builtin_fmaf(w[1], win[1], acc);
+    acc = __builtin_fmaf(w[2], win[2], acc);
+    acc = __builtin_fmaf(w[3], win[3], acc);
+    return acc * __builtin_amdgcn_rcpf(1.0f + fast_exp(-acc));
+}
+
 // ------------------------------------------------------------ conv + norm
 
 template <typename Act>
@@ -140,7 +154,7 @@ __global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, co
         float yv[TB];
 #pragma unroll
         for (int j = 0; j < TB; ++j)
-            yv[j] = (t0 + j < T) ? conv_silu(wf, &hist[j]) : 0.0f;
+            yv[j] = (t0 + j < T) ? conv_silu_fast(wf, &hist[j]) : 0.0f;
         if (ch < 2 * D) {
 #pragma unroll
             for (int j = 0; j < TB; ++j)
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, co
         const float e0 = ys[tl][which * D + lane];
         const float e1 = ys[tl][which * D + lane + kWave];
         const float ss = group_sum<kWave>(__builtin_fmaf(e1, e1, e0 * e0));
-        const float r = 1.0f / sqrtf(ss + kEps);
+        const float r = __builtin_amdgcn_rsqf(ss + kEps);
         const _Float16 h0 = static_cast<_Float16>(e0 * r), h1 = static_cast<_Float16>(e1 * r);
         _Float16* gdst = (which ? ws.k : ws.q) + ((static_cast<size_t>(bq) * Hk + g) * SP + sl + tl) * D;
         gdst[lane] = h0;
@@ -192,7 +206,7 @@ struct alignas(16) TriSmem {
     float A[CH][MP];
     float T[CH][MP];
     float tmp[3][16][17];
-    float G[CH];
+    float G[CH];     // cumulative log2 decay inside the chunk
     float beta[CH];
     float bv[CH];    // beta_t            (scales V in U~)
     float bk[CH];    // beta_t e^{G_t}    (scales K in W~)
@@ -258,14 +272,15 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
             if (lane >= off)
                 la += up;
         }
-        const float glast = __shfl(la, kWave - 1, kWave);
-        const float eg = expf(la);
-        sm.G[lane] = la;
+        const float l2 = la * kLog2e;             // G in log2 units
+        const float glast = __shfl(l2, kWave - 1, kWave);
+        const float eg = __builtin_amdgcn_exp2f(l2);
+        sm.G[lane] = l2;
         sm.beta[lane] = be;
         sm.bv[lane] = be;
         sm.bk[lane] = be * eg;
         ws.eg[hs + lane] = eg;
-        ws.egd[hs + lane] = expf(glast - la);
+        ws.egd[hs + lane] = __builtin_amdgcn_exp2f(glast - l2);
     }
     __syncthreads();
 
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = i0 + r;
-                const float dg = (i >= j) ? expf(sm.G[i] - sm.G[j]) : 0.0f;
+                const float dg = (i >= j) ? __builtin_amdgcn_exp2f(sm.G[i] - sm.G[j]) : 0.0f;
                 Pm[i * CH + j] = static_cast<_Float16>(dg * qk[r]);
                 sm.A[i][j] = (i > j) ? sm.beta[i] * dg * kk[r] : 0.0f;
             }
