@@ -71,38 +71,69 @@ struct alignas(16) NodeSmem {
     int32_t ok;
 };
 
-// Fill conv outputs, normalised q/k, k.q and gates for tokens 0..count-1 from
-// sm.node, sm.depth and sm.anc.  Every global load is issued before any is
-// used: each thread requests its channel's raw input at every token at once.
+// Conv outputs, normalised q/k, k.q and gates for tokens 0..count-1 (from
+// sm.node, sm.depth and sm.anc), in two steps so that the caller can overlap
+// other work with the loads: fill_issue requests every global input into
+// registers at once (each thread its channels' raw inputs at every token),
+// fill_finish stores them to LDS, convolves, normalises and computes gates.
 template <int D, int ROWS, int MAXN, typename Act>
-__device__ void fill_nodes(NodeSmem<D, ROWS, MAXN, Act>& sm, int count, const Act* __restrict__ x,
-                           const Act* __restrict__ tail, const Act* __restrict__ w, const float* __restrict__ a,
-                           const float* __restrict__ b, int Hk, int Hv, int C, int grp, int h, int row0) {
-    constexpr int PER = NodeSmem<D, ROWS, MAXN, Act>::PER;
-    if (threadIdx.x < MAXN) {
+struct FillRegs {
+    static constexpr int PER = NodeSmem<D, ROWS, MAXN, Act>::PER;
+    static constexpr int SLOTS = (PER + 255) / 256;
+    Act r[SLOTS][MAXN];
+    typename Quad<Act>::raw tq[SLOTS], wq[SLOTS];
+    float ga, gb;
+};
+
+template <int D, int ROWS, int MAXN, typename Act>
+__device__ __forceinline__ void fill_issue(FillRegs<D, ROWS, MAXN, Act>& f, const NodeSmem<D, ROWS, MAXN, Act>& sm,
+                                           int count, const Act* __restrict__ x, const Act* __restrict__ tail,
+                                           const Act* __restrict__ w, const float* __restrict__ a,
+                                           const float* __restrict__ b, int Hk, int Hv, int C, int grp, int h,
+                                           int row0) {
+    constexpr int PER = FillRegs<D, ROWS, MAXN, Act>::PER;
+    {
         const int i = threadIdx.x < count ? threadIdx.x : count - 1;
-        const size_t gi = static_cast<size_t>(sm.node[i]) * Hv + h;
-        sm.ga[threadIdx.x] = a[gi];
-        sm.gb[threadIdx.x] = b[gi];
+        const size_t gi = static_cast<size_t>(sm.node[i < MAXN ? i : MAXN - 1]) * Hv + h;
+        f.ga = a[gi];
+        f.gb = b[gi];
     }
-    for (int ch = threadIdx.x; ch < PER; ch += blockDim.x) {
+#pragma unroll
+    for (int k = 0; k < FillRegs<D, ROWS, MAXN, Act>::SLOTS; ++k) {
+        const int ch0 = threadIdx.x + 256 * k;
+        const int ch = ch0 < PER ? ch0 : PER - 1;   // clamped: loads stay unconditional
         const int c = ch < D ? grp * D + ch : ch < 2 * D ? Hk * D + grp * D + (ch - D) : 2 * Hk * D + h * D + row0 + (ch - 2 * D);
-        Act r[MAXN];
 #pragma unroll
         for (int i = 0; i < MAXN; ++i)
-            r[i] = x[static_cast<size_t>(sm.node[i < count ? i : count - 1]) * C + c];
-        const typename Quad<Act>::raw tq = Quad<Act>::load(tail + static_cast<size_t>(c) * 4);
-        float wf[4];
-        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
+            f.r[k][i] = x[static_cast<size_t>(sm.node[i < count ? i : count - 1]) * C + c];
+        f.tq[k] = Quad<Act>::load(tail + static_cast<size_t>(c) * 4);
+        f.wq[k] = Quad<Act>::load(w + static_cast<size_t>(c) * 4);
+    }
+}
+
+template <int D, int ROWS, int MAXN, typename Act>
+__device__ void fill_finish(const FillRegs<D, ROWS, MAXN, Act>& f, NodeSmem<D, ROWS, MAXN, Act>& sm, int count) {
+    constexpr int PER = FillRegs<D, ROWS, MAXN, Act>::PER;
+    if (threadIdx.x < MAXN) {
+        sm.ga[threadIdx.x] = f.ga;
+        sm.gb[threadIdx.x] = f.gb;
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sm.tl[ch][j] = Quad<Act>::elem(tq, j);
-            sm.wl[ch][j] = wf[j];
+    for (int k = 0; k < FillRegs<D, ROWS, MAXN, Act>::SLOTS; ++k) {
+        const int ch = threadIdx.x + 256 * k;
+        if (ch < PER) {
+            float wf[4];
+            Quad<Act>::to_float(f.wq[k], wf);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sm.tl[ch][j] = Quad<Act>::elem(f.tq[k], j);
+                sm.wl[ch][j] = wf[j];
+            }
+#pragma unroll
+            for (int i = 0; i < MAXN; ++i)
+                if (i < count)
+                    sm.xr[i][ch] = f.r[k][i];
         }
-#pragma unroll
-        for (int i = 0; i < MAXN; ++i)
-            if (i < count)
-                sm.xr[i][ch] = r[i];
     }
     __syncthreads();
     // conv + SiLU per (token, channel), from LDS only
@@ -488,28 +519,35 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     for (int j = 0; j < NV; ++j)
         s[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
 
-    if (wave == 0) {
+    // Token i of the commit is path position i; its ancestors are the
+    // positions before it.  Node ids are clamped into the tree so that every
+    // load below stays in bounds whatever the path holds; a malformed path is
+    // rejected before anything is written.
+    if (threadIdx.x < kMaxDepth) {
+        const int i = threadIdx.x < L ? threadIdx.x : L - 1;
+        int nd = path[i];
+        nd = nd < 0 ? 0 : nd >= n ? n - 1 : nd;
+        sm.node[threadIdx.x] = nd;
+        sm.depth[threadIdx.x] = threadIdx.x + 1;
+#pragma unroll
+        for (int k = 1; k <= 3; ++k)
+            sm.anc[threadIdx.x][k - 1] = threadIdx.x - k;
+    }
+    __syncthreads();
+    FillRegs<D, ROWS, kMaxDepth, Act> fr;
+    fill_issue<D, ROWS, kMaxDepth, Act>(fr, sm, L, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
+    if (wave == 0) {   // validation overlaps the loads just issued
         bool ok = tree_tables_wave(n, parent, nullptr, nullptr);
         ok = ok && path_check_wave(n, parent, L, path);
-        if (lane < L) {
-            // token i of the commit is path position i: its ancestors are the positions before it
-            sm.node[lane] = ok ? path[lane] : 0;
-            sm.depth[lane] = lane + 1;
-#pragma unroll
-            for (int k = 1; k <= 3; ++k)
-                sm.anc[lane][k - 1] = lane - k;
-        }
         if (lane == 0) {
             sm.ok = ok ? 1 : 0;
             if (status && blockIdx.x == 0)
                 *status = ok ? 0 : 5;
         }
     }
-    __syncthreads();
+    fill_finish<D, ROWS, kMaxDepth, Act>(fr, sm, L);
     if (!sm.ok)
         return;
-
-    fill_nodes<D, ROWS, kMaxDepth, Act>(sm, L, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
 
     TokOps<D> cur, nxt;
     tok_load(cur, sm, 0, r, lrow);
@@ -526,29 +564,38 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
 }
 
 // The tail after a commit holds the last four raw inputs of (old tail ++ path).
+// Path node ids are clamped into the tree so the loads can be issued before
+// the path is validated; nothing is written unless it is valid.
 template <typename Act>
 __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail, int n,
                                                           const int32_t* __restrict__ parent,
                                                           const Act* __restrict__ x, int L,
                                                           const int32_t* __restrict__ path, int C) {
     __shared__ int32_t ok_s;
-    __shared__ int32_t path_s[kMaxDepth];
+    const int c0 = blockIdx.x * blockDim.x + threadIdx.x;
+    const int c = c0 < C ? c0 : C - 1;
+    using Q = Quad<Act>;
+    typename Q::raw t = Q::load(tail + static_cast<size_t>(c) * 4);
+    Act xin[kMaxDepth];
+#pragma unroll
+    for (int j = 0; j < kMaxDepth; ++j) {
+        int nd = path[j < L ? j : L - 1];
+        nd = nd < 0 ? 0 : nd >= n ? n - 1 : nd;
+        xin[j] = x[static_cast<size_t>(nd) * C + c];
+    }
     if (threadIdx.x < kWave) {
         bool ok = tree_tables_wave(n, parent, nullptr, nullptr);
         ok = ok && path_check_wave(n, parent, L, path);
-        if (threadIdx.x < L)
-            path_s[threadIdx.x] = ok ? path[threadIdx.x] : 0;
         if (threadIdx.x == 0)
             ok_s = ok ? 1 : 0;
     }
     __syncthreads();
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (!ok_s || c >= C)
+    if (!ok_s || c0 >= C)
         return;
-    using Q = Quad<Act>;
-    typename Q::raw t = Q::load(tail + static_cast<size_t>(c) * 4);
-    for (int j = 0; j < L; ++j)
-        t = Q::push(t, x[static_cast<size_t>(path_s[j]) * C + c]);
+#pragma unroll
+    for (int j = 0; j < kMaxDepth; ++j)
+        if (j < L)
+            t = Q::push(t, xin[j]);
     Q::store(tail + static_cast<size_t>(c) * 4, t);
 }
 
