@@ -118,14 +118,24 @@ __device__ __forceinline__ float conv_silu_fast(const float w[4], const float wi
 // ------------------------------------------------------------ conv + norm
 
 template <typename Act>
-__global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, const Act* __restrict__ tail,
+__global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, const Act* __restrict__ tail,
                                                    const Act* __restrict__ w, Ws ws, int T, int seg0, int SP,
-                                                   int nblk, int Hk, int Hv, int C) {
+                                                   int nblk, int B, int Hk, int Hv, int C) {
     __shared__ float ys[TB][2 * D];                  // q~ | k~ of the block, fp32
     __shared__ __align__(16) _Float16 khs[TB][D];    // k^ of the block, fp16
-    const int tb = blockIdx.x % nblk;
-    const int g = (blockIdx.x / nblk) % Hk;
-    const int bq = blockIdx.x / (nblk * Hk);
+    // The CH / TB blocks of one chunk write disjoint pieces of the same
+    // 128-byte lines of v^T and k^T.  They share an XCD (blockIdx % 8 picks
+    // it), so the pieces merge in one L2 instead of reaching memory as
+    // partial lines.
+    constexpr int BPC = CH / TB;                     // blocks per chunk
+    const int nch = nblk / BPC;
+    const int xcd = blockIdx.x % 8, r8 = blockIdx.x / 8;
+    const int chunk_id = (r8 / BPC) * 8 + xcd;       // (sequence, q/k head, chunk of the segment)
+    if (chunk_id >= B * Hk * nch)
+        return;
+    const int tb = (chunk_id % nch) * BPC + r8 % BPC;
+    const int g = (chunk_id / nch) % Hk;
+    const int bq = chunk_id / (nch * Hk);
     const int G = Hv / Hk;
     const int NC = SP / CH;
     const int t0 = seg0 + tb * TB;                   // prompt index of the block's first token
@@ -137,24 +147,36 @@ __global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, co
     const Act* tbq = tail + static_cast<size_t>(bq) * C * 4;
     const int per_group = (2 + G) * D;
 
-    for (int ch = threadIdx.x; ch < per_group; ch += blockDim.x) {
-        const int c = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
-        float wf[4];
-        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
-        float hist[TB + 3];
+    // Two channels per thread (the block has per_group / 2 threads); the
+    // window loads of both are issued before either is used.
+    int chs[2], cs[2];
+    float wfs[2][4];
+    float hist[2][TB + 3];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int ch0 = threadIdx.x + k * blockDim.x;
+        const int ch = ch0 < per_group ? ch0 : per_group - 1;
+        chs[k] = ch0;
+        cs[k] = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
+        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(cs[k]) * 4), wfs[k]);
         // unconditional loads from selected addresses: all of them in flight at once
 #pragma unroll
         for (int m = 0; m < TB + 3; ++m) {
             const int t = t0 + m - 3;
             const int tc = t < T ? t : T - 1;
-            const Act* src = t < 0 ? tbq + static_cast<size_t>(c) * 4 + 4 + t : xb + static_cast<size_t>(tc) * C + c;
-            const float v = widen(*src);
-            hist[m] = t < T ? v : 0.0f;
+            const Act* src = t < 0 ? tbq + static_cast<size_t>(cs[k]) * 4 + 4 + t : xb + static_cast<size_t>(tc) * C + cs[k];
+            hist[k][m] = widen(*src);
         }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int ch = chs[k];
+        if (ch >= per_group)
+            continue;
         float yv[TB];
 #pragma unroll
         for (int j = 0; j < TB; ++j)
-            yv[j] = (t0 + j < T) ? conv_silu_fast(wf, &hist[j]) : 0.0f;
+            yv[j] = (t0 + j < T) ? conv_silu_fast(wfs[k], &hist[k][j]) : 0.0f;
         if (ch < 2 * D) {
 #pragma unroll
             for (int j = 0; j < TB; ++j)
@@ -174,7 +196,8 @@ __global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, co
         }
     }
     __syncthreads();
-    for (int vec = wave; vec < 2 * TB; vec += 4) {
+    const int nwaves = blockDim.x / kWave;
+    for (int vec = wave; vec < 2 * TB; vec += nwaves) {
         const int tl = vec >> 1, which = vec & 1;
         const float e0 = ys[tl][which * D + lane];
         const float e1 = ys[tl][which * D + lane + kWave];
@@ -190,8 +213,8 @@ __global__ __launch_bounds__(256) void conv_kernel(const Act* __restrict__ x, co
         }
     }
     __syncthreads();
-    {
-        const int d = threadIdx.x >> 1, half = threadIdx.x & 1;
+    for (int idx = threadIdx.x; idx < 2 * D; idx += blockDim.x) {
+        const int d = idx >> 1, half = idx & 1;
         h8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -700,15 +723,17 @@ hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int
         const int len = std::min(pf::SEG, T - seg0);
         const int nch = (len + pf::CH - 1) / pf::CH;
         const int nblk = nch * (pf::CH / pf::TB);
-        const dim3 cgrid(static_cast<unsigned>(g.B * g.Hk * nblk));
+        const int chunks = g.B * g.Hk * nch;
+        const dim3 cgrid(static_cast<unsigned>(8 * ((chunks + 7) / 8) * (pf::CH / pf::TB)));
+        const dim3 cblock(static_cast<unsigned>(((2 + G) * pf::D / 2 + kWave - 1) / kWave * kWave));
         if (g.bf16)
-            hipLaunchKernelGGL(pf::conv_kernel<uint16_t>, cgrid, block, 0, s, static_cast<const uint16_t*>(x),
+            hipLaunchKernelGGL(pf::conv_kernel<uint16_t>, cgrid, cblock, 0, s, static_cast<const uint16_t*>(x),
                                static_cast<const uint16_t*>(tail), static_cast<const uint16_t*>(w), W, T, seg0, SP,
-                               nblk, g.Hk, g.Hv, g.C);
+                               nblk, g.B, g.Hk, g.Hv, g.C);
         else
-            hipLaunchKernelGGL(pf::conv_kernel<float>, cgrid, block, 0, s, static_cast<const float*>(x),
+            hipLaunchKernelGGL(pf::conv_kernel<float>, cgrid, cblock, 0, s, static_cast<const float*>(x),
                                static_cast<const float*>(tail), static_cast<const float*>(w), W, T, seg0, SP, nblk,
-                               g.Hk, g.Hv, g.C);
+                               g.B, g.Hk, g.Hv, g.C);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
