@@ -48,7 +48,9 @@ enum { ORACLE_OK = 0, ORACLE_ERR_ARG = 1, ORACLE_ERR_TREE = 2 };
 
 /* ------------------------------------------------------------ storage widening */
 
-/* bf16 is the top half of an IEEE binary32; widening is exact. */
+/* bf16 is the top half of an IEEE binary32; widening is exact ("Serving a
+ * research architecture on CPU", exactness paragraphs: 16-bit stored values
+ * are converted exactly before arithmetic). */
 double oracle_bf16_to_f64(uint16_t h)
 {
     uint32_t bits = (uint32_t)h << 16;
@@ -104,7 +106,10 @@ static void mark_needed(const geom* g, int h_lo, int h_hi, unsigned char* need)
 
 /* One token of the causal depthwise conv.  tail[c][0..W-1] holds the last W
  * raw inputs, oldest first; it shifts by one and takes x[c] as the newest,
- * then y[c] = SiLU(sum_j w[c][j] * tail[c][j]) for the channels marked. */
+ * then y[c] = SiLU(sum_j w[c][j] * tail[c][j]) for the channels marked.
+ * ("Architecture" section 8.1 table: a 4-wide convolution tail per layer;
+ * CPU page, constant-state paragraph: short convolutions keep rings of
+ * recent inputs.) */
 static void conv_token(const geom* g, double* tail, const void* w, int w_bf16,
                        const void* x, int x_bf16, size_t x_off,
                        const unsigned char* need, double* y)
@@ -124,7 +129,10 @@ static void conv_token(const geom* g, double* tail, const void* w, int w_bf16,
 }
 
 /* One token of the recurrence for v heads [h_lo, h_hi), given the conv output
- * y.  S is [Hv][dv][dk]; o (nullable) is [Hv][dv]. */
+ * y.  S is [Hv][dv][dk]; o (nullable) is [Hv][dv].  ("Architecture" section
+ * 8.1: a fixed-size fp32 state per head, advanced per token; CPU page,
+ * constant-state paragraph: a rank-1 outer-product update of each head's
+ * square state, in place.) */
 static void recur_token(const geom* g, double* S, const double* y, const double* a, const double* b,
                         double* o, int h_lo, int h_hi, double* qh, double* kh)
 {
@@ -173,7 +181,9 @@ static void recur_token(const geom* g, double* S, const double* y, const double*
 /* ------------------------------------------------------------ exported calls */
 
 /*
- * oracle_run: T tokens of one sequence from (S, tail), in place.
+ * oracle_run: T tokens of one sequence from (S, tail), in place: the
+ * token-by-token definition (CPU page, exactness paragraphs: the scalar path
+ * is what the fast paths answer to).
  *   S     double [Hv][dv][dk]          in/out
  *   tail  double [C][W]                in/out (raw inputs, oldest first)
  *   w     act   [C][W]   (bf16 bits if w_bf16 else float)
@@ -216,7 +226,7 @@ int oracle_run(int Hk, int Hv, int dk, int dv, int W,
 }
 
 /*
- * oracle_recur: one token of the recurrence alone, from a given conv output
+ * oracle_recur (same passages as recur_token): one token of the recurrence alone, from a given conv output
  * y[C] (already split as q|k|v) and gate inputs a[Hv], b[Hv].  All heads.
  */
 int oracle_recur(int Hk, int Hv, int dk, int dv, double* S, const double* y,
@@ -240,7 +250,7 @@ int oracle_recur(int Hk, int Hv, int dk, int dv, double* S, const double* y,
 }
 
 /*
- * oracle_conv: T tokens of the conv alone over all C channels.
+ * oracle_conv (same passages as conv_token): T tokens of the conv alone over all C channels.
  *   tail double [C][W] in/out; y double [T][C].
  */
 int oracle_conv(int C, int W, double* tail, const void* w, int w_bf16,
@@ -261,7 +271,9 @@ int oracle_conv(int C, int W, double* tail, const void* w, int w_bf16,
 }
 
 /*
- * Draft-tree tables.  A tree of n nodes is a parent array: parent[0] == -1
+ * Draft-tree tables (repository "Architecture" page, decode-loop diagram: a
+ * draft tree of up to 32 nodes grown from the last committed token).  A tree
+ * of n nodes is a parent array: parent[0] == -1
  * (node 0 is the root, the last committed token) and 0 <= parent[i] < i for
  * i > 0.  depth[root] = 1; depth[i] = depth[parent[i]] + 1 <= max_depth.
  * order[] is the depth-first pre-order that visits children in increasing
@@ -296,7 +308,10 @@ int oracle_tree_tables(int n, const int32_t* parent, int max_depth, int32_t* dep
 }
 
 /*
- * oracle_tree_verify: for every node, the output o at that node after running
+ * oracle_tree_verify (repository "Architecture" page, decode-loop diagram:
+ * the whole tree is verified in one pass and the model's token is produced at
+ * every node; "Architecture" section 8.1: the state is branched for a tree of
+ * guesses): for every node, the output o at that node after running
  * the root-first path to it from copies of the checkpoint (S_c, tail_c).  The
  * checkpoint is not modified.  o is [n][Hv][dv]; heads outside [h_lo, h_hi)
  * are left untouched.  Brute force: each node replays its own path.
@@ -342,7 +357,9 @@ done:
 }
 
 /*
- * oracle_commit_path: advance (S, tail) in place over an accepted root-first
+ * oracle_commit_path ("Architecture" section 8.1: exact undo and branch of
+ * the recurrent state; decode-loop diagram: the accepted tokens are committed):
+ * advance (S, tail) in place over an accepted root-first
  * path of the tree (path[0] == 0, parent[path[j]] == path[j-1]).  This is the
  * sequential definition over the path's tokens.  On an invalid path nothing is
  * modified and ORACLE_ERR_TREE is returned.

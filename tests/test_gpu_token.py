@@ -85,3 +85,34 @@ def test_fused_leaves_tail_in_untouched():
     assert torch.equal(tin, keep)
     with pytest.raises(gdn.GdnError):
         gdn.decode_token(d, S, tin, tin, w, act_to_dev(inp.x[0]), f32_to_dev(inp.a[0]), f32_to_dev(inp.b[0]), o)
+
+
+def test_fused_4096_chained_steps_sampled_heads():
+    """The timed workload's launch configuration: 4,096 chained fused steps at
+    batch 1; the oracle follows q/k heads 0 and 15 (value heads 0-2, 45-47)."""
+    inp = gi.decode_inputs(73, QWEN27B_LAYER, 1, 4096)
+    o, S, tail = run_gpu_token(inp)
+    for lo, hi in ((0, 3), (45, 48)):
+        o_r, S_r, t_r = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:, 0], inp.a[:, 0],
+                                   inp.b[:, 0], h_range=(lo, hi))
+        for t in range(4096):
+            err = normwise(o[t, 0, lo:hi], o_r[t, lo:hi])
+            assert err < TOL, f"heads {lo}-{hi} step {t}: o error {err:.3e}"
+        assert normwise(S[0, lo:hi], S_r[lo:hi]) < TOL
+        assert np.array_equal(oracle.f64(tail[0]), t_r)
+
+
+def test_fused_batch64_256_steps_sampled():
+    """Batch 64, the two-row-quad launch, 256 chained fused steps; sampled
+    sequences and q/k heads against the oracle."""
+    inp = gi.decode_inputs(74, QWEN27B_LAYER, 64, 256)
+    o, S, tail = run_gpu_token(inp)
+    for s in (0, 29, 63):
+        for lo, hi in ((0, 3), (24, 27)):
+            o_r, S_r, t_r = oracle.run(QWEN27B_LAYER, inp.state[s], inp.tail[s], inp.w, inp.x[:, s], inp.a[:, s],
+                                       inp.b[:, s], h_range=(lo, hi))
+            for t in range(256):
+                err = normwise(o[t, s, lo:hi], o_r[t, lo:hi])
+                assert err < TOL, f"seq {s} heads {lo}-{hi} step {t}: o error {err:.3e}"
+            assert normwise(S[s, lo:hi], S_r[lo:hi]) < TOL
+            assert np.array_equal(oracle.f64(tail[s]), t_r)

@@ -180,14 +180,16 @@ def test_commit_without_outputs(case):
     assert torch.equal(S1.view(torch.int32), S2.view(torch.int32)) and torch.equal(t1, t2)
 
 
-@pytest.mark.parametrize("bad", [[1], [0, 0], [0, 31, 1]])
-def test_commit_rejects_bad_path_and_leaves_state(bad):
+@pytest.mark.parametrize("kind", ["not_from_root", "repeated_node", "skips_a_level", "past_the_tree"])
+def test_commit_rejects_bad_path_and_leaves_state(kind):
     inp = gi.tree_inputs(3, QWEN27B_LAYER, n_nodes=32, max_depth=8)
     c = dev_case(inp)
     parent = inp.extra["parent"]
+    n = len(parent)
+    bad = {"not_from_root": [1], "repeated_node": [0, 0],
+           "skips_a_level": [0, next(i for i in range(1, n) if parent[i] != 0)],
+           "past_the_tree": [0, n]}[kind]
     bad = np.array(bad, np.int32)
-    if len(bad) > 1 and all(parent[bad[j]] == bad[j - 1] for j in range(1, len(bad))) and bad[0] == 0:
-        pytest.skip("drawn tree makes this a valid path")
     _, S, t, st = gpu_commit(c, bad, want_o=False)
     assert st == 5
     assert torch.equal(S.view(torch.int32), c["S"].view(torch.int32))

@@ -375,13 +375,21 @@ def test_commit_equals_sequential_decode_of_path(small_tree_case, oracle_lib):
     assert np.array_equal(t_c, hist[-4:].T)
 
 
-@pytest.mark.parametrize("bad", [[1], [0, 5], [0, 1, 1]])
-def test_commit_rejects_non_paths(bad, small_tree_case, oracle_lib):
+@pytest.mark.parametrize("kind", ["not_from_root", "repeated_node", "skips_a_level", "past_the_tree"])
+def test_commit_rejects_non_paths(kind, small_tree_case, oracle_lib):
     shape, inp = small_tree_case
     parent = inp.extra["parent"].copy()
+    n = len(parent)
+    if kind == "not_from_root":
+        bad = [1]
+    elif kind == "repeated_node":
+        bad = [0, 0]
+    elif kind == "skips_a_level":
+        k = next(i for i in range(1, n) if parent[i] != 0)   # a node that is not a child of the root
+        bad = [0, k]
+    else:
+        bad = [0, n]
     bad = np.array(bad, np.int32)
-    if len(bad) > 1 and parent[bad[1]] == bad[0] and (len(bad) < 3 or parent[bad[2]] == bad[1]):
-        pytest.skip("drawn tree makes this a valid path")
     with pytest.raises(oracle.OracleError) as e:
         oracle.commit_path(shape, inp.state[0], inp.tail[0], inp.w, parent, inp.x[:, 0], inp.a[:, 0],
                            inp.b[:, 0], bad)
