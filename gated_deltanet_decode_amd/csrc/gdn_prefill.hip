@@ -56,15 +56,17 @@ constexpr int HP = CH + 8;   // fp16 pitch of a 64-token row in LDS
 constexpr float kScale = Scale<D>::value;
 
 // Workspace of one segment; SP = token pitch (segment length rounded to 64),
-// NC = SP / 64 chunks.
-//   q, k  fp16 [B][Hk][SP][D]        normalised q^, k^ (zero past the prompt)
-//   kt    fp16 [B][Hk][NC][D][64]    k^ transposed per chunk
-//   vt    fp16 [B][Hv][NC][D][64]    v transposed per chunk
-//   ut    fp16 [B][Hv][NC][D][64]    U~ = T (beta V), transposed per chunk
-//   wt    fp16 [B][Hv][SP][D]        W~ = T (beta e^G K)
-//   P     fp16 [B][Hv][NC][64][64]
-//   eg    f32  [B][Hv][SP]           e^{G_t}
-//   egd   f32  [B][Hv][SP]           e^{G_last - G_t}
+// NC = SP / 64 chunks.  Every chunk operand is stored in the order the MFMA
+// fragments read it (a_off / b_off / c_off below), so that each wave's
+// operand load is one contiguous run of 64 lanes x 16 bytes:
+//   q, k  fp16 [B][Hk][NC][64 x 128 A order]   normalised q^, k^ (zero past the prompt)
+//   kt    fp16 [B][Hk][NC][64 x 128 B order]   k^ with the token index as k
+//   vt    fp16 [B][Hv][NC][64 x 128 B order]   v with the token index as k
+//   ut    fp16 [B][Hv][NC][64 x 128 C order]   U~ = T (beta V)
+//   wt    fp16 [B][Hv][NC][64 x 128 A order]   W~ = T (beta e^G K)
+//   P     fp16 [B][Hv][NC][64 x 64 A order]
+//   eg    f32  [B][Hv][SP]                     e^{G_t}
+//   egd   f32  [B][Hv][SP]                     e^{G_last - G_t}
 struct Ws {
     _Float16 *q, *k, *kt, *vt, *ut, *wt, *P;
     float *eg, *egd;
@@ -101,6 +103,27 @@ __device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mf
 __device__ __forceinline__ h8 ld8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
 __device__ __forceinline__ f4 zero4() { return f4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// Fragment orders of one chunk's matrices for 16x16x32 MFMAs.  A fragment
+// (16 rows x 32 k): lane (lq, lr) holds row lr, k 8 lq .. 8 lq + 7.  B fragment
+// (32 k x 16 columns): lane (lq, lr) holds column lr, k 8 lq .. 8 lq + 7.  C
+// tile (16 x 16): lane (lq, lr) holds rows 4 lq .. 4 lq + 3 of column lr.
+// Tiles are laid out one after another, 64 lanes x 8 (A, B) or x 4 (C) fp16.
+//   a_off: M[row][k], ks k-steps per row tile;  b_off: M[k][col], ks k-steps
+//   per column tile;  c_off: M[row][col], nct column tiles per row tile.
+__device__ __forceinline__ int a_off(int row, int k, int ks) {
+    return (((row >> 4) * ks + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (row & 15)) * 8 + (k & 7);
+}
+__device__ __forceinline__ int b_off(int k, int col, int ks) {
+    return (((col >> 4) * ks + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (col & 15)) * 8 + (k & 7);
+}
+__device__ __forceinline__ int c_off(int row, int col, int nct) {
+    return (((row >> 4) * nct + (col >> 4)) * 64 + ((row & 15) >> 2) * 16 + (col & 15)) * 4 + (row & 3);
+}
+// One A or B fragment of tile `tile` in a fragment-ordered matrix.
+__device__ __forceinline__ h8 ldfrag(const _Float16* m, int tile, int lane) { return ld8(m + tile * 512 + lane * 8); }
+constexpr int kChunkQK = CH * D;   // fp16 elements of one chunk of q, k, k^T, v^T, U~, W~
+constexpr int kChunkP = CH * CH;   // fp16 elements of one chunk of P
+
 // Prefill stores q^, k^ and v as fp16 (relative step 2^-11), so its conv and
 // norm use the hardware exp2, reciprocal and reciprocal square root (about one
 // ulp of fp32 each) instead of the correctly rounded library calls the
@@ -122,7 +145,7 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
                                                    const Act* __restrict__ w, Ws ws, int T, int seg0, int SP,
                                                    int nblk, int B, int Hk, int Hv, int C) {
     __shared__ float ys[TB][2 * D];                  // q~ | k~ of the block, fp32
-    __shared__ __align__(16) _Float16 khs[TB][D];    // k^ of the block, fp16
+    __shared__ __align__(16) _Float16 qkh[2][TB][D]; // q^, k^ of the block, fp16
     // The CH / TB blocks of one chunk write disjoint pieces of the same
     // 128-byte lines of v^T and k^T.  They share an XCD (blockIdx % 8 picks
     // it), so the pieces merge in one L2 instead of reaching memory as
@@ -190,9 +213,10 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
                 lo[j] = static_cast<_Float16>(yv[j]);
                 hi[j] = static_cast<_Float16>(yv[8 + j]);
             }
-            _Float16* dst = ws.vt + (((static_cast<size_t>(bq) * Hv + h) * NC + cl) * D + d) * CH + co;
-            *reinterpret_cast<h8*>(dst) = lo;
-            *reinterpret_cast<h8*>(dst + 8) = hi;
+            // tokens co .. co + 15 of column d: two B-order runs of 8
+            _Float16* vc = ws.vt + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkQK;
+            *reinterpret_cast<h8*>(vc + b_off(co, d, CH / 32)) = lo;
+            *reinterpret_cast<h8*>(vc + b_off(co + 8, d, CH / 32)) = hi;
         }
     }
     __syncthreads();
@@ -203,31 +227,35 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
         const float e1 = ys[tl][which * D + lane + kWave];
         const float ss = group_sum<kWave>(__builtin_fmaf(e1, e1, e0 * e0));
         const float r = __builtin_amdgcn_rsqf(ss + kEps);
-        const _Float16 h0 = static_cast<_Float16>(e0 * r), h1 = static_cast<_Float16>(e1 * r);
-        _Float16* gdst = (which ? ws.k : ws.q) + ((static_cast<size_t>(bq) * Hk + g) * SP + sl + tl) * D;
-        gdst[lane] = h0;
-        gdst[lane + kWave] = h1;
-        if (which) {
-            khs[tl][lane] = h0;
-            khs[tl][lane + kWave] = h1;
-        }
+        qkh[which][tl][lane] = static_cast<_Float16>(e0 * r);
+        qkh[which][tl][lane + kWave] = static_cast<_Float16>(e1 * r);
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 2 * D; idx += blockDim.x) {
-        const int d = idx >> 1, half = idx & 1;
+    // The block is row tile co / 16 of the chunk: q^ and k^ in A order (16
+    // tokens x 8 keys per run), k^ in B order (8 tokens x 1 key per run).
+    const size_t qkc = ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * kChunkQK;
+    for (int idx = threadIdx.x; idx < 2 * TB * D / 8; idx += blockDim.x) {
+        const int which = idx / (TB * D / 8), f = idx % (TB * D / 8);
+        const int tl = f % TB, k0 = 8 * (f / TB);
+        const h8 v = *reinterpret_cast<const h8*>(&qkh[which][tl][k0]);
+        *reinterpret_cast<h8*>((which ? ws.k : ws.q) + qkc + a_off(co + tl, k0, D / 32)) = v;
+    }
+    for (int idx = threadIdx.x; idx < TB / 8 * D; idx += blockDim.x) {
+        const int d = idx % D, half = idx / D;
         h8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            v[j] = khs[8 * half + j][d];
-        *reinterpret_cast<h8*>(ws.kt + (((static_cast<size_t>(bq) * Hk + g) * NC + cl) * D + d) * CH + co + 8 * half) = v;
+            v[j] = qkh[1][8 * half + j][d];
+        *reinterpret_cast<h8*>(ws.kt + qkc + b_off(co + 8 * half, d, CH / 32)) = v;
     }
 }
 
 // ------------------------------------------------------------ tri
 
 struct alignas(16) TriSmem {
-    float A[CH][MP];
+    float A[CH][MP];              // after the inverse: W~ staged as fp16 [64][128]
     float T[CH][MP];
+    _Float16 Ps[CH][CH + 8];      // P staged for its A-order store
     float tmp[3][16][17];
     float G[CH];     // cumulative log2 decay inside the chunk
     float beta[CH];
@@ -262,25 +290,27 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
     // Every operand fragment this wave needs is requested up front.
     //   K K^T / Q K^T: wave w computes row block w (tiles (w, J), J <= w).
     //   U~ / W~: wave w computes column tiles 2w and 2w+1 for all token rows.
-    const _Float16* qg = ws.q + ((static_cast<size_t>(bq) * Hk + g) * SP + s0) * D;
-    const _Float16* kg = ws.k + ((static_cast<size_t>(bq) * Hk + g) * SP + s0) * D;
-    const _Float16* vth = ws.vt + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * D * CH;
-    const _Float16* ktg = ws.kt + ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * D * CH;
+    const size_t qkc = ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * kChunkQK;
+    const size_t hc = ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkQK;
+    const _Float16* qg = ws.q + qkc;
+    const _Float16* kg = ws.k + qkc;
+    const _Float16* vth = ws.vt + hc;
+    const _Float16* ktg = ws.kt + qkc;
     h8 qa[4], ka[4], kb[3][4], vb[2][2], kt[2][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        qa[s] = ld8(qg + static_cast<size_t>(16 * wave + lr) * D + 32 * s + 8 * lq);
-        ka[s] = ld8(kg + static_cast<size_t>(16 * wave + lr) * D + 32 * s + 8 * lq);
+        qa[s] = ldfrag(qg, 4 * wave + s, lane);
+        ka[s] = ldfrag(kg, 4 * wave + s, lane);
 #pragma unroll
         for (int J = 0; J < 3; ++J)
-            kb[J][s] = ld8(kg + static_cast<size_t>(16 * (J < wave ? J : wave) + lr) * D + 32 * s + 8 * lq);
+            kb[J][s] = ldfrag(kg, 4 * (J < wave ? J : wave) + s, lane);
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            vb[tt][s] = ld8(vth + static_cast<size_t>(16 * (2 * wave + tt) + lr) * CH + 32 * s + 8 * lq);
-            kt[tt][s] = ld8(ktg + static_cast<size_t>(16 * (2 * wave + tt) + lr) * CH + 32 * s + 8 * lq);
+            vb[tt][s] = ldfrag(vth, 2 * (2 * wave + tt) + s, lane);
+            kt[tt][s] = ldfrag(ktg, 2 * (2 * wave + tt) + s, lane);
         }
 
     if (wave == 0) {
@@ -309,7 +339,6 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 
     // K K^T -> A and Q K^T -> P for row block w; the blocks right of the
     // diagonal are zero in P and in T.
-    _Float16* Pm = ws.P + (((static_cast<size_t>(bq) * Hv + h) * NC + cl) * CH) * CH;
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         const int i0 = 16 * wave + 4 * lq, j = 16 * J + lr;
@@ -325,18 +354,25 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
             for (int r = 0; r < 4; ++r) {
                 const int i = i0 + r;
                 const float dg = (i >= j) ? __builtin_amdgcn_exp2f(sm.G[i] - sm.G[j]) : 0.0f;
-                Pm[i * CH + j] = static_cast<_Float16>(dg * qk[r]);
+                sm.Ps[i][j] = static_cast<_Float16>(dg * qk[r]);
                 sm.A[i][j] = (i > j) ? sm.beta[i] * dg * kk[r] : 0.0f;
             }
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Pm[(i0 + r) * CH + j] = static_cast<_Float16>(0.0f);
+                sm.Ps[i0 + r][j] = static_cast<_Float16>(0.0f);
                 sm.T[i0 + r][j] = 0.0f;
             }
         }
     }
     __syncthreads();
+    {
+        _Float16* Pc = ws.P + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkP;
+        for (int idx = threadIdx.x; idx < kChunkP / 8; idx += blockDim.x) {
+            const int i = idx % CH, j0 = 8 * (idx / CH);
+            *reinterpret_cast<h8*>(Pc + a_off(i, j0, CH / 32)) = *reinterpret_cast<const h8*>(&sm.Ps[i][j0]);
+        }
+    }
 
     // diagonal 16x16 blocks of (I + A)^-1: wave 0, lane = (block, column)
     if (wave == 0) {
@@ -397,8 +433,8 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
                 ksc[tt][s][e] = static_cast<_Float16>(static_cast<float>(kt[tt][s][e]) * fk[e]);
             }
     }
-    _Float16* uto = ws.ut + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * D * CH;
-    _Float16* wto = ws.wt + hs * D;
+    _Float16* uto = ws.ut + hc;
+    _Float16* wst = reinterpret_cast<_Float16*>(&sm.A[0][0]);   // W~ staging [64][128] (A is no longer needed)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         h8 tf[2];
@@ -421,10 +457,16 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uh[r] = static_cast<_Float16>(u[r]);
-                wto[static_cast<size_t>(16 * m + 4 * lq + r) * D + d] = static_cast<_Float16>(wv[r]);
+                wst[(16 * m + 4 * lq + r) * D + d] = static_cast<_Float16>(wv[r]);
             }
-            *reinterpret_cast<h4*>(uto + static_cast<size_t>(d) * CH + 16 * m + 4 * lq) = uh;
+            *reinterpret_cast<h4*>(uto + c_off(16 * m + 4 * lq, d, D / 16)) = uh;
         }
+    }
+    __syncthreads();
+    _Float16* wto = ws.wt + hc;
+    for (int idx = threadIdx.x; idx < kChunkQK / 8; idx += blockDim.x) {
+        const int t = idx % CH, k0 = 8 * (idx / CH);
+        *reinterpret_cast<h8*>(wto + a_off(t, k0, D / 32)) = *reinterpret_cast<const h8*>(&wst[t * D + k0]);
     }
 }
 
@@ -472,32 +514,36 @@ struct ScanCtx {
 
 __device__ __forceinline__ void load_state(StateOps& op, const Ws& ws, const ScanCtx& c, int cl) {
     const int s0 = cl * CH;
-    const size_t trow = static_cast<size_t>(s0 + 16 * c.w + c.lr);
+    const int lane = 16 * c.lq + c.lr;
+    const _Float16* wc = ws.wt + (c.utbase + cl) * kChunkQK;
+    const _Float16* kc = ws.kt + (c.ktbase + cl) * kChunkQK;
+    const _Float16* uc = ws.ut + (c.utbase + cl) * kChunkQK;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        op.wf[s] = ld8(ws.wt + (c.hbase + trow) * D + 32 * s + 8 * c.lq);
+        op.wf[s] = ldfrag(wc, 4 * c.w + s, lane);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-            op.kf[tt][s] = ld8(ws.kt + ((c.ktbase + cl) * D + 16 * (2 * c.w + tt) + c.lr) * CH + 32 * s + 8 * c.lq);
+            op.kf[tt][s] = ldfrag(kc, 2 * (2 * c.w + tt) + s, lane);
 #pragma unroll
     for (int it = 0; it < DS / 16; ++it)
-        op.u[it] = *reinterpret_cast<const uint2*>(ws.ut + ((c.utbase + cl) * D + c.row0 + 16 * it + c.lr) * CH +
-                                                   16 * c.w + 4 * c.lq);
+        op.u[it] = *reinterpret_cast<const uint2*>(uc + ((c.w * (D / 16) + c.row0 / 16 + it) * 64 + lane) * 4);
     op.egd = *reinterpret_cast<const f4*>(ws.egd + c.hbase + s0 + 16 * c.w + 4 * c.lq);
     op.eglast = ws.eg[c.hbase + s0 + CH - 1];
 }
 
 __device__ __forceinline__ void load_out(OutOps& op, const Ws& ws, const ScanCtx& c, int cl) {
     const int s0 = cl * CH;
-    const size_t trow = static_cast<size_t>(s0 + 16 * c.w + c.lr);
+    const int lane = 16 * c.lq + c.lr;
+    const _Float16* qc = ws.q + (c.ktbase + cl) * kChunkQK;
+    const _Float16* pc = ws.P + (c.pbase + cl) * kChunkP;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        op.qf[s] = ld8(ws.q + (c.gbase + trow) * D + 32 * s + 8 * c.lq);
+        op.qf[s] = ldfrag(qc, 4 * c.w + s, lane);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        op.pf[s] = ld8(ws.P + ((c.pbase + cl) * CH + 16 * c.w + c.lr) * CH + 32 * s + 8 * c.lq);
+        op.pf[s] = ldfrag(pc, 2 * c.w + s, lane);
     op.eg = *reinterpret_cast<const f4*>(ws.eg + c.hbase + s0 + 16 * c.w + 4 * c.lq);
 }
 
