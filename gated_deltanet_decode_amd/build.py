@@ -31,11 +31,15 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_token.hip", "gdn_tree.hip", "gdn_prefill.hip"]
+# The prefill kernels keep their MFMA accumulators in ordinary VGPRs: the scan
+# scales and converts its state accumulators every chunk, which would otherwise
+# cost a copy out of and back into the accumulation registers each time.
+EXTRA = {"gdn_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -13,24 +13,21 @@
 // Only differences G_i - G_j with i >= j are exponentiated, so nothing
 // overflows however strong the decay.
 //
-// Work split for MI355X, per segment of at most 2,048 tokens:
+// Work split for MI355X, per segment of at most 2,048 tokens, every chunk
+// product on 32x32x16 fp16 MFMAs (fp32 accumulation):
 //   conv  (parallel over 16-token blocks x q/k heads): conv + SiLU of the
 //         q/k head's channels and of its value heads' channels, q/k L2 norm;
-//         writes fp16 q^, k^, k^ transposed per chunk and v transposed per
-//         chunk.  Small LDS, many waves per CU.
-//   tri   (parallel over value heads x chunks): gates and G, K K^T and Q K^T
-//         on MFMA, A, the blocked inverse T in fp32 (16x16 diagonal blocks by
+//         writes fp16 q^, k^, k^ transposed and v transposed, as fragments.
+//   tri   (parallel over value heads x chunks): gates and G, K K^T and K Q^T,
+//         A, the blocked inverse T in fp32 (16x16 diagonal blocks by
 //         substitution, off-diagonal blocks by block products), then
-//         U~ = T (beta V) and W~ = T (beta e^G K) on MFMA, and P.
+//         U~ = T (beta V) and W~^T = (beta e^G K)^T T^T.  P, U~ and W~ are
+//         written straight from the accumulators.
 //   scan  (sequential over chunks; one workgroup per (sequence, value head,
-//         32-row slice of the state), one workgroup per CU): Z = W~ S0^T and
-//         Y = Q S0^T, U = U~ - Z, O = s (e^G Y + P U),
-//         S <- e^{G_n} S + U^T (e^{G_n - G} K), all on 16x16x32 fp16 MFMAs,
-//         two barriers per chunk.  Four waves carry the state (fp32, in
-//         registers across chunks); four more compute and store o off the
-//         state's critical path.  Operands stream through a four-stage
-//         register ring, three chunks ahead.  Workgroups of one q/k head sit
-//         on one XCD and share its L2.
+//         32-row slice of the state)): Z = W~ S0^T, U = U~ - Z,
+//         O = s (e^G (.) Q S0^T + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K).
+//         The state is held transposed in accumulator tiles, so the
+//         recurrence passes from one product to the next in registers.
 // The workspace holds one segment (about 114 MB at the 27B-class shape),
 // whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
@@ -44,6 +41,7 @@ namespace pf {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;       // head width handled by the prefill kernels
 constexpr int CH = 64;       // chunk length
@@ -51,31 +49,31 @@ constexpr int SEG = 2048;    // tokens per segment
 constexpr int TB = 16;       // tokens per conv workgroup
 constexpr int DS = 32;       // state rows per scan workgroup
 constexpr int NS = D / DS;   // scan workgroups per value head
-constexpr int MP = CH + 1;   // fp32 pitch of a 64x64 matrix row in LDS
-constexpr int HP = CH + 8;   // fp16 pitch of a 64-token row in LDS
+constexpr int MP = CH + 1;   // fp32 pitch of A (a 64x64 matrix) in LDS
+constexpr int TP = CH + 4;   // fp32 pitch of T in LDS: rows 16-byte aligned
 constexpr float kScale = Scale<D>::value;
 
 // Workspace of one segment; SP = token pitch (segment length rounded to 64),
-// NC = SP / 64 chunks.  Every chunk operand is stored in the order the MFMA
-// fragments read it (a_off / b_off / c_off below), so that each wave's
-// operand load is one contiguous run of 64 lanes x 16 bytes:
-//   q, k  fp16 [B][Hk][NC][64 x 128 A order]   normalised q^, k^ (zero past the prompt)
-//   kt    fp16 [B][Hk][NC][64 x 128 B order]   k^ with the token index as k
-//   vt    fp16 [B][Hv][NC][64 x 128 B order]   v with the token index as k
-//   ut    fp16 [B][Hv][NC][64 x 128 C order]   U~ = T (beta V)
-//   wt    fp16 [B][Hv][NC][64 x 128 A order]   W~ = T (beta e^G K)
-//   P     fp16 [B][Hv][NC][64 x 64 A order]
+// NC = SP / 64 chunks.  Chunk matrices are stored in the order the 32x32x16
+// MFMAs read them (frag_base / acc_base below), so that each wave's operand
+// load is one contiguous run of 64 lanes x 16 bytes:
+//   q, k  fp16 [B][Hk][NC][fragments of 64 tokens x 128 keys]   q^, k^ (zero past the prompt)
+//   kt    fp16 [B][Hk][NC][fragments of 128 keys x 64 tokens]   k^ transposed
+//   vt    fp16 [B][Hv][NC][fragments of 128 dims x 64 tokens]   v transposed
+//   ut    fp16 [B][Hv][NC][accumulators of 64 tokens x 128 dims] U~ = T (beta V)
+//   wt    fp16 [B][Hv][NC][fragments of 64 tokens x 128 keys]   W~ = T (beta e^G K)
+//   kd    fp16 [B][Hv][NC][fragments of 128 keys x 64 tokens]   (e^{G_last - G} k^)^T
+//   P     fp16 [B][Hv][NC][fragments of 64 x 64 tokens]
 //   eg    f32  [B][Hv][SP]                     e^{G_t}
-//   egd   f32  [B][Hv][SP]                     e^{G_last - G_t}
 struct Ws {
-    _Float16 *q, *k, *kt, *vt, *ut, *wt, *P;
-    float *eg, *egd;
+    _Float16 *q, *k, *kt, *vt, *ut, *wt, *kd, *P;
+    float* eg;
 };
 
 inline size_t seg_pitch(int T) { return static_cast<size_t>(T >= SEG ? SEG : (T + CH - 1) / CH * CH); }
 
 inline size_t ws_bytes(int B, int Hk, int Hv, size_t SP) {
-    const size_t per_tok = 3ull * Hk * D * 2 + 3ull * Hv * D * 2 + Hv * CH * 2ull + Hv * 8ull;
+    const size_t per_tok = 3ull * Hk * D * 2 + 4ull * Hv * D * 2 + Hv * CH * 2ull + Hv * 4ull;
     return static_cast<size_t>(B) * SP * per_tok + 256 * 10;
 }
 
@@ -93,35 +91,46 @@ inline Ws carve(void* base, int B, int Hk, int Hv, size_t SP) {
     w.vt = take16(nv);
     w.ut = take16(nv);
     w.wt = take16(nv);
+    w.kd = take16(nv);
     w.P = take16(nm);
     w.eg = take32(ng);
-    w.egd = take32(ng);
     return w;
 }
 
-__device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ __forceinline__ h8 ld8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
-__device__ __forceinline__ f4 zero4() { return f4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// Fragment orders of one chunk's matrices for 16x16x32 MFMAs.  A fragment
-// (16 rows x 32 k): lane (lq, lr) holds row lr, k 8 lq .. 8 lq + 7.  B fragment
-// (32 k x 16 columns): lane (lq, lr) holds column lr, k 8 lq .. 8 lq + 7.  C
-// tile (16 x 16): lane (lq, lr) holds rows 4 lq .. 4 lq + 3 of column lr.
-// Tiles are laid out one after another, 64 lanes x 8 (A, B) or x 4 (C) fp16.
-//   a_off: M[row][k], ks k-steps per row tile;  b_off: M[k][col], ks k-steps
-//   per column tile;  c_off: M[row][col], nct column tiles per row tile.
-__device__ __forceinline__ int a_off(int row, int k, int ks) {
-    return (((row >> 4) * ks + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (row & 15)) * 8 + (k & 7);
+// 32x32x16 fp16 MFMA.  Lane (hi, c) = (lane / 32, lane % 32).  A fragment: row c,
+// eight k values; B fragment: column c, the same eight k; accumulator v of lane
+// (hi, c) is row 8 (v / 4) + 4 hi + v % 4, column c.
+__device__ __forceinline__ f16v mma32(h8 a, h8 b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ int b_off(int k, int col, int ks) {
-    return (((col >> 4) * ks + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (col & 15)) * 8 + (k & 7);
+__device__ __forceinline__ f16v zero16() {
+    f16v z;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        z[v] = 0.0f;
+    return z;
 }
-__device__ __forceinline__ int c_off(int row, int col, int nct) {
-    return (((row >> 4) * nct + (col >> 4)) * 64 + ((row & 15) >> 2) * 16 + (col & 15)) * 4 + (row & 3);
+
+// Fragment order of a chunk matrix M[row][k].  Tiles of 32 rows x 16 k follow
+// one another (nks k-steps per row tile), each 64 lanes x 8 fp16.  Slot e of
+// lane half hi holds k = kperm(hi, e) of its k-step rather than 8 hi + e: the
+// accumulator values 8 s' .. 8 s' + 7 of a 32 x 32 product are exactly the rows
+// 16 s' + kperm(hi, e), so a product's accumulators feed the next product's B
+// operand in registers, with the other operand stored in this order.  A
+// contraction is indifferent to the order of its k, so the same storage serves
+// as A fragment (rows as M) and as B fragment (rows as N).
+__host__ __device__ constexpr int kperm(int hi, int e) { return ((e >> 2) << 3) + 4 * hi + (e & 3); }
+__device__ __forceinline__ int frag_base(int row, int ks, int nks, int hi) {
+    return ((((row >> 5) * nks + ks) * 64) + hi * 32 + (row & 31)) * 8;
 }
-// One A or B fragment of tile `tile` in a fragment-ordered matrix.
+// Accumulator order of M[row][col] (32 x 32 tiles, nct per row of tiles):
+// lane (hi, c) holds the 16 values of its accumulator, fp16, contiguously.
+__device__ __forceinline__ int acc_base(int rt, int ct, int nct, int lane) { return ((rt * nct + ct) * 64 + lane) * 16; }
+// Fragment `tile` of a fragment-ordered matrix: one contiguous 1 KB run per wave.
 __device__ __forceinline__ h8 ldfrag(const _Float16* m, int tile, int lane) { return ld8(m + tile * 512 + lane * 8); }
-constexpr int kChunkQK = CH * D;   // fp16 elements of one chunk of q, k, k^T, v^T, U~, W~
+constexpr int kChunkQK = CH * D;   // fp16 elements of one chunk of q, k, k^T, v^T, U~, W~, kd
 constexpr int kChunkP = CH * CH;   // fp16 elements of one chunk of P
 
 // Prefill stores q^, k^ and v as fp16 (relative step 2^-11), so its conv and
@@ -146,10 +155,8 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
                                                    int nblk, int B, int Hk, int Hv, int C) {
     __shared__ float ys[TB][2 * D];                  // q~ | k~ of the block, fp32
     __shared__ __align__(16) _Float16 qkh[2][TB][D]; // q^, k^ of the block, fp16
-    // The CH / TB blocks of one chunk write disjoint pieces of the same
-    // 128-byte lines of v^T and k^T.  They share an XCD (blockIdx % 8 picks
-    // it), so the pieces merge in one L2 instead of reaching memory as
-    // partial lines.
+    // The CH / TB blocks of one chunk write the two halves of the same
+    // q^ / k^ fragments; they share an XCD (blockIdx % 8 picks it).
     constexpr int BPC = CH / TB;                     // blocks per chunk
     const int nch = nblk / BPC;
     const int xcd = blockIdx.x % 8, r8 = blockIdx.x / 8;
@@ -164,6 +171,7 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
     const int t0 = seg0 + tb * TB;                   // prompt index of the block's first token
     const int sl = tb * TB;                          // segment index of the same token
     const int cl = sl / CH, co = sl % CH;            // its chunk and offset in the chunk
+    const int ks = co / TB;                          // the block's tokens are k-step ks of the chunk
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const Act* xb = x + static_cast<size_t>(bq) * T * C;
@@ -205,18 +213,18 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
             for (int j = 0; j < TB; ++j)
                 ys[j][ch] = yv[j];
         } else {
+            // v^T: row d, k = token; this thread owns both lane halves of row d
             const int h = G * g + (ch - 2 * D) / D;
             const int d = (ch - 2 * D) % D;
-            h8 lo, hi;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                lo[j] = static_cast<_Float16>(yv[j]);
-                hi[j] = static_cast<_Float16>(yv[8 + j]);
-            }
-            // tokens co .. co + 15 of column d: two B-order runs of 8
             _Float16* vc = ws.vt + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkQK;
-            *reinterpret_cast<h8*>(vc + b_off(co, d, CH / 32)) = lo;
-            *reinterpret_cast<h8*>(vc + b_off(co + 8, d, CH / 32)) = hi;
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+                h8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = static_cast<_Float16>(yv[kperm(hi, e)]);
+                *reinterpret_cast<h8*>(vc + frag_base(d, ks, CH / 16, hi)) = v;
+            }
         }
     }
     __syncthreads();
@@ -231,31 +239,33 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
         qkh[which][tl][lane + kWave] = static_cast<_Float16>(e1 * r);
     }
     __syncthreads();
-    // The block is row tile co / 16 of the chunk: q^ and k^ in A order (16
-    // tokens x 8 keys per run), k^ in B order (8 tokens x 1 key per run).
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    // q^, k^: row = token co + tl, k = key; slot group (hi) of key step s holds
+    // keys 16 s + 4 hi .. + 3 and 16 s + 8 + 4 hi .. + 3.
     const size_t qkc = ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * kChunkQK;
-    for (int idx = threadIdx.x; idx < 2 * TB * D / 8; idx += blockDim.x) {
-        const int which = idx / (TB * D / 8), f = idx % (TB * D / 8);
-        const int tl = f % TB, k0 = 8 * (f / TB);
-        const h8 v = *reinterpret_cast<const h8*>(&qkh[which][tl][k0]);
-        *reinterpret_cast<h8*>((which ? ws.k : ws.q) + qkc + a_off(co + tl, k0, D / 32)) = v;
+    for (int idx = threadIdx.x; idx < 2 * (D / 16) * 2 * TB; idx += blockDim.x) {
+        const int tl = idx % TB, hi = (idx / TB) & 1, s = (idx / (2 * TB)) % (D / 16), which = idx / (D / 16 * 2 * TB);
+        const h4 lo = *reinterpret_cast<const h4*>(&qkh[which][tl][16 * s + 4 * hi]);
+        const h4 up = *reinterpret_cast<const h4*>(&qkh[which][tl][16 * s + 8 + 4 * hi]);
+        const h8 v = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        *reinterpret_cast<h8*>((which ? ws.k : ws.q) + qkc + frag_base(co + tl, s, D / 16, hi)) = v;
     }
-    for (int idx = threadIdx.x; idx < TB / 8 * D; idx += blockDim.x) {
-        const int d = idx % D, half = idx / D;
+    // k^T: row = key, k = token
+    for (int idx = threadIdx.x; idx < 2 * D; idx += blockDim.x) {
+        const int key = idx % D, hi = idx / D;
         h8 v;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = qkh[1][8 * half + j][d];
-        *reinterpret_cast<h8*>(ws.kt + qkc + b_off(co + 8 * half, d, CH / 32)) = v;
+        for (int e = 0; e < 8; ++e)
+            v[e] = qkh[1][kperm(hi, e)][key];
+        *reinterpret_cast<h8*>(ws.kt + qkc + frag_base(key, ks, CH / 16, hi)) = v;
     }
 }
 
 // ------------------------------------------------------------ tri
 
 struct alignas(16) TriSmem {
-    float A[CH][MP];              // after the inverse: W~ staged as fp16 [64][128]
-    float T[CH][MP];
-    _Float16 Ps[CH][CH + 8];      // P staged for its A-order store
+    float T[CH][TP];              // (I + A)^-1; rows 16-byte aligned for the fragment reads
+    float A[CH][MP];
     float tmp[3][16][17];
     float G[CH];     // cumulative log2 decay inside the chunk
     float beta[CH];
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
     const int s0 = cl * CH;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int lr = lane & 15, lq = lane >> 4;
+    const int hi = lane >> 5, c32 = lane & 31;
     const size_t hs = (static_cast<size_t>(bq) * Hv + h) * SP + s0;   // this head's token row base
 
     // Gate inputs first, then every operand fragment this wave needs, so that
@@ -287,31 +297,46 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         av = a[idx];
         bv = bg[idx];
     }
-    // Every operand fragment this wave needs is requested up front.
-    //   K K^T / Q K^T: wave w computes row block w (tiles (w, J), J <= w).
-    //   U~ / W~: wave w computes column tiles 2w and 2w+1 for all token rows.
+    // 32 x 32 token tiles (m, n) of K K^T and K Q^T (m: tile of k as rows, n:
+    // tile of k or q as columns; only m <= n is needed):
+    //   wave 0: KK(0,0), KQ(0,0);  wave 1: KK(0,1);  wave 2: KQ(0,1);  wave 3: KK(1,1), KQ(1,1).
+    // Then U~ and W~: wave w owns value column tile w and key tile w.
+    const int mt = wave == 3 ? 1 : 0;
+    const int nt = wave == 0 ? 0 : 1;
     const size_t qkc = ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * kChunkQK;
     const size_t hc = ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkQK;
-    const _Float16* qg = ws.q + qkc;
-    const _Float16* kg = ws.k + qkc;
-    const _Float16* vth = ws.vt + hc;
-    const _Float16* ktg = ws.kt + qkc;
-    h8 qa[4], ka[4], kb[3][4], vb[2][2], kt[2][2];
+    const _Float16* kA = ws.k + qkc;
+    const _Float16* kB = (wave == 1 ? ws.k : ws.q) + qkc;
+    h8 fa[8], fb[8], vf[4], kf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        qa[s] = ldfrag(qg, 4 * wave + s, lane);
-        ka[s] = ldfrag(kg, 4 * wave + s, lane);
-#pragma unroll
-        for (int J = 0; J < 3; ++J)
-            kb[J][s] = ldfrag(kg, 4 * (J < wave ? J : wave) + s, lane);
+    for (int s = 0; s < 8; ++s) {
+        fa[s] = ldfrag(kA, mt * 8 + s, lane);
+        fb[s] = ldfrag(kB, nt * 8 + s, lane);
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int s = 0; s < 4; ++s) {
+        vf[s] = ldfrag(ws.vt + hc, wave * 4 + s, lane);
+        kf[s] = ldfrag(ws.kt + qkc, wave * 4 + s, lane);
+    }
+    // upper blocks of T are zero (the diagonal blocks are written whole below)
+    for (int e = threadIdx.x; e < 6 * 256; e += blockDim.x) {
+        const int blk = e / 256, r = (e / 16) % 16, c = e % 16;
+        const int I = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+        const int J = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        sm.T[16 * I + r][16 * J + c] = 0.0f;
+    }
+
+    f16v kk = zero16(), kq = zero16();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            vb[tt][s] = ldfrag(vth, 2 * (2 * wave + tt) + s, lane);
-            kt[tt][s] = ldfrag(ktg, 2 * (2 * wave + tt) + s, lane);
+    for (int s = 0; s < 8; ++s) {
+        if (wave == 1) {
+            kk = mma32(fa[s], fb[s], kk);
+        } else {
+            if (wave != 2)
+                kk = mma32(fa[s], fa[s], kk);
+            kq = mma32(fa[s], fb[s], kq);
         }
+    }
 
     if (wave == 0) {
         float la = 0.0f, be = 0.0f;
@@ -326,57 +351,57 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
                 la += up;
         }
         const float l2 = la * kLog2e;             // G in log2 units
-        const float glast = __shfl(l2, kWave - 1, kWave);
         const float eg = __builtin_amdgcn_exp2f(l2);
         sm.G[lane] = l2;
         sm.beta[lane] = be;
         sm.bv[lane] = be;
         sm.bk[lane] = be * eg;
         ws.eg[hs + lane] = eg;
-        ws.egd[hs + lane] = __builtin_amdgcn_exp2f(glast - l2);
     }
     __syncthreads();
 
-    // K K^T -> A and Q K^T -> P for row block w; the blocks right of the
-    // diagonal are zero in P and in T.
+    // Accumulator v of tile (mt, nt) is row t' = 32 mt + 8 (v / 4) + 4 hi + v % 4
+    // (k side), column t = 32 nt + c32 (k or q side).
+    {
+        const int t = 32 * nt + c32;
+        const float gt = sm.G[t], bt = sm.beta[t];
+        if (wave != 2) {
+            // A[t][t'] = beta_t e^{G_t - G_t'} k_t . k_t' for t > t'
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        const int i0 = 16 * wave + 4 * lq, j = 16 * J + lr;
-        if (J <= wave) {
-            f4 kk = zero4(), qk = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const h8 b = (J == wave) ? ka[s] : kb[J < 3 ? J : 0][s];
-                kk = mma(ka[s], b, kk);
-                qk = mma(qa[s], b, qk);
+            for (int v = 0; v < 16; ++v) {
+                const int tp = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
+                if (t > tp)
+                    sm.A[t][tp] = bt * __builtin_amdgcn_exp2f(gt - sm.G[tp]) * kk[v];
             }
+        }
+        _Float16* Pc = ws.P + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkP;
+        if (wave != 1) {
+            // P[t][t'] = e^{G_t - G_t'} q_t . k_t' for t >= t': the accumulators
+            // 8 j .. 8 j + 7 are P's fragment (row tile nt, k-step 2 mt + j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + r;
-                const float dg = (i >= j) ? __builtin_amdgcn_exp2f(sm.G[i] - sm.G[j]) : 0.0f;
-                sm.Ps[i][j] = static_cast<_Float16>(dg * qk[r]);
-                sm.A[i][j] = (i > j) ? sm.beta[i] * dg * kk[r] : 0.0f;
+            for (int j = 0; j < 2; ++j) {
+                h8 p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = 8 * j + e;
+                    const int tp = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
+                    p[e] = static_cast<_Float16>(t >= tp ? __builtin_amdgcn_exp2f(gt - sm.G[tp]) * kq[v] : 0.0f);
+                }
+                *reinterpret_cast<h8*>(Pc + ((nt * 4 + 2 * mt + j) * 64 + lane) * 8) = p;
             }
         } else {
+            // P's fragments (row tile 0, k-steps 2, 3) lie above the diagonal
+            const h8 zero = {};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sm.Ps[i0 + r][j] = static_cast<_Float16>(0.0f);
-                sm.T[i0 + r][j] = 0.0f;
-            }
+            for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<h8*>(Pc + ((2 + j) * 64 + lane) * 8) = zero;
         }
     }
     __syncthreads();
-    {
-        _Float16* Pc = ws.P + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkP;
-        for (int idx = threadIdx.x; idx < kChunkP / 8; idx += blockDim.x) {
-            const int i = idx % CH, j0 = 8 * (idx / CH);
-            *reinterpret_cast<h8*>(Pc + a_off(i, j0, CH / 32)) = *reinterpret_cast<const h8*>(&sm.Ps[i][j0]);
-        }
-    }
 
     // diagonal 16x16 blocks of (I + A)^-1: wave 0, lane = (block, column)
     if (wave == 0) {
-        const int o = 16 * lq, j = lr;
+        const int o = 16 * (lane >> 4), j = lane & 15;
         float X[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -415,220 +440,115 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         __syncthreads();
     }
 
-    // U~ = T (beta V) and W~ = T (beta e^G K): wave w owns column tiles 2w, 2w+1
-    h8 vsc[2][2], ksc[2][2];
+    // T as fragments (row tile tt, k-step s over t'); the same registers are
+    // T's A fragment for U~ and T^T's B fragment for W~^T.
+    h8 tf[2][4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        float fv[8], fk[8];
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const f4 lo = *reinterpret_cast<const f4*>(&sm.T[32 * tt + c32][16 * s + 4 * hi]);
+            const f4 up = *reinterpret_cast<const f4*>(&sm.T[32 * tt + c32][16 * s + 8 + 4 * hi]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tf[tt][s][e] = static_cast<_Float16>(lo[e]);
+                tf[tt][s][4 + e] = static_cast<_Float16>(up[e]);
+            }
+        }
+    // beta V (column tile w) and beta e^G K (key tile w) with the token as k;
+    // e^{G_last - G} K (key tile w) is the scan's state-update operand
+    h8 vs[4], ks[4];
+    const float glast = sm.G[CH - 1];
+    _Float16* kdo = ws.kd + hc;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        h8 kd;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            fv[e] = sm.bv[32 * s + 8 * lq + e];
-            fk[e] = sm.bk[32 * s + 8 * lq + e];
+            const int tp = 16 * s + kperm(hi, e);
+            const float kv = static_cast<float>(kf[s][e]);
+            vs[s][e] = static_cast<_Float16>(static_cast<float>(vf[s][e]) * sm.bv[tp]);
+            ks[s][e] = static_cast<_Float16>(kv * sm.bk[tp]);
+            kd[e] = static_cast<_Float16>(kv * __builtin_amdgcn_exp2f(glast - sm.G[tp]));
         }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                vsc[tt][s][e] = static_cast<_Float16>(static_cast<float>(vb[tt][s][e]) * fv[e]);
-                ksc[tt][s][e] = static_cast<_Float16>(static_cast<float>(kt[tt][s][e]) * fk[e]);
-            }
+        *reinterpret_cast<h8*>(kdo + ((wave * 4 + s) * 64 + lane) * 8) = kd;
     }
     _Float16* uto = ws.ut + hc;
-    _Float16* wst = reinterpret_cast<_Float16*>(&sm.A[0][0]);   // W~ staging [64][128] (A is no longer needed)
+    _Float16* wto = ws.wt + hc;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        h8 tf[2];
+    for (int tt = 0; tt < 2; ++tt) {
+        f16v u = zero16(), wv = zero16();
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 4; ++s) {
+            u = mma32(tf[tt][s], vs[s], u);    // U~[t][d]:  rows t (tile tt), columns d (tile w)
+            wv = mma32(ks[s], tf[tt][s], wv);  // W~^T[key][t]: rows key (tile w), columns t (tile tt)
+        }
+        // U~ in accumulator order
+        h8 u0, u1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            u0[e] = static_cast<_Float16>(u[e]);
+            u1[e] = static_cast<_Float16>(u[8 + e]);
+        }
+        _Float16* up = uto + acc_base(tt, wave, D / 32, lane);
+        *reinterpret_cast<h8*>(up) = u0;
+        *reinterpret_cast<h8*>(up + 8) = u1;
+        // W~^T's accumulators 8 j .. 8 j + 7 are W~'s fragment (row tile tt, key step 2 w + j)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            h8 f;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                tf[s][e] = static_cast<_Float16>(sm.T[16 * m + lr][32 * s + 8 * lq + e]);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f4 u = zero4(), wv = zero4();
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u = mma(tf[s], vsc[tt][s], u);
-                wv = mma(tf[s], ksc[tt][s], wv);
-            }
-            const int d = 16 * (2 * wave + tt) + lr;
-            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-            h4 uh;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uh[r] = static_cast<_Float16>(u[r]);
-                wst[(16 * m + 4 * lq + r) * D + d] = static_cast<_Float16>(wv[r]);
-            }
-            *reinterpret_cast<h4*>(uto + c_off(16 * m + 4 * lq, d, D / 16)) = uh;
+                f[e] = static_cast<_Float16>(wv[8 * j + e]);
+            *reinterpret_cast<h8*>(wto + ((tt * (D / 16) + 2 * wave + j) * 64 + lane) * 8) = f;
         }
-    }
-    __syncthreads();
-    _Float16* wto = ws.wt + hc;
-    for (int idx = threadIdx.x; idx < kChunkQK / 8; idx += blockDim.x) {
-        const int t = idx % CH, k0 = 8 * (idx / CH);
-        *reinterpret_cast<h8*>(wto + a_off(t, k0, D / 32)) = *reinterpret_cast<const h8*>(&wst[t * D + k0]);
     }
 }
 
 // ------------------------------------------------------------ scan
 
-// The scan workgroup owns DS rows of one value head's state and has two roles
-// of four waves.  State waves carry the recurrence: Z = W~ S0^T, U = U~ - Z,
-// S <- e^{G_n} S + U^T (e^{G_n - G} K), the state in fp32 registers across
-// chunks.  Output waves compute Y = Q S0^T and P U and store o.  The roles meet
-// at two barriers per chunk; S0 and U^T pass through LDS, double-buffered by
-// chunk parity.
-//
-// The workgroup's operands of a chunk (W~, K^T, Q and P of its head; U~ of its
-// rows) are read once per workgroup, so the chip-wide operand traffic is
-// (value heads x 128 / DS) copies per chunk: DS = 32 keeps it within what the
-// L2 delivers while one workgroup per CU keeps every state slice resident.
-// Each wave streams its operands through a ring of kScanRing register stages,
-// so the chunk it computes was requested kScanRing - 1 chunks earlier.  The
-// chunk loop body holds kScanRing chunks, which keeps every ring slot in fixed
-// registers while the code stays small enough for the instruction cache.
-constexpr int kScanRing = 4;
+// One workgroup per (sequence, value head, 32-row slice of the state), four
+// waves with one barrier per chunk:
+//   state  (wave 0) holds S^T of the slice (keys x rows) in four 32 x 32
+//          accumulator tiles across chunks.  Their fp16 copies are directly
+//          the B fragments of Z = W~ S0^T; Z's accumulators give U = U~ - Z,
+//          whose fp16 copies are directly the B fragments of the update
+//          S^T <- e^{G_n} S^T + (e^{G_n - G} K)^T U: no LDS round trip and no
+//          barrier inside the recurrence.  It hands S0^T and U, as B
+//          fragments, to the output waves through LDS (two buffers).
+//   output (waves 1, 2; token tile 32 (w - 1)) compute Y = Q S0^T and P U one
+//          chunk behind and store o = s (e^G Y + P U); Q and P stream through
+//          a register ring.
+//   loader (wave 3) copies W~, (e^{G_n - G} K)^T, this slice's U~ and e^G of
+//          chunk k + 2 into a three-stage LDS ring by direct global-to-LDS loads,
+//          and waits for chunk k + 1 before the barrier that ends step k.
+// Workgroups of one (sequence, q/k head) share an XCD and its L2.
+constexpr int kStages = 3;
+constexpr int kOutRing = 3;
+constexpr int kDmaPerChunk = 16 + 16 + 4 + 1;   // W~, kd, U~ (two 2 KB tiles), e^G
 
 struct alignas(16) ScanSmem {
-    _Float16 s0[2][DS][D + 8];   // S0 slice, fp16, [row][key]
-    _Float16 ut[2][DS][HP];      // U^T [row][t]
-    _Float16 utd[DS][HP];        // U^T scaled by e^{G_last - G} (state waves only)
+    h8 wt[kStages][16][64];     // W~ fragments (token tile, key step)
+    h8 kd[kStages][16][64];     // (e^{G_n - G} K)^T fragments (key tile, token step)
+    h8 ut[kStages][2][64][2];   // U~ of the slice: token tile, lane, 32 bytes
+    float eg[kStages][CH];
+    h8 xs[2][8][64];            // S0^T as B fragments (key step)
+    h8 xu[2][4][64];            // U as B fragments (token step)
 };
 
-struct StateOps {
-    h8 wf[4], kf[2][2];
-    uint2 u[DS / 16];   // four fp16 U~ values per row tile
-    f4 egd;
-    float eglast;
-};
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 struct OutOps {
-    h8 qf[4], pf[2];
-    f4 eg;
+    h8 qf[8], pf[4];
+    f4 eg[4];
 };
 
-struct ScanCtx {
-    size_t gbase, hbase, pbase, ktbase, utbase;
-    int w, lr, lq, row0;   // w: this wave's index within its role
-};
-
-__device__ __forceinline__ void load_state(StateOps& op, const Ws& ws, const ScanCtx& c, int cl) {
-    const int s0 = cl * CH;
-    const int lane = 16 * c.lq + c.lr;
-    const _Float16* wc = ws.wt + (c.utbase + cl) * kChunkQK;
-    const _Float16* kc = ws.kt + (c.ktbase + cl) * kChunkQK;
-    const _Float16* uc = ws.ut + (c.utbase + cl) * kChunkQK;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        op.wf[s] = ldfrag(wc, 4 * c.w + s, lane);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-            op.kf[tt][s] = ldfrag(kc, 2 * (2 * c.w + tt) + s, lane);
-#pragma unroll
-    for (int it = 0; it < DS / 16; ++it)
-        op.u[it] = *reinterpret_cast<const uint2*>(uc + ((c.w * (D / 16) + c.row0 / 16 + it) * 64 + lane) * 4);
-    op.egd = *reinterpret_cast<const f4*>(ws.egd + c.hbase + s0 + 16 * c.w + 4 * c.lq);
-    op.eglast = ws.eg[c.hbase + s0 + CH - 1];
-}
-
-__device__ __forceinline__ void load_out(OutOps& op, const Ws& ws, const ScanCtx& c, int cl) {
-    const int s0 = cl * CH;
-    const int lane = 16 * c.lq + c.lr;
-    const _Float16* qc = ws.q + (c.ktbase + cl) * kChunkQK;
-    const _Float16* pc = ws.P + (c.pbase + cl) * kChunkP;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        op.qf[s] = ldfrag(qc, 4 * c.w + s, lane);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        op.pf[s] = ldfrag(pc, 2 * c.w + s, lane);
-    op.eg = *reinterpret_cast<const f4*>(ws.eg + c.hbase + s0 + 16 * c.w + 4 * c.lq);
-}
-
-// x S0^T for one 16-token tile and the 16 state rows starting at s0, keys
-// split into two independent chains.
-__device__ __forceinline__ f4 times_s0(const h8 (&a)[4], const _Float16 (*s0)[D + 8], int lr, int lq) {
-    f4 z0 = zero4(), z1 = zero4();
-    z0 = mma(a[0], ld8(&s0[lr][8 * lq]), z0);
-    z1 = mma(a[2], ld8(&s0[lr][64 + 8 * lq]), z1);
-    z0 = mma(a[1], ld8(&s0[lr][32 + 8 * lq]), z0);
-    z1 = mma(a[3], ld8(&s0[lr][96 + 8 * lq]), z1);
-    return z0 + z1;
-}
-
-// sacc[it][tt]: rows 16*it.., keys 16*(2w+tt).. of the slice (C layout: row
-// 4*lq + r, column lr).
-template <int PAR>
-__device__ __forceinline__ void state_chunk(const StateOps& op, ScanSmem& sm, f4 (&sacc)[DS / 16][2],
-                                            const ScanCtx& c) {
-    const int w = c.w, lr = c.lr, lq = c.lq;
-#pragma unroll
-    for (int it = 0; it < DS / 16; ++it)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm.s0[PAR][16 * it + 4 * lq + r][16 * (2 * w + tt) + lr] = static_cast<_Float16>(sacc[it][tt][r]);
-    __syncthreads();
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int it = 0; it < DS / 16; ++it) {
-        const f4 Z = times_s0(op.wf, &sm.s0[PAR][16 * it], lr, lq);
-        const h4 uh = __builtin_bit_cast(h4, op.u[it]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * w + 4 * lq + r;
-            const float U = static_cast<float>(uh[r]) - Z[r];
-            sm.ut[PAR][16 * it + lr][t] = static_cast<_Float16>(U);
-            sm.utd[16 * it + lr][t] = static_cast<_Float16>(U * op.egd[r]);
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < DS / 16; ++it)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[it][tt][r] *= op.eglast;
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                sacc[it][tt] = mma(ld8(&sm.utd[16 * it + lr][32 * s + 8 * lq]), op.kf[tt][s], sacc[it][tt]);
-        }
-}
-
-// orow points at the chunk's first token row of o for this head and slice; a
-// final partial chunk stores only its n valid tokens.
-template <int PAR, bool MASKED>
-__device__ __forceinline__ void out_chunk(const OutOps& op, ScanSmem& sm, const ScanCtx& c,
-                                          float* __restrict__ orow, int n, size_t ostride) {
-    const int w = c.w, lr = c.lr, lq = c.lq;
-    __syncthreads();
-    f4 Y[DS / 16];
-#pragma unroll
-    for (int it = 0; it < DS / 16; ++it)
-        Y[it] = times_s0(op.qf, &sm.s0[PAR][16 * it], lr, lq);
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < DS / 16; ++it) {
-        f4 PU = zero4();
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            PU = mma(op.pf[s], ld8(&sm.ut[PAR][16 * it + lr][32 * s + 8 * lq]), PU);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * w + 4 * lq + r;
-            if (!MASKED || t < n)
-                orow[static_cast<size_t>(t) * ostride + 16 * it + lr] =
-                    kScale * __builtin_fmaf(op.eg[r], Y[it][r], PU[r]);
-        }
-    }
-}
-
-__global__ __launch_bounds__(512, 2) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
-                                                      int seg0, int SP, int nch, int B, int Hk, int Hv) {
+__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
+                                                   int seg0, int SP, int nch, int B, int Hk, int Hv) {
     __shared__ ScanSmem sm;
     const int G = Hv / Hk;
     // workgroups of one (sequence, q/k head) share an XCD: blockIdx % 8 picks the XCD
@@ -637,96 +557,211 @@ __global__ __launch_bounds__(512, 2) void scan_kernel(float* __restrict__ S, flo
     if (gu >= B * Hk)
         return;
     const int rem = r8 % (G * NS);
-    const int bq = gu / Hk, g = gu % Hk, h = G * g + rem / NS, row0 = (rem % NS) * DS;
+    const int bq = gu / Hk, g = gu % Hk, h = G * g + rem / NS, slc = rem % NS, row0 = slc * DS;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const bool state_role = wave < 4;
+    const int hi = lane >> 5, c32 = lane & 31;
     const int NC = SP / CH;
-    ScanCtx c;
-    c.w = wave & 3;
-    c.lr = lane & 15;
-    c.lq = lane >> 4;
-    c.row0 = row0;
-    c.gbase = (static_cast<size_t>(bq) * Hk + g) * SP;   // token rows of q/k head g
-    c.hbase = (static_cast<size_t>(bq) * Hv + h) * SP;   // token rows of value head h
-    c.pbase = (static_cast<size_t>(bq) * Hv + h) * NC;
-    c.utbase = c.pbase;
-    c.ktbase = (static_cast<size_t>(bq) * Hk + g) * NC;
+    const size_t hbase = (static_cast<size_t>(bq) * Hv + h) * SP;   // token rows of value head h
+    const size_t vbase = (static_cast<size_t>(bq) * Hv + h) * NC;   // chunks of value head h
+    const size_t kbase = (static_cast<size_t>(bq) * Hk + g) * NC;   // chunks of q/k head g
     const int len = min(SEG, T - seg0);
-    const int nfull = len / CH, tailn = len % CH;
-    // Chunk nfull (if tailn > 0) is partial: its workspace rows past the
-    // prompt are zero, so the state waves treat it like any other.
 
-    if (state_role) {
-        float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0) * D;
-        f4 sacc[DS / 16][2];
+    if (wave == 3) {
+        // ---- loader
+        auto issue = [&](int cl) {
+            const int st = cl % kStages;
+            const char* wsrc = reinterpret_cast<const char*>(ws.wt + (vbase + cl) * kChunkQK) + lane * 16;
+            const char* ksrc = reinterpret_cast<const char*>(ws.kd + (vbase + cl) * kChunkQK) + lane * 16;
+            const char* usrc = reinterpret_cast<const char*>(ws.ut + (vbase + cl) * kChunkQK) + lane * 16;
 #pragma unroll
-        for (int it = 0; it < DS / 16; ++it)
+            for (int i = 0; i < 16; ++i)
+                __builtin_amdgcn_global_load_lds(wsrc + i * 1024, &sm.wt[st][i][0], 16, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                __builtin_amdgcn_global_load_lds(ksrc + i * 1024, &sm.kd[st][i][0], 16, 0, 0);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sacc[it][tt][r] = Sh[(16 * it + 4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr];
-        StateOps ring[kScanRing];
-#pragma unroll
-        for (int p = 0; p < kScanRing; ++p)
-            load_state(ring[p], ws, c, min(p, nch - 1));
-        // chunk cl uses ring slot cl % kScanRing and LDS parity cl & 1, both
-        // fixed per position in the unrolled body because cl0 % kScanRing == 0
-        auto step = [&](auto pc, int cl) {
-            constexpr int P = decltype(pc)::value;
-            state_chunk<P & 1>(ring[P], sm, sacc, c);
-            load_state(ring[P], ws, c, min(cl + kScanRing, nch - 1));
+                for (int q = 0; q < 2; ++q)   // accumulator tile (tt, slc) of U~: 2 KB
+                    __builtin_amdgcn_global_load_lds(usrc + (tt * (D / 32) + slc) * 2048 + q * 1024,
+                                                     &sm.ut[st][tt][0][0] + q * 64, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ws.eg + hbase + cl * CH + lane, &sm.eg[st][0], 4, 0, 0);
         };
-        int cl0 = 0;
-        for (; cl0 + kScanRing <= nch; cl0 += kScanRing) {
-            step(std::integral_constant<int, 0>{}, cl0);
-            step(std::integral_constant<int, 1>{}, cl0 + 1);
-            step(std::integral_constant<int, 2>{}, cl0 + 2);
-            step(std::integral_constant<int, 3>{}, cl0 + 3);
+        issue(0);
+        if (nch > 1) {
+            issue(1);
+            wait_vmem<kDmaPerChunk>();
+        } else {
+            wait_vmem<0>();
         }
-        if (cl0 < nch)
-            step(std::integral_constant<int, 0>{}, cl0);
-        if (cl0 + 1 < nch)
-            step(std::integral_constant<int, 1>{}, cl0 + 1);
-        if (cl0 + 2 < nch)
-            step(std::integral_constant<int, 2>{}, cl0 + 2);
+        __builtin_amdgcn_s_barrier();
+        for (int k = 0; k < nch; ++k) {
+            if (k + 2 < nch) {
+                issue(k + 2);
+                wait_vmem<kDmaPerChunk>();
+            } else {
+                wait_vmem<0>();
+            }
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_barrier();
+    } else if (wave == 0) {
+        // ---- state
+        float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0 + c32) * D;   // row row0 + c32
+        f16v st[4];   // st[kt][v]: key 32 kt + 8 (v / 4) + 4 hi + v % 4, row row0 + c32
 #pragma unroll
-        for (int it = 0; it < DS / 16; ++it)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int j = 0; j < 4; ++j) {
+                const f4 v = *reinterpret_cast<const f4*>(Sh + 32 * kt + 8 * j + 4 * hi);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Sh[(16 * it + 4 * c.lq + r) * D + 16 * (2 * c.w + tt) + c.lr] = sacc[it][tt][r];
+                    st[kt][4 * j + r] = v[r];
+            }
+        __syncthreads();
+        for (int k = 0; k < nch; ++k) {
+            const int stg = k % kStages, par = k & 1;
+            // the chunk's operands, all requested before the first product
+            h8 wf[16], kf[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wf[i] = sm.wt[stg][i][lane];
+            const h8 ua[2][2] = {{sm.ut[stg][0][lane][0], sm.ut[stg][0][lane][1]},
+                                 {sm.ut[stg][1][lane][0], sm.ut[stg][1][lane][1]}};
+            const float eglast = sm.eg[stg][CH - 1];
+            __builtin_amdgcn_sched_barrier(0);
+            h8 bs[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bs[s][e] = static_cast<_Float16>(st[s >> 1][8 * (s & 1) + e]);
+            f16v z0 = zero16(), z1 = zero16();
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                z0 = mma32(wf[s], bs[s], z0);
+                z1 = mma32(wf[8 + s], bs[s], z1);
+            }
+            // (e^{G_n - G} K)^T is read while Z is in the matrix pipe
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                kf[i] = sm.kd[stg][i][lane];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                st[kt] *= eglast;
+            // S0^T for the output waves, off the recurrence's path
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                sm.xs[par][s][lane] = bs[s];
+            // U = U~ - Z (accumulator order: token 32 tt + 8 (v / 4) + 4 hi + v % 4, row c32);
+            // token step s of U is accumulator values 8 (s & 1) .. + 7 of tile s / 2
+            h8 bu[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int tt = s >> 1, j = s & 1;
+                const f16v& z = tt ? z1 : z0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bu[s][e] = static_cast<_Float16>(static_cast<float>(ua[tt][j][e]) - z[8 * j + e]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    st[kt] = mma32(kf[kt * 4 + s], bu[s], st[kt]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                sm.xu[par][s][lane] = bu[s];
+            __syncthreads();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = st[kt][4 * j + r];
+                *reinterpret_cast<f4*>(Sh + 32 * kt + 8 * j + 4 * hi) = v;
+            }
     } else {
+        // ---- output, token tile tt
+        const int tt = wave - 1;
         const size_t ostride = static_cast<size_t>(Hv) * D;
-        float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
-        OutOps ring[kScanRing];
+        float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0 + c32;
+        auto load = [&](OutOps& op, int cl) {
+            const _Float16* qc = ws.q + (kbase + cl) * kChunkQK;
+            const _Float16* pc = ws.P + (vbase + cl) * kChunkP;
 #pragma unroll
-        for (int p = 0; p < kScanRing; ++p)
-            load_out(ring[p], ws, c, min(p, nch - 1));
+            for (int s = 0; s < 8; ++s)
+                op.qf[s] = ldfrag(qc, tt * 8 + s, lane);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                op.pf[s] = ldfrag(pc, tt * 4 + s, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                op.eg[j] = *reinterpret_cast<const f4*>(ws.eg + hbase + cl * CH + 32 * tt + 8 * j + 4 * hi);
+        };
+        OutOps ring[kOutRing];
+#pragma unroll
+        for (int p = 0; p < kOutRing; ++p)
+            load(ring[p], min(p, nch - 1));
+        __syncthreads();
+        __syncthreads();
         auto step = [&](auto pc, int cl) {
             constexpr int P = decltype(pc)::value;
+            const OutOps& op = ring[P];
+            const int par = cl & 1;
+            h8 xs[8], xu[4];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                xs[s] = sm.xs[par][s][lane];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xu[s] = sm.xu[par][s][lane];
+            __builtin_amdgcn_sched_barrier(0);
+            f16v y = zero16(), pu = zero16();
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                y = mma32(op.qf[s], xs[s], y);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                pu = mma32(op.pf[s], xu[s], pu);
+            const int n = min(CH, len - cl * CH);
             float* orow = obase + static_cast<size_t>(cl) * CH * ostride;
-            if (cl < nfull)
-                out_chunk<P & 1, false>(ring[P], sm, c, orow, CH, ostride);
-            else
-                out_chunk<P & 1, true>(ring[P], sm, c, orow, tailn, ostride);
-            load_out(ring[P], ws, c, min(cl + kScanRing, nch - 1));
+            if (n == CH) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        orow[static_cast<size_t>(32 * tt + 8 * j + 4 * hi + r) * ostride] =
+                            kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 32 * tt + 8 * j + 4 * hi + r;
+                        if (t < n)
+                            orow[static_cast<size_t>(t) * ostride] =
+                                kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]);
+                    }
+            }
+            load(ring[P], min(cl + kOutRing, nch - 1));
+            __syncthreads();
         };
         int cl0 = 0;
-        for (; cl0 + kScanRing <= nch; cl0 += kScanRing) {
+        for (; cl0 + kOutRing <= nch; cl0 += kOutRing) {
             step(std::integral_constant<int, 0>{}, cl0);
             step(std::integral_constant<int, 1>{}, cl0 + 1);
             step(std::integral_constant<int, 2>{}, cl0 + 2);
-            step(std::integral_constant<int, 3>{}, cl0 + 3);
         }
         if (cl0 < nch)
             step(std::integral_constant<int, 0>{}, cl0);
         if (cl0 + 1 < nch)
             step(std::integral_constant<int, 1>{}, cl0 + 1);
-        if (cl0 + 2 < nch)
-            step(std::integral_constant<int, 2>{}, cl0 + 2);
     }
 }
 
@@ -787,7 +822,7 @@ hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int
                            seg0, SP, nch, g.Hk, g.Hv);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), dim3(512), 0, s, S, o, W, T,
+        hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), dim3(256), 0, s, S, o, W, T,
                            seg0, SP, nch, g.B, g.Hk, g.Hv);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
