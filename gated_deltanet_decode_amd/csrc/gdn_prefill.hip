@@ -266,11 +266,12 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
 struct alignas(16) TriSmem {
     float T[CH][TP];              // (I + A)^-1; rows 16-byte aligned for the fragment reads
     float A[CH][MP];
-    float tmp[3][16][17];
+    float tmp[3][16][16];         // per-wave intermediate of the off-diagonal blocks
     float G[CH];     // cumulative log2 decay inside the chunk
     float beta[CH];
     float bv[CH];    // beta_t            (scales V in U~)
     float bk[CH];    // beta_t e^{G_t}    (scales K in W~)
+    float ed[CH];    // e^{G_last - G_t}  (scales K in the scan's update operand)
 };
 
 __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, const float* __restrict__ bg, Ws ws,
@@ -326,18 +327,7 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         sm.T[16 * I + r][16 * J + c] = 0.0f;
     }
 
-    f16v kk = zero16(), kq = zero16();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        if (wave == 1) {
-            kk = mma32(fa[s], fb[s], kk);
-        } else {
-            if (wave != 2)
-                kk = mma32(fa[s], fa[s], kk);
-            kq = mma32(fa[s], fb[s], kq);
-        }
-    }
-
+    // gates first in program order: their inputs were requested first
     if (wave == 0) {
         float la = 0.0f, be = 0.0f;
         if (lane < n) {
@@ -352,12 +342,25 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         }
         const float l2 = la * kLog2e;             // G in log2 units
         const float eg = __builtin_amdgcn_exp2f(l2);
+        sm.ed[lane] = __builtin_amdgcn_exp2f(__shfl(l2, kWave - 1, kWave) - l2);
         sm.G[lane] = l2;
         sm.beta[lane] = be;
         sm.bv[lane] = be;
         sm.bk[lane] = be * eg;
         ws.eg[hs + lane] = eg;
     }
+    f16v kk = zero16(), kq = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if (wave == 1) {
+            kk = mma32(fa[s], fb[s], kk);
+        } else {
+            if (wave != 2)
+                kk = mma32(fa[s], fa[s], kk);
+            kq = mma32(fa[s], fb[s], kq);
+        }
+    }
+
     __syncthreads();
 
     // Accumulator v of tile (mt, nt) is row t' = 32 mt + 8 (v / 4) + 4 hi + v % 4
@@ -414,30 +417,44 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         }
     }
     __syncthreads();
-    // off-diagonal blocks, one block diagonal at a time: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-    for (int lvl = 1; lvl < 4; ++lvl) {
-        const int nb = 4 - lvl;
-        for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) {
-            const int q = e / 256, r = (e / 16) % 16, c = e % 16;
-            const int I = lvl + q, J = q;
-            float s = 0.0f;
-            for (int K = J; K < I; ++K)
+    // off-diagonal blocks, one block diagonal at a time: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
+    // Wave I computes block (I, I - lvl) alone (lane: row r, four columns), its
+    // intermediate in LDS private to the wave, so one barrier per level.
+    {
+        const int r = lane >> 2, c0 = 4 * (lane & 3);
+        for (int lvl = 1; lvl < 4; ++lvl) {
+            if (wave >= lvl) {
+                const int I = wave, J = wave - lvl;
+                f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma nounroll
+                for (int K = J; K < I; ++K)
+#pragma unroll 4
+                    for (int k = 0; k < 16; ++k) {
+                        const float av = sm.A[16 * I + r][16 * K + k];
+                        const f4 tv = *reinterpret_cast<const f4*>(&sm.T[16 * K + k][16 * J + c0]);
 #pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    s = __builtin_fmaf(sm.A[16 * I + r][16 * K + k], sm.T[16 * K + k][16 * J + c], s);
-            sm.tmp[q][r][c] = s;
-        }
-        __syncthreads();
-        for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) {
-            const int q = e / 256, r = (e / 16) % 16, c = e % 16;
-            const int I = lvl + q, J = q;
-            float s = 0.0f;
+                        for (int e = 0; e < 4; ++e)
+                            acc[e] = __builtin_fmaf(av, tv[e], acc[e]);
+                    }
+                *reinterpret_cast<f4*>(&sm.tmp[wave - 1][r][c0]) = acc;
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+                __builtin_amdgcn_wave_barrier();
+                f4 res = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                s = __builtin_fmaf(sm.T[16 * I + r][16 * I + k], sm.tmp[q][k][c], s);
-            sm.T[16 * I + r][16 * J + c] = -s;
+                for (int k = 0; k < 16; ++k) {
+                    const float tv = sm.T[16 * I + r][16 * I + k];
+                    const f4 xv = *reinterpret_cast<const f4*>(&sm.tmp[wave - 1][k][c0]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        res[e] = __builtin_fmaf(tv, xv[e], res[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    res[e] = -res[e];
+                *reinterpret_cast<f4*>(&sm.T[16 * I + r][16 * J + c0]) = res;
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     // T as fragments (row tile tt, k-step s over t'); the same registers are
@@ -458,7 +475,6 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
     // beta V (column tile w) and beta e^G K (key tile w) with the token as k;
     // e^{G_last - G} K (key tile w) is the scan's state-update operand
     h8 vs[4], ks[4];
-    const float glast = sm.G[CH - 1];
     _Float16* kdo = ws.kd + hc;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -469,7 +485,7 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
             const float kv = static_cast<float>(kf[s][e]);
             vs[s][e] = static_cast<_Float16>(static_cast<float>(vf[s][e]) * sm.bv[tp]);
             ks[s][e] = static_cast<_Float16>(kv * sm.bk[tp]);
-            kd[e] = static_cast<_Float16>(kv * __builtin_amdgcn_exp2f(glast - sm.G[tp]));
+            kd[e] = static_cast<_Float16>(kv * sm.ed[tp]);
         }
         *reinterpret_cast<h8*>(kdo + ((wave * 4 + s) * 64 + lane) * 8) = kd;
     }
