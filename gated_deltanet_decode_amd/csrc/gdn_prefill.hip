@@ -46,7 +46,7 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 constexpr int D = 128;       // head width handled by the prefill kernels
 constexpr int CH = 64;       // chunk length
 constexpr int SEG = 2048;    // tokens per segment
-constexpr int TB = 16;       // tokens per conv workgroup
+constexpr int TB = 16;       // tokens per conv sub-block (one k-step of a chunk)
 constexpr int DS = 32;       // state rows per scan workgroup
 constexpr int NS = D / DS;   // scan workgroups per value head
 constexpr int MP = CH + 1;   // fp32 pitch of A (a 64x64 matrix) in LDS
@@ -149,115 +149,153 @@ __device__ __forceinline__ float conv_silu_fast(const float w[4], const float wi
 
 // ------------------------------------------------------------ conv + norm
 
+// Two adjacent channels of one token, loaded together.
+template <typename Act>
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+    using raw = uint32_t;
+    __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    __device__ static raw make(uint16_t a, uint16_t b) { return a | (static_cast<uint32_t>(b) << 16); }
+    __device__ static float lo(raw v) { return __uint_as_float(v << 16); }
+    __device__ static float hi(raw v) { return __uint_as_float(v & 0xFFFF0000u); }
+};
+template <>
+struct Pair<float> {
+    using raw = float2;
+    __device__ static raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    __device__ static raw make(float a, float b) { return make_float2(a, b); }
+    __device__ static float lo(raw v) { return v.x; }
+    __device__ static float hi(raw v) { return v.y; }
+};
+
+constexpr int SUB = 2;   // 16-token sub-blocks per conv workgroup
+
+// One workgroup per (sequence, q/k head, 32 tokens), one thread per pair of
+// adjacent channels of the head's group (q, k and its value heads).  Every
+// window load of both sub-blocks is issued before the first is used, and the
+// grid is small enough that all workgroups are resident at once.
 template <typename Act>
 __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, const Act* __restrict__ tail,
                                                    const Act* __restrict__ w, Ws ws, int T, int seg0, int SP,
-                                                   int nblk, int B, int Hk, int Hv, int C) {
-    __shared__ float ys[TB][2 * D];                  // q~ | k~ of the block, fp32
-    __shared__ __align__(16) _Float16 qkh[2][TB][D]; // q^, k^ of the block, fp16
-    // The CH / TB blocks of one chunk write the two halves of the same
-    // q^ / k^ fragments; they share an XCD (blockIdx % 8 picks it).
-    constexpr int BPC = CH / TB;                     // blocks per chunk
-    const int nch = nblk / BPC;
+                                                   int nch, int B, int Hk, int Hv, int C) {
+    __shared__ __align__(16) float ys[TB][2 * D];    // q~ | k~ of a sub-block, fp32
+    __shared__ __align__(16) _Float16 qkh[2][TB][D]; // q^, k^ of a sub-block, fp16
+    // The workgroups of one chunk write the two halves of the same q^ / k^
+    // fragments; they share an XCD (blockIdx % 8 picks it).
+    constexpr int BPC = CH / (SUB * TB);             // workgroups per chunk
     const int xcd = blockIdx.x % 8, r8 = blockIdx.x / 8;
     const int chunk_id = (r8 / BPC) * 8 + xcd;       // (sequence, q/k head, chunk of the segment)
     if (chunk_id >= B * Hk * nch)
         return;
-    const int tb = (chunk_id % nch) * BPC + r8 % BPC;
+    const int cl = chunk_id % nch;
     const int g = (chunk_id / nch) % Hk;
     const int bq = chunk_id / (nch * Hk);
+    const int cb = (r8 % BPC) * SUB * TB;            // chunk offset of the workgroup's first token
+    const int t0 = seg0 + cl * CH + cb;              // its prompt index
     const int G = Hv / Hk;
     const int NC = SP / CH;
-    const int t0 = seg0 + tb * TB;                   // prompt index of the block's first token
-    const int sl = tb * TB;                          // segment index of the same token
-    const int cl = sl / CH, co = sl % CH;            // its chunk and offset in the chunk
-    const int ks = co / TB;                          // the block's tokens are k-step ks of the chunk
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const Act* xb = x + static_cast<size_t>(bq) * T * C;
     const Act* tbq = tail + static_cast<size_t>(bq) * C * 4;
-    const int per_group = (2 + G) * D;
-
-    // Two channels per thread (the block has per_group / 2 threads); the
-    // window loads of both are issued before either is used.
-    int chs[2], cs[2];
-    float wfs[2][4];
-    float hist[2][TB + 3];
+    const int npair = (2 + G) * D / 2;
+    const bool active = static_cast<int>(threadIdx.x) < npair;
+    const int ch = 2 * (active ? static_cast<int>(threadIdx.x) : npair - 1);   // first channel in the group
+    const int cg = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
+    using P = Pair<Act>;
+    float wf0[4], wf1[4];
+    Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(cg) * 4), wf0);
+    Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(cg + 1) * 4), wf1);
+    typename P::raw hist[SUB * TB + 3];
+    if (t0 >= 3) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int ch0 = threadIdx.x + k * blockDim.x;
-        const int ch = ch0 < per_group ? ch0 : per_group - 1;
-        chs[k] = ch0;
-        cs[k] = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
-        Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(cs[k]) * 4), wfs[k]);
-        // unconditional loads from selected addresses: all of them in flight at once
-#pragma unroll
-        for (int m = 0; m < TB + 3; ++m) {
+        for (int m = 0; m < SUB * TB + 3; ++m) {
             const int t = t0 + m - 3;
-            const int tc = t < T ? t : T - 1;
-            const Act* src = t < 0 ? tbq + static_cast<size_t>(cs[k]) * 4 + 4 + t : xb + static_cast<size_t>(tc) * C + cs[k];
-            hist[k][m] = widen(*src);
+            hist[m] = P::load(xb + static_cast<size_t>(t < T ? t : T - 1) * C + cg);
+        }
+    } else {   // the prompt's first tokens: the window reaches into the tail
+#pragma unroll
+        for (int m = 0; m < SUB * TB + 3; ++m) {
+            const int t = t0 + m - 3;
+            hist[m] = t < 0 ? P::make(tbq[static_cast<size_t>(cg) * 4 + 4 + t], tbq[static_cast<size_t>(cg + 1) * 4 + 4 + t])
+                            : P::load(xb + static_cast<size_t>(t < T ? t : T - 1) * C + cg);
         }
     }
+    const size_t qkc = ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * kChunkQK;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int ch = chs[k];
-        if (ch >= per_group)
-            continue;
-        float yv[TB];
+    for (int sb = 0; sb < SUB; ++sb) {
+        const int co = cb + sb * TB;                 // chunk offset of the sub-block's first token
+        const int ks = co / TB;                      // the sub-block's tokens are k-step ks of the chunk
+        float y0[TB], y1[TB];
 #pragma unroll
-        for (int j = 0; j < TB; ++j)
-            yv[j] = (t0 + j < T) ? conv_silu_fast(wfs[k], &hist[k][j]) : 0.0f;
-        if (ch < 2 * D) {
+        for (int j = 0; j < TB; ++j) {
+            float w0[4], w1[4];
 #pragma unroll
-            for (int j = 0; j < TB; ++j)
-                ys[j][ch] = yv[j];
-        } else {
-            // v^T: row d, k = token; this thread owns both lane halves of row d
-            const int h = G * g + (ch - 2 * D) / D;
-            const int d = (ch - 2 * D) % D;
-            _Float16* vc = ws.vt + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkQK;
+            for (int m = 0; m < 4; ++m) {
+                w0[m] = P::lo(hist[sb * TB + j + m]);
+                w1[m] = P::hi(hist[sb * TB + j + m]);
+            }
+            const bool valid = t0 + sb * TB + j < T;
+            y0[j] = valid ? conv_silu_fast(wf0, w0) : 0.0f;
+            y1[j] = valid ? conv_silu_fast(wf1, w1) : 0.0f;
+        }
+        if (active) {
+            if (ch < 2 * D) {
 #pragma unroll
-            for (int hi = 0; hi < 2; ++hi) {
-                h8 v;
+                for (int j = 0; j < TB; ++j)
+                    *reinterpret_cast<float2*>(&ys[j][ch]) = make_float2(y0[j], y1[j]);
+            } else {
+                // v^T: rows d and d + 1, k = token; this thread owns both lane halves of each row
+                const int h = G * g + (ch - 2 * D) / D;
+                const int d = (ch - 2 * D) % D;
+                _Float16* vc = ws.vt + ((static_cast<size_t>(bq) * Hv + h) * NC + cl) * kChunkQK;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    v[e] = static_cast<_Float16>(yv[kperm(hi, e)]);
-                *reinterpret_cast<h8*>(vc + frag_base(d, ks, CH / 16, hi)) = v;
+                for (int hi = 0; hi < 2; ++hi) {
+                    h8 v0, v1;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        v0[e] = static_cast<_Float16>(y0[kperm(hi, e)]);
+                        v1[e] = static_cast<_Float16>(y1[kperm(hi, e)]);
+                    }
+                    *reinterpret_cast<h8*>(vc + frag_base(d, ks, CH / 16, hi)) = v0;
+                    *reinterpret_cast<h8*>(vc + frag_base(d + 1, ks, CH / 16, hi)) = v1;
+                }
             }
         }
-    }
-    __syncthreads();
-    const int nwaves = blockDim.x / kWave;
-    for (int vec = wave; vec < 2 * TB; vec += nwaves) {
-        const int tl = vec >> 1, which = vec & 1;
-        const float e0 = ys[tl][which * D + lane];
-        const float e1 = ys[tl][which * D + lane + kWave];
-        const float ss = group_sum<kWave>(__builtin_fmaf(e1, e1, e0 * e0));
-        const float r = __builtin_amdgcn_rsqf(ss + kEps);
-        qkh[which][tl][lane] = static_cast<_Float16>(e0 * r);
-        qkh[which][tl][lane + kWave] = static_cast<_Float16>(e1 * r);
-    }
-    __syncthreads();
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    // q^, k^: row = token co + tl, k = key; slot group (hi) of key step s holds
-    // keys 16 s + 4 hi .. + 3 and 16 s + 8 + 4 hi .. + 3.
-    const size_t qkc = ((static_cast<size_t>(bq) * Hk + g) * NC + cl) * kChunkQK;
-    for (int idx = threadIdx.x; idx < 2 * (D / 16) * 2 * TB; idx += blockDim.x) {
-        const int tl = idx % TB, hi = (idx / TB) & 1, s = (idx / (2 * TB)) % (D / 16), which = idx / (D / 16 * 2 * TB);
-        const h4 lo = *reinterpret_cast<const h4*>(&qkh[which][tl][16 * s + 4 * hi]);
-        const h4 up = *reinterpret_cast<const h4*>(&qkh[which][tl][16 * s + 8 + 4 * hi]);
-        const h8 v = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-        *reinterpret_cast<h8*>((which ? ws.k : ws.q) + qkc + frag_base(co + tl, s, D / 16, hi)) = v;
-    }
-    // k^T: row = key, k = token
-    for (int idx = threadIdx.x; idx < 2 * D; idx += blockDim.x) {
-        const int key = idx % D, hi = idx / D;
-        h8 v;
+        __syncthreads();
+        const int nwaves = blockDim.x / kWave;
+        for (int vec = wave; vec < 2 * TB; vec += nwaves) {
+            const int tl = vec >> 1, which = vec & 1;
+            const float e0 = ys[tl][which * D + lane];
+            const float e1 = ys[tl][which * D + lane + kWave];
+            const float ss = group_sum<kWave>(__builtin_fmaf(e1, e1, e0 * e0));
+            const float r = __builtin_amdgcn_rsqf(ss + kEps);
+            qkh[which][tl][lane] = static_cast<_Float16>(e0 * r);
+            qkh[which][tl][lane + kWave] = static_cast<_Float16>(e1 * r);
+        }
+        __syncthreads();
+        // q^, k^: row = token co + tl, k = key; slot group (hi) of key step s holds
+        // keys 16 s + 4 hi .. + 3 and 16 s + 8 + 4 hi .. + 3.
+        for (int idx = threadIdx.x; idx < 2 * (D / 16) * 2 * TB; idx += blockDim.x) {
+            const int tl = idx % TB, hi = (idx / TB) & 1, s = (idx / (2 * TB)) % (D / 16), which = idx / (D / 16 * 2 * TB);
+            const h4 lo = *reinterpret_cast<const h4*>(&qkh[which][tl][16 * s + 4 * hi]);
+            const h4 up = *reinterpret_cast<const h4*>(&qkh[which][tl][16 * s + 8 + 4 * hi]);
+            const h8 v = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+            *reinterpret_cast<h8*>((which ? ws.k : ws.q) + qkc + frag_base(co + tl, s, D / 16, hi)) = v;
+        }
+        // k^T: row = key, k = token
+        for (int idx = threadIdx.x; idx < 2 * D; idx += blockDim.x) {
+            const int key = idx % D, hi = idx / D;
+            h8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = qkh[1][kperm(hi, e)][key];
-        *reinterpret_cast<h8*>(ws.kt + qkc + frag_base(key, ks, CH / 16, hi)) = v;
+            for (int e = 0; e < 8; ++e)
+                v[e] = qkh[1][kperm(hi, e)][key];
+            *reinterpret_cast<h8*>(ws.kt + qkc + frag_base(key, ks, CH / 16, hi)) = v;
+        }
+        if (sb + 1 < SUB)
+            __syncthreads();   // ys and qkh are reused by the next sub-block
     }
 }
 
@@ -819,17 +857,16 @@ hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int
     for (int seg0 = 0; seg0 < T; seg0 += pf::SEG) {
         const int len = std::min(pf::SEG, T - seg0);
         const int nch = (len + pf::CH - 1) / pf::CH;
-        const int nblk = nch * (pf::CH / pf::TB);
         const int chunks = g.B * g.Hk * nch;
-        const dim3 cgrid(static_cast<unsigned>(8 * ((chunks + 7) / 8) * (pf::CH / pf::TB)));
+        const dim3 cgrid(static_cast<unsigned>(8 * ((chunks + 7) / 8) * (pf::CH / (pf::SUB * pf::TB))));
         const dim3 cblock(static_cast<unsigned>(((2 + G) * pf::D / 2 + kWave - 1) / kWave * kWave));
         if (g.bf16)
             hipLaunchKernelGGL(pf::conv_kernel<uint16_t>, cgrid, cblock, 0, s, static_cast<const uint16_t*>(x),
                                static_cast<const uint16_t*>(tail), static_cast<const uint16_t*>(w), W, T, seg0, SP,
-                               nblk, g.B, g.Hk, g.Hv, g.C);
+                               nch, g.B, g.Hk, g.Hv, g.C);
         else
             hipLaunchKernelGGL(pf::conv_kernel<float>, cgrid, cblock, 0, s, static_cast<const float*>(x),
-                               static_cast<const float*>(tail), static_cast<const float*>(w), W, T, seg0, SP, nblk,
+                               static_cast<const float*>(tail), static_cast<const float*>(w), W, T, seg0, SP, nch,
                                g.B, g.Hk, g.Hv, g.C);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
