@@ -352,11 +352,6 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         fa[s] = ldfrag(kA, mt * 8 + s, lane);
         fb[s] = ldfrag(kB, nt * 8 + s, lane);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        vf[s] = ldfrag(ws.vt + hc, wave * 4 + s, lane);
-        kf[s] = ldfrag(ws.kt + qkc, wave * 4 + s, lane);
-    }
     // upper blocks of T are zero (the diagonal blocks are written whole below)
     for (int e = threadIdx.x; e < 6 * 256; e += blockDim.x) {
         const int blk = e / 256, r = (e / 16) % 16, c = e % 16;
@@ -399,6 +394,13 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         }
     }
 
+    // v and k^T fragments are needed only after the inverse: requested once
+    // the products have freed fa / fb, which keeps the workgroup at 4 per CU
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        vf[s] = ldfrag(ws.vt + hc, wave * 4 + s, lane);
+        kf[s] = ldfrag(ws.kt + qkc, wave * 4 + s, lane);
+    }
     __syncthreads();
 
     // Accumulator v of tile (mt, nt) is row t' = 32 mt + 8 (v / 4) + 4 hi + v % 4
