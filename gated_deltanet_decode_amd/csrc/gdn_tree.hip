@@ -217,12 +217,15 @@ __device__ __forceinline__ void tok_load(TokOps<D>& t, const NodeSmem<D, ROWS, M
 //   kq  f32 [n][Hk]       k^.q^
 //   v   f32 [n][Hv][D]    conv output of each value head's v channels
 //   ab  f32 [n][Hv][2]    alpha, beta
+// abk holds (alpha, beta, k^.q^, 0) per (node, value head): the walk loads
+// it with a lane-dependent address, so it is a vector load counted with the
+// other vector loads rather than a scalar load sharing the LDS counter.
 struct TreeWs {
-    float *qk, *kq, *v, *ab;
+    float *qk, *v, *abk;
 };
 
 size_t tree_ws_bytes(int n, int Hk, int Hv, int D) {
-    return static_cast<size_t>(n) * (2ull * Hk * D + Hk + static_cast<size_t>(Hv) * D + 2ull * Hv) * 4 + 4 * 256;
+    return static_cast<size_t>(n) * (2ull * Hk * D + static_cast<size_t>(Hv) * D + 4ull * Hv) * 4 + 3 * 256;
 }
 
 static TreeWs tree_ws_carve(void* base, int n, int Hk, int Hv, int D) {
@@ -231,9 +234,8 @@ static TreeWs tree_ws_carve(void* base, int n, int Hk, int Hv, int D) {
     TreeWs w;
     auto take = [&](size_t cnt) { float* r = reinterpret_cast<float*>(p); p = align(p + cnt * 4); return r; };
     w.qk = take(static_cast<size_t>(n) * Hk * 2 * D);
-    w.kq = take(static_cast<size_t>(n) * Hk);
     w.v = take(static_cast<size_t>(n) * Hv * D);
-    w.ab = take(static_cast<size_t>(n) * Hv * 2);
+    w.abk = take(static_cast<size_t>(n) * Hv * 4);
     return w;
 }
 
@@ -292,8 +294,9 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
         const int h = G * g + threadIdx.x;
         float al, be;
         gates(a[static_cast<size_t>(i) * Hv + h], b[static_cast<size_t>(i) * Hv + h], al, be);
-        ws.ab[(static_cast<size_t>(i) * Hv + h) * 2] = al;
-        ws.ab[(static_cast<size_t>(i) * Hv + h) * 2 + 1] = be;
+        ws.abk[(static_cast<size_t>(i) * Hv + h) * 4] = al;
+        ws.abk[(static_cast<size_t>(i) * Hv + h) * 4 + 1] = be;
+        ws.abk[(static_cast<size_t>(i) * Hv + h) * 4 + 3] = 0.0f;
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -316,8 +319,8 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
                 dst[D + e] = kv[j];
             }
         }
-        if (lane == 0)
-            ws.kq[static_cast<size_t>(i) * Hk + g] = kq;
+        if (lane < G)
+            ws.abk[(static_cast<size_t>(i) * Hv + G * g + lane) * 4 + 2] = kq;
     }
 }
 
@@ -345,8 +348,14 @@ __device__ __forceinline__ void walk_all(F& f, std::integer_sequence<int, I...>)
 template <int D>
 struct NodeOps {
     float4 k[Row<D>::NV], q[Row<D>::NV];
-    float v, alpha, beta, kq;
+    float v, abk;   // abk: lane l holds element l % 4 of (alpha, beta, k^.q^, 0)
 };
+
+// Value of lane 4 (l / 4) + E in lane l: broadcasts one element of abk.
+template <int E>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), E * 0x55, 0xF, 0xF, false));
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, int n,
@@ -401,16 +410,14 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
             t.q[j] = *reinterpret_cast<const float4*>(qk + R::key(j, r));
         }
         t.v = ws.v[(static_cast<size_t>(i) * Hv + h) * D + row];
-        t.alpha = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2];
-        t.beta = ws.ab[(static_cast<size_t>(i) * Hv + h) * 2 + 1];
-        t.kq = ws.kq[static_cast<size_t>(i) * Hk + grp];
+        t.abk = ws.abk[(static_cast<size_t>(i) * Hv + h) * 4 + (lane & 3)];
     };
     NodeOps<D> ring[kRing];
 #pragma unroll
     for (int p = 0; p < kRing; ++p)
         load_node(ring[p], p);
     float4 s[NV];
-    float* oh = o + static_cast<size_t>(h) * D + row;
+    float outv[kMaxNodes];   // o of each walk step, stored after the walk
     int dprev = 0;
     // One walk step per node, expanded at compile time (at most kMaxNodes),
     // so that ring slots are static registers and every wait on a slot counts
@@ -420,7 +427,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
         constexpr int p = it % kRing;
         if (it >= n)
             return false;
-        const int node = __builtin_amdgcn_readlane(ord_l, it);
         const int d = __builtin_amdgcn_readlane(dep_l, it);
         if (d == 1) {
 #pragma unroll
@@ -432,21 +438,25 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
                 s[j] = sm.stack[d - 2][j][tid];
         }
         const NodeOps<D>& t = ring[p];
-        const float out = row_update<D>(s, t.k, t.q, t.alpha, t.beta, t.v, t.kq);
+        outv[it] = row_update<D>(s, t.k, t.q, quad_bcast<0>(t.abk), quad_bcast<1>(t.abk), t.v, quad_bcast<2>(t.abk));
         if (d < kMaxDepth) {
 #pragma unroll
             for (int j = 0; j < NV; ++j)
                 sm.stack[d - 1][j][tid] = s[j];
         }
-        // Every lane of the row holds the same sum (the butterfly adds
-        // commuted pairs), so all of them store it: no exec branch.
-        oh[static_cast<size_t>(node) * Hv * D] = out;
         dprev = d;
         if (it + kRing < kMaxNodes)
             load_node(ring[p], it + kRing);
         return true;
     };
     walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
+    // Every lane of a row holds the same sum (the butterfly adds commuted
+    // pairs), so all of them store it: no exec branch.
+    float* oh = o + static_cast<size_t>(h) * D + row;
+#pragma unroll
+    for (int it = 0; it < kMaxNodes; ++it)
+        if (it < n)
+            oh[static_cast<size_t>(__builtin_amdgcn_readlane(ord_l, it)) * Hv * D] = outv[it];
 }
 
 // Runs f(D, Act) for the geometry's head width and activation type.
