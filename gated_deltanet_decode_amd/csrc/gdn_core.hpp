@@ -69,6 +69,17 @@ struct Quad<float> {
     __device__ static float elem(raw v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 };
 
+// State rows are streamed once per call: non-temporal loads and stores keep
+// them from displacing what the caches hold for reuse.
+typedef float nt4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+    const nt4 v = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float* p, float4 v) {
+    __builtin_nontemporal_store(nt4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt4*>(p));
+}
+
 // ------------------------------------------------------------ scalar pieces
 
 // y = SiLU(sum_j w[j] * win[j]) with the taps summed oldest first.

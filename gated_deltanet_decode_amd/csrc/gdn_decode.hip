@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
         row[p] = (blk * PASSES + p) * ROWS_PASS + wave * RPW + lane / LPR;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-            s[p][j] = *reinterpret_cast<const float4*>(Sh + row[p] * D + R::key(j, r));
+            s[p][j] = load_stream(Sh + row[p] * D + R::key(j, r));
     }
 
     __shared__ __align__(16) float qs[D];
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
         const float out = row_update<D>(s[p], kk, qq, alpha, beta, v[p], kq);
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-            *reinterpret_cast<float4*>(Sh + row[p] * D + R::key(j, r)) = s[p][j];
+            store_stream(Sh + row[p] * D + R::key(j, r), s[p][j]);
         if (r == 0)
             oh[row[p]] = out;
     }

@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     float4 base[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        base[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
+        base[j] = load_stream(Sh + row * D + R::key(j, r));
 
     if (wave == 0) {
         const bool ok = tree_tables_wave(n, parent, sm.depth, sm.order);
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     float4 s[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        s[j] = *reinterpret_cast<const float4*>(Sh + row * D + R::key(j, r));
+        s[j] = load_stream(Sh + row * D + R::key(j, r));
 
     // Token i of the commit is path position i; its ancestors are the
     // positions before it.  Node ids are clamped into the tree so that every
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        *reinterpret_cast<float4*>(Sh + row * D + R::key(j, r)) = s[j];
+        store_stream(Sh + row * D + R::key(j, r), s[j]);
 }
 
 // The tail after a commit holds the last four raw inputs of (old tail ++ path).
