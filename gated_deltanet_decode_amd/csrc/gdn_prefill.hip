@@ -130,6 +130,10 @@ __device__ __forceinline__ int frag_base(int row, int ks, int nks, int hi) {
 __device__ __forceinline__ int acc_base(int rt, int ct, int nct, int lane) { return ((rt * nct + ct) * 64 + lane) * 16; }
 // Fragment `tile` of a fragment-ordered matrix: one contiguous 1 KB run per wave.
 __device__ __forceinline__ h8 ldfrag(const _Float16* m, int tile, int lane) { return ld8(m + tile * 512 + lane * 8); }
+// The same for a fragment read once (non-temporal: it need not stay cached).
+__device__ __forceinline__ h8 ldfrag_once(const _Float16* m, int tile, int lane) {
+    return __builtin_nontemporal_load(reinterpret_cast<const h8*>(m + tile * 512 + lane * 8));
+}
 constexpr int kChunkQK = CH * D;   // fp16 elements of one chunk of q, k, k^T, v^T, U~, W~, kd
 constexpr int kChunkP = CH * CH;   // fp16 elements of one chunk of P
 
@@ -155,7 +159,7 @@ struct Pair;
 template <>
 struct Pair<uint16_t> {
     using raw = uint32_t;
-    __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    __device__ static raw load(const uint16_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
     __device__ static raw make(uint16_t a, uint16_t b) { return a | (static_cast<uint32_t>(b) << 16); }
     __device__ static float lo(raw v) { return __uint_as_float(v << 16); }
     __device__ static float hi(raw v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -163,7 +167,11 @@ struct Pair<uint16_t> {
 template <>
 struct Pair<float> {
     using raw = float2;
-    __device__ static raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    __device__ static raw load(const float* p) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 v = __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
+        return make_float2(v.x, v.y);
+    }
     __device__ static raw make(float a, float b) { return make_float2(a, b); }
     __device__ static float lo(raw v) { return v.x; }
     __device__ static float hi(raw v) { return v.y; }
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
     // the products have freed fa / fb, which keeps the workgroup at 4 per CU
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        vf[s] = ldfrag(ws.vt + hc, wave * 4 + s, lane);
+        vf[s] = ldfrag_once(ws.vt + hc, wave * 4 + s, lane);   // v^T of this value head: read once
         kf[s] = ldfrag(ws.kt + qkc, wave * 4 + s, lane);
     }
     __syncthreads();
@@ -792,8 +800,8 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        orow[static_cast<size_t>(32 * tt + 8 * j + 4 * hi + r) * ostride] =
-                            kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]);
+                        __builtin_nontemporal_store(kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]),
+                                                    orow + static_cast<size_t>(32 * tt + 8 * j + 4 * hi + r) * ostride);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -801,8 +809,8 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
                     for (int r = 0; r < 4; ++r) {
                         const int t = 32 * tt + 8 * j + 4 * hi + r;
                         if (t < n)
-                            orow[static_cast<size_t>(t) * ostride] =
-                                kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]);
+                            __builtin_nontemporal_store(kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]),
+                                                        orow + static_cast<size_t>(t) * ostride);
                     }
             }
             load(ring[P], min(cl + kOutRing, nch - 1));
