@@ -105,6 +105,7 @@ __device__ __forceinline__ h8 ld8(const _Float16* p) { return *reinterpret_cast<
 __device__ __forceinline__ f16v mma32(h8 a, h8 b, f16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f4 zero4() { return f4{0.0f, 0.0f, 0.0f, 0.0f}; }
 __device__ __forceinline__ f16v zero16() {
     f16v z;
 #pragma unroll
@@ -312,7 +313,6 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
 struct alignas(16) TriSmem {
     float T[CH][TP];              // (I + A)^-1; rows 16-byte aligned for the fragment reads
     float A[CH][MP];
-    float tmp[3][16][16];         // per-wave intermediate of the off-diagonal blocks
     float G[CH];     // cumulative log2 decay inside the chunk
     float beta[CH];
     float bv[CH];    // beta_t            (scales V in U~)
@@ -466,40 +466,28 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
     }
     __syncthreads();
     // off-diagonal blocks, one block diagonal at a time: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
-    // Wave I computes block (I, I - lvl) alone (lane: row r, four columns), its
-    // intermediate in LDS private to the wave, so one barrier per level.
+    // Wave I computes block (I, I - lvl) on fp32 16x16x4 MFMAs, lane (q, c) =
+    // (lane / 16, lane % 16).  Step s of a product takes k = 4 q + s, so the
+    // accumulators of Z = sum A_IK T_KJ (lane (q, c): rows 4 q .. 4 q + 3, column
+    // c) are directly the B operand of -T_II Z.  One barrier per level.
     {
-        const int r = lane >> 2, c0 = 4 * (lane & 3);
+        const int q = lane >> 4, c = lane & 15;
         for (int lvl = 1; lvl < 4; ++lvl) {
             if (wave >= lvl) {
                 const int I = wave, J = wave - lvl;
-                f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma nounroll
+                f4 z = zero4();
                 for (int K = J; K < I; ++K)
-#pragma unroll 4
-                    for (int k = 0; k < 16; ++k) {
-                        const float av = sm.A[16 * I + r][16 * K + k];
-                        const f4 tv = *reinterpret_cast<const f4*>(&sm.T[16 * K + k][16 * J + c0]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[e] = __builtin_fmaf(av, tv[e], acc[e]);
-                    }
-                *reinterpret_cast<f4*>(&sm.tmp[wave - 1][r][c0]) = acc;
-                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
-                __builtin_amdgcn_wave_barrier();
-                f4 res = {0.0f, 0.0f, 0.0f, 0.0f};
+                    for (int s = 0; s < 4; ++s)
+                        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.A[16 * I + c][16 * K + 4 * q + s],
+                                                                 sm.T[16 * K + 4 * q + s][16 * J + c], z, 0, 0, 0);
+                f4 t = zero4();
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const float tv = sm.T[16 * I + r][16 * I + k];
-                    const f4 xv = *reinterpret_cast<const f4*>(&sm.tmp[wave - 1][k][c0]);
+                for (int s = 0; s < 4; ++s)
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.T[16 * I + c][16 * I + 4 * q + s], z[s], t, 0, 0, 0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        res[e] = __builtin_fmaf(tv, xv[e], res[e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    res[e] = -res[e];
-                *reinterpret_cast<f4*>(&sm.T[16 * I + r][16 * J + c0]) = res;
+                for (int r = 0; r < 4; ++r)
+                    sm.T[16 * I + 4 * q + r][16 * J + c] = -t[r];
             }
             __syncthreads();
         }
