@@ -243,3 +243,24 @@ def test_pipelined_call_keeps_caller_stream_order_and_graph_capture():
         assert torch.equal(o.view(torch.int32), ref_o.view(torch.int32))
         assert torch.equal(S.view(torch.int32), ref_S.view(torch.int32))
         assert torch.equal(tail, ref_tail)
+
+
+@pytest.mark.parametrize("T", [150, 2100])
+def test_f32_activations(T):
+    """fp32 activations (the float channel-pair loads of conv, the fp32 tail),
+    from a random state and tail, within one segment and across two."""
+    shape = LayerShape(2, 6, 128, 128, 4, "f32")
+    inp = gi.prefill_inputs(12 + T, shape, T, state_sigma=0.1, tail_random=True)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail)
+
+
+@pytest.mark.parametrize("heads", [(2, 2), (1, 8)], ids=["one_v_head_per_qk_head", "eight_v_heads_per_qk_head"])
+def test_group_ratios(heads):
+    """The smallest and largest supported value heads per q/k head (1 and 8):
+    conv blocks of 192 and 640 threads, scan workgroup-to-head mapping."""
+    hk, hv = heads
+    shape = LayerShape(hk, hv, 128, 128, 4, "bf16")
+    inp = gi.prefill_inputs(14 + hv, shape, 200, state_sigma=0.1, tail_random=True)
+    o, S, tail = gpu_prefill(inp)
+    check_against_oracle(inp, o, S, tail)
