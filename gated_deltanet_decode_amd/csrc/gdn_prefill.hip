@@ -15,20 +15,20 @@
 //
 // Work split for MI355X, per segment of at most 2,048 tokens, every chunk
 // product on 32x32x16 fp16 MFMAs (fp32 accumulation):
-//   conv  (parallel over 16-token blocks x q/k heads): conv + SiLU of the
+//   conv  (parallel over 32-token blocks x q/k heads): conv + SiLU of the
 //         q/k head's channels and of its value heads' channels, q/k L2 norm;
 //         writes fp16 q^, k^, k^ transposed and v transposed, as fragments.
 //   tri   (parallel over value heads x chunks): gates and G, K K^T and K Q^T,
 //         A, the blocked inverse T in fp32 (16x16 diagonal blocks by
-//         substitution, off-diagonal blocks by block products), then
-//         U~ = T (beta V) and W~^T = (beta e^G K)^T T^T.  P, U~ and W~ are
-//         written straight from the accumulators.
+//         substitution, off-diagonal blocks by fp32 MFMA block products), then
+//         U~ = T (beta V) and W~^T = (beta e^G K)^T T^T.  P, U~, W~ and the
+//         decay-scaled k^T of the scan are written straight from registers.
 //   scan  (sequential over chunks; one workgroup per (sequence, value head,
 //         32-row slice of the state)): Z = W~ S0^T, U = U~ - Z,
 //         O = s (e^G (.) Q S0^T + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K).
 //         The state is held transposed in accumulator tiles, so the
 //         recurrence passes from one product to the next in registers.
-// The workspace holds one segment (about 114 MB at the 27B-class shape),
+// The workspace holds one segment (about 139 MB at the 27B-class shape),
 // whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
 #include <utility>
