@@ -16,8 +16,9 @@ weights, gates, o) over the time.
 
 Extra rows, each with its own roofline fraction: the same step under a hip
 graph and as two calls, the state step alone, batch-64 decode (ping-pong
-over two batches), 32-node tree verify, path commit, chunked prefill at
-T = 32,768; and the CPU oracle on a bounded sample as the host baseline.
+over two batches), 32-node tree verify and path commit at batch 1 and over
+64 sequences' trees, chunked prefill at T = 32,768; and the CPU oracle on a
+bounded sample as the host baseline.
 Inputs are seeded synthetic tensors of the workload's shapes.
 """
 from __future__ import annotations
@@ -58,14 +59,20 @@ def token_bytes(B, shape):
     return B * per_seq + C * 4 * 2
 
 
-def tree_bytes(n, shape):
+def tree_bytes(n, shape, B=1):
+    """Algorithmic bytes of one tree verify over B sequences' trees of n nodes: per sequence the
+    checkpoint read once, x, conv tail (bf16), gates, parent and o; the conv weights once."""
     Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
-    return (Hv * D * D * 4 + n * C * 2 + C * 4 * 2 + C * 4 * 2 + 2 * n * Hv * 4 + n * Hv * D * 4 + n * 4)
+    per_seq = Hv * D * D * 4 + n * C * 2 + C * 4 * 2 + 2 * n * Hv * 4 + n * Hv * D * 4 + n * 4
+    return B * per_seq + C * 4 * 2
 
 
-def commit_bytes(L, shape):
+def commit_bytes(lens, shape):
+    """Algorithmic bytes of one commit without per-token outputs (o = NULL, the caller has them
+    from verify): per sequence with L accepted tokens the state read and written, the conv
+    tail read and written, L rows of x and gates; the conv weights once."""
     Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
-    return (2 * Hv * D * D * 4 + L * C * 2 + 2 * C * 4 * 2 + C * 4 * 2 + 2 * L * Hv * 4 + L * Hv * D * 4)
+    return sum(2 * Hv * D * D * 4 + 2 * C * 4 * 2 + L * (C * 2 + 2 * Hv * 4) for L in lens) + C * 4 * 2
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "token_kernel_b1_27b_layer_counters.md")
@@ -132,7 +139,7 @@ def main():
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--buffers", type=int, default=160, help="independent states rotated through (cold runs)")
-    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,prefill,hot,cpu or all/none")
+    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,tree64,prefill,hot,cpu or all/none")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 512 MiB device copy (for byte counters)")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
     args = ap.parse_args()
@@ -147,7 +154,7 @@ def main():
     import gated_deltanet_decode_amd as gdn
     import gdn_inputs as gi
 
-    rows = set(["graph", "kernel", "b64", "tree", "commit", "prefill", "hot", "cpu"]) if args.rows == "all" else \
+    rows = set(["graph", "kernel", "b64", "tree", "commit", "tree64", "prefill", "hot", "cpu"]) if args.rows == "all" else \
         set() if args.rows == "none" else set(args.rows.split(","))
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -311,13 +318,47 @@ def main():
         if "commit" in rows:
             us = graph_time_us(torch, lambda r: gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt,
                                                                  path, None, st), nrep)
-            cbt = commit_bytes(L, shape)
+            cbt = commit_bytes([L], shape)
             res["commit_path"] = {"us": us, "path_len": L, "GBps": cbt / us / 1e3,
                                   "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt, "launch": "hipGraph"}
             if "tree_verify_n32" in res:
                 res["commit_path"]["committed_tokens_per_s"] = L / (us + res["tree_verify_n32"]["us"]) * 1e6
         assert st.item() == 0
         del Sp, Tp
+
+    # ---------------------------------------------------------------- batched tree verify + commit
+    # 64 sequences, one 32-node tree each, accepted paths of mixed lengths;
+    # two batches of checkpoints (403 MB) alternate so states come from HBM.
+    if "tree64" in rows:
+        B = 64
+        tbi = gi.tree_batch_inputs(5, shape, B, n_nodes=32, max_depth=8)
+        pool = gi.decode_inputs(105, shape, 2 * B, 1, state_sigma=0.1, tail_random=True)
+        S2 = f32(pool.state).view(2, B, Hv, D, D)
+        T2 = act(pool.tail).view(2, B, C, 4)
+        del pool
+        dB = gdn.dims(B, 16, 48, 128, 128, 4, "bf16")
+        seq = lambda arr: np.ascontiguousarray(np.swapaxes(arr, 0, 1))   # [n][B][...] -> [B][n][...]
+        xB, aB, bB, wB = act(seq(tbi.x)), f32(seq(tbi.a)), f32(seq(tbi.b)), act(tbi.w)
+        parentB = torch.from_numpy(tbi.extra["parent"]).to(dev)
+        pathB = torch.from_numpy(tbi.extra["path"]).to(dev)
+        lens = [int(np.argmax(r == -1)) if (r == -1).any() else len(r) for r in tbi.extra["path"]]
+        oB = torch.empty(B, 32, Hv, D, device=dev)
+        stB = torch.zeros(B, dtype=torch.int32, device=dev)
+        wsB = torch.empty(gdn.tree_workspace_bytes(dB, 32), dtype=torch.uint8, device=dev)
+        us = graph_time_us(torch, lambda r: gdn.tree_verify(dB, S2[r % 2], T2[r % 2], wB, parentB, xB, aB, bB, oB,
+                                                             stB, wsB), 32, reps=2)
+        tb = tree_bytes(32, shape, B)
+        res["tree_verify_b64_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
+                                      "nodes_per_s": B * 32 / us * 1e6, "bytes": tb, "launch": "hipGraph",
+                                      "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
+        us = graph_time_us(torch, lambda r: gdn.commit_path(dB, S2[r % 2], T2[r % 2], wB, parentB, xB, aB, bB, pathB,
+                                                             None, stB), 32, reps=2)
+        cbt = commit_bytes(lens, shape)
+        res["commit_path_b64"] = {"us": us, "accepted_tokens": sum(lens), "GBps": cbt / us / 1e3,
+                                  "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt, "launch": "hipGraph",
+                                  "committed_tokens_per_s": sum(lens) / (us + res["tree_verify_b64_n32"]["us"]) * 1e6}
+        assert int(stB.abs().sum().item()) == 0
+        del S2, T2, xB, aB, bB, oB, wsB
 
     # ---------------------------------------------------------------- chunked prefill
     if "prefill" in rows:

@@ -162,8 +162,12 @@ def tree_workspace_bytes(d: Dims, n_nodes: int) -> int:
 
 
 def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, workspace=None, stream=None) -> None:
-    """workspace: a device byte tensor of at least tree_workspace_bytes(d, n) bytes."""
-    n = parent.numel()
+    """One tree of n nodes per sequence: parent [B][n]; workspace: a device byte tensor of at
+    least tree_workspace_bytes(d, n) bytes; status [B] or None."""
+    B = d.batch
+    if parent.numel() % B:
+        raise ValueError("parent must be [B][n_nodes]")
+    n = parent.numel() // B
     Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
     need = tree_workspace_bytes(d, n)
     if workspace is None or workspace.device.type != "cuda" or not workspace.is_contiguous():
@@ -171,23 +175,27 @@ def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, worksp
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < need:
         raise ValueError(f"workspace of {ws_bytes} bytes, need {need}")
-    _check(_lib.gdn_tree_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, Hv * dv * dk),
-                                _t(tail, "conv_tail", d.act_torch, Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
-                                n, _t(parent, "parent", torch.int32, n), _t(x, "x", d.act_torch, n * Cc),
-                                _t(a, "a", torch.float32, n * Hv), _t(b, "b", torch.float32, n * Hv),
-                                _t(o, "o", torch.float32, n * Hv * dv), _opt(status, "tree_status", torch.int32, 1),
+    _check(_lib.gdn_tree_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
+                                _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                                n, _t(parent, "parent", torch.int32, B * n), _t(x, "x", d.act_torch, B * n * Cc),
+                                _t(a, "a", torch.float32, B * n * Hv), _t(b, "b", torch.float32, B * n * Hv),
+                                _t(o, "o", torch.float32, B * n * Hv * dv), _opt(status, "tree_status", torch.int32, B),
                                 workspace.data_ptr(), ws_bytes, _stream(stream)), "gdn_tree_verify")
 
 
 def commit_path(d: Dims, state, tail, w, parent, x, a, b, path, o=None, status=None, stream=None) -> None:
-    n, L = parent.numel(), path.numel()
+    """path [B][L]: each row root first, -1 after its end; o [B][L][Hv][dv] or None; status [B] or None."""
+    B = d.batch
+    if parent.numel() % B or path.numel() % B:
+        raise ValueError("parent must be [B][n_nodes] and path [B][path_len]")
+    n, L = parent.numel() // B, path.numel() // B
     Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
-    _check(_lib.gdn_commit_path(C.byref(d), _t(state, "state", torch.float32, Hv * dv * dk),
-                                _t(tail, "conv_tail", d.act_torch, Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
-                                n, _t(parent, "parent", torch.int32, n), _t(x, "x", d.act_torch, n * Cc),
-                                _t(a, "a", torch.float32, n * Hv), _t(b, "b", torch.float32, n * Hv),
-                                L, _t(path, "path", torch.int32, L), _opt(o, "o", torch.float32, L * Hv * dv),
-                                _opt(status, "tree_status", torch.int32, 1), _stream(stream)), "gdn_commit_path")
+    _check(_lib.gdn_commit_path(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                                n, _t(parent, "parent", torch.int32, B * n), _t(x, "x", d.act_torch, B * n * Cc),
+                                _t(a, "a", torch.float32, B * n * Hv), _t(b, "b", torch.float32, B * n * Hv),
+                                L, _t(path, "path", torch.int32, B * L), _opt(o, "o", torch.float32, B * L * Hv * dv),
+                                _opt(status, "tree_status", torch.int32, B), _stream(stream)), "gdn_commit_path")
 
 
 def tree_tables(parent, depth, order, status, stream=None) -> None:

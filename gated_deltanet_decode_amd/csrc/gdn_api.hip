@@ -144,7 +144,7 @@ size_t gdn_tree_workspace_bytes(const gdn_dims* d, int32_t n_nodes) {
     gdn::Geo g;
     if (check_dims(d, g) != GDN_OK || n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES)
         return 0;
-    return gdn::tree_ws_bytes(n_nodes, g.Hk, g.Hv, g.D);
+    return gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D);
 }
 
 gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
@@ -152,7 +152,7 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
                            float* o, int32_t* tree_status, void* workspace, size_t workspace_bytes, void* stream) {
     gdn::Geo g;
     gdn_status st = check_dims(d, g);
-    if (st == GDN_OK && g.B != 1)
+    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
         st = GDN_ERR_SHAPE;
     if (st == GDN_OK)
         st = ptrs_ok({state_ckpt, conv_tail, conv_w, parent, x, a, b, o});
@@ -162,7 +162,7 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
         st = GDN_ERR_TREE;
     if (st != GDN_OK)
         return st;
-    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(n_nodes, g.Hk, g.Hv, g.D))
+    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D))
         return GDN_ERR_WORKSPACE;
     if (!aligned16(workspace))
         return GDN_ERR_ALIGN;
@@ -175,7 +175,7 @@ gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, con
                            const int32_t* path, float* o, int32_t* tree_status, void* stream) {
     gdn::Geo g;
     gdn_status st = check_dims(d, g);
-    if (st == GDN_OK && g.B != 1)
+    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
         st = GDN_ERR_SHAPE;
     if (st == GDN_OK)
         st = ptrs_ok({state, conv_tail, conv_w, parent, x, a, b, path});

@@ -19,7 +19,7 @@ hipError_t launch_token(const Geo& g, float* S, const void* tail_in, void* tail_
                         const float* a, const float* b, float* o, hipStream_t s);
 hipError_t launch_tree_tables(int n, const int32_t* parent, int32_t* depth, int32_t* order, int32_t* status,
                               hipStream_t s);
-size_t tree_ws_bytes(int n, int Hk, int Hv, int D);
+size_t tree_ws_bytes(int B, int n, int Hk, int Hv, int D);
 hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
                               const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                               int32_t* status, void* ws, hipStream_t s);

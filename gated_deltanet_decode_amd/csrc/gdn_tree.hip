@@ -69,6 +69,7 @@ struct alignas(16) NodeSmem {
     int32_t anc[MAXN][3];       // token index of the ancestor 1..3 steps up, -1 past the root
     int32_t order[MAXN];        // depth-first pre-order of the tokens (verify)
     int32_t ok;
+    int32_t len;                // tokens of the accepted path (commit)
 };
 
 // Conv outputs, normalised q/k, k.q and gates for tokens 0..count-1 (from
@@ -212,35 +213,46 @@ __device__ __forceinline__ void tok_load(TokOps<D>& t, const NodeSmem<D, ROWS, M
 
 // ------------------------------------------------------------ verify
 
-// Per-node operands of a tree, prepared once by tree_prep_kernel:
-//   qk  f32 [n][Hk][2*D]  q^ | k^ of each q/k head (normalised)
-//   kq  f32 [n][Hk]       k^.q^
-//   v   f32 [n][Hv][D]    conv output of each value head's v channels
-//   ab  f32 [n][Hv][2]    alpha, beta
+// Per-node operands of the batch's trees, prepared once by tree_prep_kernel
+// (node index m = sequence * n + node):
+//   qk   f32 [B*n][Hk][2*D]  q^ | k^ of each q/k head (normalised)
+//   v    f32 [B*n][Hv][D]    conv output of each value head's v channels
+//   abk  f32 [B*n][Hv][4]    alpha, beta, k^.q^ of the value head's q/k head, 0
+//   tab  i32 [B][2n+1]       per sequence: the node at each pre-order position,
+//                            the depth at each position, then 1 if the tree is
+//                            valid (0 otherwise)
 // abk holds (alpha, beta, k^.q^, 0) per (node, value head): the walk loads
 // it with a lane-dependent address, so it is a vector load counted with the
 // other vector loads rather than a scalar load sharing the LDS counter.
 struct TreeWs {
     float *qk, *v, *abk;
+    int32_t* tab;
 };
 
-size_t tree_ws_bytes(int n, int Hk, int Hv, int D) {
-    return static_cast<size_t>(n) * (2ull * Hk * D + static_cast<size_t>(Hv) * D + 4ull * Hv) * 4 + 3 * 256;
+size_t tree_ws_bytes(int B, int n, int Hk, int Hv, int D) {
+    const size_t m = static_cast<size_t>(B) * n;
+    return m * (2ull * Hk * D + static_cast<size_t>(Hv) * D + 4ull * Hv) * 4 +
+           static_cast<size_t>(B) * (2 * n + 1) * 4 + 4 * 256;
 }
 
-static TreeWs tree_ws_carve(void* base, int n, int Hk, int Hv, int D) {
+static TreeWs tree_ws_carve(void* base, int B, int n, int Hk, int Hv, int D) {
     auto align = [](uintptr_t p) { return (p + 255) & ~static_cast<uintptr_t>(255); };
     uintptr_t p = align(reinterpret_cast<uintptr_t>(base));
+    const size_t m = static_cast<size_t>(B) * n;
     TreeWs w;
-    auto take = [&](size_t cnt) { float* r = reinterpret_cast<float*>(p); p = align(p + cnt * 4); return r; };
-    w.qk = take(static_cast<size_t>(n) * Hk * 2 * D);
-    w.v = take(static_cast<size_t>(n) * Hv * D);
-    w.abk = take(static_cast<size_t>(n) * Hv * 4);
+    auto take = [&](size_t cnt) { void* r = reinterpret_cast<void*>(p); p = align(p + cnt * 4); return r; };
+    w.qk = static_cast<float*>(take(m * Hk * 2 * D));
+    w.v = static_cast<float*>(take(m * Hv * D));
+    w.abk = static_cast<float*>(take(m * Hv * 4));
+    w.tab = static_cast<int32_t*>(take(static_cast<size_t>(B) * (2 * n + 1)));
     return w;
 }
 
-// One workgroup per (node, q/k head): the node's conv window over its q/k
-// head's channels and its value heads' channels, the q/k norm and the gates.
+// Workgroups 0 .. B-1 build each sequence's tree tables (validity, pre-order,
+// depths) once for every workgroup of the verify kernel, and report the
+// sequence's status.  The others, one per (sequence, q/k head, node): the
+// node's conv window over its q/k head's channels and its value heads'
+// channels, the q/k norm and the gates.
 // The ancestor chain is followed at most three links and every link is
 // checked, so a malformed parent array stays in bounds (the verify kernel
 // reports it and writes nothing).
@@ -248,13 +260,44 @@ template <int D, typename Act>
 __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
                                                         int n, const int32_t* __restrict__ parent,
                                                         const Act* __restrict__ x, const float* __restrict__ a,
-                                                        const float* __restrict__ b, TreeWs ws, int Hk, int Hv,
-                                                        int C) {
+                                                        const float* __restrict__ b, TreeWs ws,
+                                                        int32_t* __restrict__ status, int B, int Hk, int Hv, int C) {
     __shared__ float yqk[2 * D];
     __shared__ int32_t anc_s[4];
-    const int i = blockIdx.x % n;
-    const int g = blockIdx.x / n;
+    __shared__ int32_t depth_s[kMaxNodes], order_s[kMaxNodes];
+    if (static_cast<int>(blockIdx.x) < B) {
+        const int bq = blockIdx.x;
+        bool ok = false;
+        if (threadIdx.x < kWave)
+            ok = tree_tables_wave(n, parent + static_cast<size_t>(bq) * n, depth_s, order_s);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const int lane = threadIdx.x;
+            int32_t* tab = ws.tab + static_cast<size_t>(bq) * (2 * n + 1);
+            if (ok && lane < n) {
+                const int node = order_s[lane];
+                tab[lane] = node;
+                tab[n + lane] = depth_s[node];
+            }
+            if (lane == 0) {
+                tab[2 * n] = ok ? 1 : 0;
+                if (status)
+                    status[bq] = ok ? 0 : 5;
+            }
+        }
+        return;
+    }
+    const int wg = blockIdx.x - B;
+    const int i = wg % n;
+    const int g = (wg / n) % Hk;
+    const int bq = wg / (n * Hk);
     const int G = Hv / Hk;
+    const int m0 = bq * n;   // workspace index of the sequence's node 0
+    parent += m0;
+    x += static_cast<size_t>(m0) * C;
+    a += static_cast<size_t>(m0) * Hv;
+    b += static_cast<size_t>(m0) * Hv;
+    tail += static_cast<size_t>(bq) * C * 4;
     const int lane = threadIdx.x & (kWave - 1);
     if (threadIdx.x < kWave) {
         const int p = lane < n ? parent[lane] : -1;
@@ -288,15 +331,15 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
         if (ch < 2 * D)
             yqk[ch] = yv;
         else
-            ws.v[(static_cast<size_t>(i) * Hv + G * g) * D + (ch - 2 * D)] = yv;
+            ws.v[(static_cast<size_t>(m0 + i) * Hv + G * g) * D + (ch - 2 * D)] = yv;
     }
     if (threadIdx.x < G) {
         const int h = G * g + threadIdx.x;
         float al, be;
         gates(a[static_cast<size_t>(i) * Hv + h], b[static_cast<size_t>(i) * Hv + h], al, be);
-        ws.abk[(static_cast<size_t>(i) * Hv + h) * 4] = al;
-        ws.abk[(static_cast<size_t>(i) * Hv + h) * 4 + 1] = be;
-        ws.abk[(static_cast<size_t>(i) * Hv + h) * 4 + 3] = 0.0f;
+        ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4] = al;
+        ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4 + 1] = be;
+        ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4 + 3] = 0.0f;
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -310,7 +353,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
         }
         float kq;
         prep_qk<D>(qv, kv, kq);
-        float* dst = ws.qk + (static_cast<size_t>(i) * Hk + g) * 2 * D;
+        float* dst = ws.qk + (static_cast<size_t>(m0 + i) * Hk + g) * 2 * D;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int e = lane + kWave * j;
@@ -320,7 +363,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
             }
         }
         if (lane < G)
-            ws.abk[(static_cast<size_t>(i) * Hv + G * g + lane) * 4 + 2] = kq;
+            ws.abk[(static_cast<size_t>(m0 + i) * Hv + G * g + lane) * 4 + 2] = kq;
     }
 }
 
@@ -332,9 +375,6 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
 template <int D>
 struct alignas(16) VerifySmem {
     float4 stack[kMaxDepth - 1][Row<D>::NV][256];
-    int32_t depth[kMaxNodes];
-    int32_t order[kMaxNodes];
-    int32_t ok;
 };
 
 constexpr int kRing = 6;   // walk steps of operand prefetch
@@ -351,58 +391,59 @@ struct NodeOps {
     float v, abk;   // abk: lane l holds element l % 4 of (alpha, beta, k^.q^, 0)
 };
 
-// Value of lane 4 (l / 4) + E in lane l: broadcasts one element of abk.
+// Value of lane 4 (l / 4) + E in lane l: broadcasts one element of abk.  Every
+// lane is written, so the move needs no initial value.
 template <int E>
 __device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), E * 0x55, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), E * 0x55, 0xF, 0xF, true));
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, int n,
-                                                          const int32_t* __restrict__ parent, TreeWs ws,
-                                                          float* __restrict__ o, int32_t* __restrict__ status,
-                                                          int Hk, int Hv, int blocks_per_head) {
+__global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, int n, TreeWs ws,
+                                                          float* __restrict__ o, int Hk, int Hv,
+                                                          int blocks_per_head) {
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
     constexpr int ROWS = 4 * RPW;
     __shared__ VerifySmem<D> sm;
 
-    const int blk = blockIdx.x % blocks_per_head;
-    const int h = blockIdx.x / blocks_per_head;
+    // Workgroups of one (sequence, q/k head) share their node operands; they
+    // are kept on one XCD.
+    const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
+    const int blk = wid % blocks_per_head;
+    const int h = (wid / blocks_per_head) % Hv;
+    const int bq = wid / (blocks_per_head * Hv);
     const int grp = h / (Hv / Hk);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int r = lane % LPR;
     const int row = blk * ROWS + wave * RPW + lane / LPR;
     const int tid = threadIdx.x;
+    const int m0 = bq * n;   // workspace index of the sequence's node 0
 
-    const float* Sh = Sc + static_cast<size_t>(h) * D * D;
+    const float* Sh = Sc + (static_cast<size_t>(bq) * Hv + h) * D * D;
     float4 base[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         base[j] = load_stream(Sh + row * D + R::key(j, r));
 
-    if (wave == 0) {
-        const bool ok = tree_tables_wave(n, parent, sm.depth, sm.order);
-        if (lane == 0) {
-            sm.ok = ok ? 1 : 0;
-            if (status && blockIdx.x == 0)
-                *status = ok ? 0 : 5;
-        }
-    }
-    __syncthreads();
-    if (!sm.ok)
+    // The sequence's tables, built by the prep launch.  Lane l holds the l-th
+    // node of the pre-order walk and its depth; the loop reads them with
+    // readlane.  Nothing is written for a malformed tree.
+    const int32_t* tab = ws.tab + static_cast<size_t>(bq) * (2 * n + 1);
+    const int ok = tab[2 * n];
+    int ord_l = lane < n ? tab[lane] : 0;
+    ord_l = ord_l < 0 ? 0 : ord_l >= n ? n - 1 : ord_l;
+    const int dep_l = lane < n ? tab[n + lane] : 1;
+    if (!ok)
         return;
 
-    // Lane l holds the l-th node of the pre-order walk and its depth; the loop
-    // reads them with readlane.  Node operands come from the prepared
-    // workspace through a ring of kRing register slots, unrolled so that each
-    // slot keeps its registers: a slot is refilled with the node kRing steps
-    // ahead as soon as its node is done, which hides the cross-XCD fetch.
-    const int ord_l = lane < n ? sm.order[lane] : 0;
-    const int dep_l = lane < n ? sm.depth[ord_l] : 1;
+    // Node operands come from the prepared workspace through a ring of kRing
+    // register slots, unrolled so that each slot keeps its registers: a slot
+    // is refilled with the node kRing steps ahead as soon as its node is done,
+    // which hides the cross-XCD fetch.
     auto load_node = [&](NodeOps<D>& t, int it) {
-        const int i = __builtin_amdgcn_readlane(ord_l, it < n ? it : n - 1);
+        const int i = m0 + __builtin_amdgcn_readlane(ord_l, it < n ? it : n - 1);
         const float* qk = ws.qk + (static_cast<size_t>(i) * Hk + grp) * 2 * D;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -428,7 +469,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
         if (it >= n)
             return false;
         const int d = __builtin_amdgcn_readlane(dep_l, it);
-        if (d == 1) {
+        // A valid tree's pre-order starts at the root, the only node of depth
+        // 1, so only the first step starts from the checkpoint rows.
+        if constexpr (it == 0) {
 #pragma unroll
             for (int j = 0; j < NV; ++j)
                 s[j] = base[j];
@@ -452,7 +495,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
     walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
     // Every lane of a row holds the same sum (the butterfly adds commuted
     // pairs), so all of them store it: no exec branch.
-    float* oh = o + static_cast<size_t>(h) * D + row;
+    float* oh = o + (static_cast<size_t>(m0) * Hv + h) * D + row;
 #pragma unroll
     for (int it = 0; it < kMaxNodes; ++it)
         if (it < n)
@@ -479,21 +522,21 @@ static hipError_t dispatch(const Geo& g, F&& f) {
 hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
                               const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                               int32_t* status, void* ws, hipStream_t s) {
-    const TreeWs W = tree_ws_carve(ws, n, g.Hk, g.Hv, g.D);
+    const TreeWs W = tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D);
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
-        hipLaunchKernelGGL((tree_prep_kernel<D, Act>), dim3(static_cast<unsigned>(n * g.Hk)), dim3(256), 0, s,
-                           static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                           static_cast<const Act*>(x), a, b, W, g.Hk, g.Hv, g.C);
+        hipLaunchKernelGGL((tree_prep_kernel<D, Act>), dim3(static_cast<unsigned>(g.B + g.B * n * g.Hk)), dim3(256),
+                           0, s, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                           static_cast<const Act*>(x), a, b, W, status, g.B, g.Hk, g.Hv, g.C);
     });
     if (e != hipSuccess)
         return e;
     return dispatch(g, [&](auto dtag, auto) {
         constexpr int D = decltype(dtag)::value;
         const int bph = D / (4 * Row<D>::RPW);
-        hipLaunchKernelGGL((tree_verify_kernel<D>), dim3(static_cast<unsigned>(g.Hv * bph)), dim3(256), 0, s, S, n,
-                           parent, W, o, status, g.Hk, g.Hv, bph);
+        hipLaunchKernelGGL((tree_verify_kernel<D>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)), dim3(256), 0, s, S, n,
+                           W, o, g.Hk, g.Hv, bph);
     });
 }
 
@@ -513,8 +556,12 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     constexpr int ROWS = 4 * RPW;
     __shared__ NodeSmem<D, ROWS, kMaxDepth, Act> sm;
 
-    const int blk = blockIdx.x % blocks_per_head;
-    const int h = blockIdx.x / blocks_per_head;
+    // Workgroups of one (sequence, q/k head) share their token inputs; they
+    // are kept on one XCD.
+    const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
+    const int blk = wid % blocks_per_head;
+    const int h = (wid / blocks_per_head) % Hv;
+    const int bq = wid / (blocks_per_head * Hv);
     const int grp = h / (Hv / Hk);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -522,50 +569,64 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     const int row0 = blk * ROWS;
     const int lrow = wave * RPW + lane / LPR;
     const int row = row0 + lrow;
+    parent += static_cast<size_t>(bq) * n;
+    path += static_cast<size_t>(bq) * L;
+    x += static_cast<size_t>(bq) * n * C;
+    a += static_cast<size_t>(bq) * n * Hv;
+    b += static_cast<size_t>(bq) * n * Hv;
+    tail += static_cast<size_t>(bq) * C * 4;
 
-    float* Sh = S + static_cast<size_t>(h) * D * D;
+    float* Sh = S + (static_cast<size_t>(bq) * Hv + h) * D * D;
     float4 s[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         s[j] = load_stream(Sh + row * D + R::key(j, r));
 
     // Token i of the commit is path position i; its ancestors are the
-    // positions before it.  Node ids are clamped into the tree so that every
-    // load below stays in bounds whatever the path holds; a malformed path is
-    // rejected before anything is written.
-    if (threadIdx.x < kMaxDepth) {
-        const int i = threadIdx.x < L ? threadIdx.x : L - 1;
-        int nd = path[i];
-        nd = nd < 0 ? 0 : nd >= n ? n - 1 : nd;
-        sm.node[threadIdx.x] = nd;
-        sm.depth[threadIdx.x] = threadIdx.x + 1;
+    // positions before it.  The row's length is the index of its first -1.
+    // Node ids are clamped into the tree so that every load below stays in
+    // bounds whatever the path holds; a malformed path is rejected before
+    // anything is written.
+    if (wave == 0) {
+        const int len = path_len_wave(L, path);
+        if (lane < kMaxDepth) {
+            int nd = path[lane < L ? lane : L - 1];
+            nd = nd < 0 ? 0 : nd >= n ? n - 1 : nd;
+            sm.node[lane] = nd;
+            sm.depth[lane] = lane + 1;
 #pragma unroll
-        for (int k = 1; k <= 3; ++k)
-            sm.anc[threadIdx.x][k - 1] = threadIdx.x - k;
+            for (int k = 1; k <= 3; ++k)
+                sm.anc[lane][k - 1] = lane - k;
+        }
+        if (lane == 0)
+            sm.len = len;
     }
     __syncthreads();
+    const int len = sm.len;
+    const int cnt = len > 0 ? len : 1;   // tokens loaded and convolved (in bounds for the empty path)
     FillRegs<D, ROWS, kMaxDepth, Act> fr;
-    fill_issue<D, ROWS, kMaxDepth, Act>(fr, sm, L, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
+    fill_issue<D, ROWS, kMaxDepth, Act>(fr, sm, cnt, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
     if (wave == 0) {   // validation overlaps the loads just issued
         bool ok = tree_tables_wave(n, parent, nullptr, nullptr);
         ok = ok && path_check_wave(n, parent, L, path);
         if (lane == 0) {
             sm.ok = ok ? 1 : 0;
-            if (status && blockIdx.x == 0)
-                *status = ok ? 0 : 5;
+            if (status && wid % (blocks_per_head * Hv) == 0)
+                status[bq] = ok ? 0 : 5;
         }
     }
-    fill_finish<D, ROWS, kMaxDepth, Act>(fr, sm, L);
-    if (!sm.ok)
+    fill_finish<D, ROWS, kMaxDepth, Act>(fr, sm, cnt);
+    if (!sm.ok || len == 0)
         return;
 
+    float* ob = o ? o + static_cast<size_t>(bq) * L * Hv * D : nullptr;
     TokOps<D> cur, nxt;
     tok_load(cur, sm, 0, r, lrow);
-    for (int i = 0; i < L; ++i) {
-        tok_load(nxt, sm, i + 1 < L ? i + 1 : i, r, lrow);
+    for (int i = 0; i < len; ++i) {
+        tok_load(nxt, sm, i + 1 < len ? i + 1 : i, r, lrow);
         const float out = row_update<D>(s, cur.k, cur.q, cur.alpha, cur.beta, cur.v, cur.kq);
-        if (o && r == 0)
-            o[(static_cast<size_t>(i) * Hv + h) * D + row] = out;
+        if (ob && r == 0)
+            ob[(static_cast<size_t>(i) * Hv + h) * D + row] = out;
         cur = nxt;
     }
 #pragma unroll
@@ -581,7 +642,12 @@ __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail
                                                           const int32_t* __restrict__ parent,
                                                           const Act* __restrict__ x, int L,
                                                           const int32_t* __restrict__ path, int C) {
-    __shared__ int32_t ok_s;
+    __shared__ int32_t ok_s, len_s;
+    const int bq = blockIdx.y;   // sequence
+    parent += static_cast<size_t>(bq) * n;
+    path += static_cast<size_t>(bq) * L;
+    x += static_cast<size_t>(bq) * n * C;
+    tail += static_cast<size_t>(bq) * C * 4;
     const int c0 = blockIdx.x * blockDim.x + threadIdx.x;
     const int c = c0 < C ? c0 : C - 1;
     using Q = Quad<Act>;
@@ -596,15 +662,19 @@ __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail
     if (threadIdx.x < kWave) {
         bool ok = tree_tables_wave(n, parent, nullptr, nullptr);
         ok = ok && path_check_wave(n, parent, L, path);
-        if (threadIdx.x == 0)
+        const int len = path_len_wave(L, path);
+        if (threadIdx.x == 0) {
             ok_s = ok ? 1 : 0;
+            len_s = len;
+        }
     }
     __syncthreads();
-    if (!ok_s || c0 >= C)
+    const int len = len_s;
+    if (!ok_s || len == 0 || c0 >= C)
         return;
 #pragma unroll
     for (int j = 0; j < kMaxDepth; ++j)
-        if (j < L)
+        if (j < len)
             t = Q::push(t, xin[j]);
     Q::store(tail + static_cast<size_t>(c) * 4, t);
 }
@@ -616,13 +686,13 @@ hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int 
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
         const int bph = D / (4 * Row<D>::RPW);
-        hipLaunchKernelGGL((commit_state_kernel<D, Act>), dim3(static_cast<unsigned>(g.Hv * bph)), dim3(256), 0,
+        hipLaunchKernelGGL((commit_state_kernel<D, Act>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)), dim3(256), 0,
                            s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
                            static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph);
     });
     if (e != hipSuccess)
         return e;
-    const dim3 grid(static_cast<unsigned>((g.C + 255) / 256)), block(256);
+    const dim3 grid(static_cast<unsigned>((g.C + 255) / 256), static_cast<unsigned>(g.B)), block(256);
     if (g.bf16)
         hipLaunchKernelGGL(commit_tail_kernel<uint16_t>, grid, block, 0, s, static_cast<uint16_t*>(tail), n, parent,
                            static_cast<const uint16_t*>(x), L, path, g.C);

@@ -59,19 +59,43 @@ __device__ inline bool tree_tables_wave(int n, const int32_t* __restrict__ paren
     return true;
 }
 
-// Checks an accepted path: path[0] == 0 and parent[path[j]] == path[j-1].
+// An accepted-path row of up to L entries holds the path root first, then -1
+// in every entry after its end, so sequences of one batch can accept paths of
+// different lengths.  Its length is the index of its first -1 (L if none).
+// Must run on one whole wave; the result is wave-uniform.
+__device__ inline int path_len_wave(int L, const int32_t* __restrict__ path) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t ends = __ballot(lane < L && path[lane < L ? lane : 0] == -1);
+    return ends ? __builtin_ctzll(ends) : L;
+}
+
+// Checks an accepted-path row: path[0] == 0 and parent[path[j]] == path[j-1]
+// up to its end, and only -1 after it (a row of -1 only is the empty path).
 // Assumes the tree itself already passed tree_tables_wave.  One whole wave.
 __device__ inline bool path_check_wave(int n, const int32_t* __restrict__ parent, int L,
                                        const int32_t* __restrict__ path) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int len = path_len_wave(L, path);
     const int pj = (lane < L) ? path[lane] : 0;
     const bool in_range = pj >= 0 && pj < n;
-    const int par = (lane < L && in_range) ? parent[pj] : -1;
+    const int par = (lane < len && in_range) ? parent[pj] : -1;
     const int prev = __shfl(pj, lane > 0 ? lane - 1 : 0, kWave);
     bool bad = false;
-    if (lane < L)
+    if (lane < len)
         bad = !in_range || ((lane == 0) ? (pj != 0) : (par != prev));
+    else if (lane < L)
+        bad = pj != -1;
     return !__any(bad);
+}
+
+// Workgroup id in an order that keeps consecutive ids on one XCD: the
+// dispatcher deals workgroups to the 8 XCDs round robin, so XCD x receives
+// blocks x, x + 8, ...; they become one contiguous run of ids.  A bijection
+// on [0, nblocks) for any nblocks.
+__device__ __forceinline__ int xcd_packed_id(int bid, int nblocks) {
+    const int q = nblocks / 8, r = nblocks % 8;
+    const int x = bid % 8, k = bid / 8;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
 }
 
 // Raw inputs of the conv window that ends at a node of depth d (root = 1):

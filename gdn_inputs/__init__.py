@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "LayerShape", "TINY", "QWEN27B_LAYER", "normal_rows", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "random_tree", "random_leaf_path", "tree_depths",
-    "decode_inputs", "tree_inputs", "prefill_inputs", "Inputs",
+    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "Inputs",
 ]
 
 BF16 = "bf16"
@@ -209,6 +209,26 @@ def tree_inputs(seed: int, shape: LayerShape, n_nodes: int = 32, max_depth: int 
     parent = random_tree(rng, n_nodes, max_depth)
     path = random_leaf_path(rng, parent)
     return Inputs(shape, 1, n_nodes, x, a, b, w, state, tail,
+                  extra={"parent": parent, "path": path, "max_depth": max_depth})
+
+
+def tree_batch_inputs(seed: int, shape: LayerShape, batch: int, n_nodes: int = 32, max_depth: int = 8,
+                      state_sigma: float = 0.1, tail_random: bool = True) -> Inputs:
+    """One draft tree of n_nodes per sequence over `batch` checkpoints; x/a/b hold one row
+    per (node, sequence), [n_nodes][batch][...].  extra["parent"] is [batch][n_nodes] (an
+    independent tree per sequence); extra["path"] is [batch][max_depth]: per row a
+    root-first prefix of the path to a uniformly chosen leaf, of uniform length between 1
+    and that path's length, padded with -1."""
+    x, a, b, w, state, tail = _common(seed, shape, batch, n_nodes, state_sigma, tail_random)
+    parent = np.empty((batch, n_nodes), dtype=np.int32)
+    path = np.full((batch, max_depth), -1, dtype=np.int32)
+    for s in range(batch):
+        rng = _gen(seed, S_TREE, 1 + s)
+        parent[s] = random_tree(rng, n_nodes, max_depth)
+        full = random_leaf_path(rng, parent[s])
+        keep = 1 + int(rng.integers(len(full)))
+        path[s, :keep] = full[:keep]
+    return Inputs(shape, batch, n_nodes, x, a, b, w, state, tail,
                   extra={"parent": parent, "path": path, "max_depth": max_depth})
 
 

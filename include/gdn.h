@@ -54,6 +54,7 @@ extern "C" {
 #define GDN_ABI_VERSION 1
 #define GDN_MAX_TREE_NODES 32 /* draft trees of up to 32 nodes (decode-loop diagram) */
 #define GDN_MAX_TREE_DEPTH 8  /* nodes on a root-to-leaf path, root counted */
+#define GDN_MAX_TREE_BATCH 65535 /* sequences per tree verify or commit call */
 #define GDN_PREFILL_CHUNK 64
 
 typedef enum {
@@ -132,25 +133,32 @@ gdn_status gdn_decode_token(const gdn_dims* d, float* state, const void* conv_ta
 
 /*
  * gdn_tree_verify -- one read-only pass over a draft tree of n_nodes tokens
- * (decode-loop diagram: a tree of up to 32 nodes verified in one pass;
- * section 8.1: the state must be branched for a tree of guesses).  Node 0 is
- * the root, the last committed token, whose parent is the checkpoint; every
- * other node's state is branched from its parent's.  Node n's output equals,
- * bit for bit, the output of gdn_conv_update + gdn_decode_step run over the
- * root-first path to n from the checkpoint.  batch must be 1.
- *   state_ckpt f32 [Hv][dv][dk]    checkpoint (read only)
- *   conv_tail  act [C][4]          checkpoint tail (read only)
+ * per sequence (decode-loop diagram: a tree of up to 32 nodes verified in one
+ * pass; section 8.1: the state must be branched for a tree of guesses; the
+ * parallel server verifies several requests' trees in one forward pass).
+ * Each of the batch's sequences has a tree of its own.  Node 0 is the root,
+ * the last committed token, whose parent is the checkpoint; every other
+ * node's state is branched from its parent's.  Node n's output equals, bit
+ * for bit, the output of gdn_conv_update + gdn_decode_step run over the
+ * root-first path to n from the sequence's checkpoint.  1 <= batch <=
+ * GDN_MAX_TREE_BATCH; every tree has n_nodes nodes (a smaller tree can be
+ * padded with extra children of its root, whose outputs the caller ignores).
+ *   state_ckpt f32 [B][Hv][dv][dk]    checkpoints (read only)
+ *   conv_tail  act [B][C][4]          checkpoint tails (read only)
  *   conv_w     act [C][4]
  *   n_nodes    1..32
- *   parent     i32 [n_nodes]       parent[0] == -1, 0 <= parent[i] < i, depth <= 8
- *   x          act [n_nodes][C];  a, b f32 [n_nodes][Hv]
- *   o          f32 [n_nodes][Hv][dv]  (written)
- *   tree_status i32 [1] or NULL: set to GDN_OK, or GDN_ERR_TREE when parent[]
- *              is malformed (o is then undefined).
+ *   parent     i32 [B][n_nodes]   per row: parent[0] == -1, 0 <= parent[i] < i,
+ *              depth <= 8
+ *   x          act [B][n_nodes][C];  a, b f32 [B][n_nodes][Hv]
+ *   o          f32 [B][n_nodes][Hv][dv]  (written)
+ *   tree_status i32 [B] or NULL: per sequence, set to GDN_OK, or GDN_ERR_TREE
+ *              when its parent row is malformed (its o is then undefined;
+ *              the other sequences are verified as usual).
  *   workspace  device bytes >= gdn_tree_workspace_bytes(d, n_nodes), 16-byte
  *              aligned, caller-owned: each node's normalised q/k, v and gates
  *              are prepared there once and shared by every value head (about
- *              1.3 MB for 32 nodes at 16 q/k and 48 value heads of 128).
+ *              1.3 MB per sequence for 32 nodes at 16 q/k and 48 value heads
+ *              of 128).
  */
 size_t gdn_tree_workspace_bytes(const gdn_dims* d, int32_t n_nodes);
 gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
@@ -160,19 +168,25 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
                            void* stream);
 
 /*
- * gdn_commit_path -- commit the accepted root-first path of a verified tree
- * (decode-loop diagram: commit the accepted path's recurrent state; section
- * 8.1: exact undo).  The new (state, tail) is bit-identical to path_len calls
- * of gdn_conv_update + gdn_decode_step over the path's tokens.  Undo is not
- * calling this.  batch must be 1.
- *   state      f32 [Hv][dv][dk]  in: checkpoint, out: committed (in/out)
- *   conv_tail  act [C][4]        in/out
+ * gdn_commit_path -- commit the accepted root-first path of each sequence's
+ * verified tree (decode-loop diagram: commit the accepted path's recurrent
+ * state; section 8.1: exact undo).  A sequence's new (state, tail) is
+ * bit-identical to one gdn_conv_update + gdn_decode_step per token of its
+ * path.  Undo is not calling this, or, for one sequence of a batch, a path
+ * row of -1 only, which commits nothing.
+ *   state      f32 [B][Hv][dv][dk]  in: checkpoints, out: committed (in/out)
+ *   conv_tail  act [B][C][4]        in/out
  *   conv_w, n_nodes, parent, x, a, b: as for gdn_tree_verify
- *   path_len   1..min(n_nodes, 8);  path i32 [path_len]: path[0] == 0,
- *              parent[path[j]] == path[j-1]
- *   o          f32 [path_len][Hv][dv] or NULL: per-token outputs
- *   tree_status i32 [1] or NULL: GDN_OK, or GDN_ERR_TREE for a malformed
- *              tree or path, in which case state and tail are untouched.
+ *   path_len   1..min(n_nodes, 8): the width of a path row
+ *   path       i32 [B][path_len]: per row the accepted path, root first
+ *              (path[0] == 0, parent[path[j]] == path[j-1]), then -1 in every
+ *              entry after its end, so rows may have different lengths (and
+ *              length 0: -1 throughout).
+ *   o          f32 [B][path_len][Hv][dv] or NULL: per-token outputs (entries
+ *              past a row's end are not written)
+ *   tree_status i32 [B] or NULL: per sequence, GDN_OK, or GDN_ERR_TREE for a
+ *              malformed tree or path row, in which case that sequence's state
+ *              and tail are untouched.
  */
 gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w,
                            int32_t n_nodes, const int32_t* parent, const void* x,

@@ -103,9 +103,17 @@ def test_tree_sizes_are_refused_before_launch(lib):
     # n_nodes out of range
     for n in (0, 33):
         assert lib.gdn_tree_verify(C.byref(d), *args, n, fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == 5
-    # batch must be 1 for trees
+    # at most GDN_MAX_TREE_BATCH sequences per call
+    big = mk(batch=65536)
+    assert lib.gdn_tree_verify(C.byref(big), *args, 4, fake, fake, fake, fake, fake, None, fake, 1 << 40, None) == 2
+    assert lib.gdn_commit_path(C.byref(big), *args, 4, fake, fake, fake, fake, 1, fake, None, None, None) == 2
+    # the workspace holds every sequence's nodes: one sized for a single tree is short for two
+    lib.gdn_tree_workspace_bytes.restype = C.c_size_t
+    lib.gdn_tree_workspace_bytes.argtypes = [C.POINTER(Dims), C.c_int32]
     d2 = mk(batch=2)
-    assert lib.gdn_tree_verify(C.byref(d2), *args, 4, fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == 2
+    one, two = lib.gdn_tree_workspace_bytes(C.byref(d), 4), lib.gdn_tree_workspace_bytes(C.byref(d2), 4)
+    assert two > one > 0
+    assert lib.gdn_tree_verify(C.byref(d2), *args, 4, fake, fake, fake, fake, fake, None, fake, one, None) == 6
     # a missing or short workspace is refused before launch
     assert lib.gdn_tree_verify(C.byref(d), *args, 4, fake, fake, fake, fake, fake, None, None, 0, None) == 6
     assert lib.gdn_tree_verify(C.byref(d), *args, 4, fake, fake, fake, fake, fake, None, fake, 1024, None) == 6

@@ -92,6 +92,27 @@ def test_bf16_widening_exhaustive(oracle_lib):
     assert np.array_equal(got[~nan].view(np.uint64), ref[~nan].view(np.uint64))
 
 
+def test_batched_tree_draws_are_valid():
+    """Every sequence of a batched draw has its own valid tree (parents earlier, depth at
+    most 8, checked by the oracle's tree tables), and each path row is a root-first chain
+    of that tree followed by -1 only; the draw mixes path lengths."""
+    inp = gi.tree_batch_inputs(11, gi.TINY, 16, n_nodes=32, max_depth=8)
+    parent, path = inp.extra["parent"], inp.extra["path"]
+    assert parent.shape == (16, 32) and path.shape == (16, 8)
+    assert inp.x.shape == (32, 16, gi.TINY.conv_channels)
+    lens = []
+    for s in range(16):
+        st, depth, _ = oracle.tree_tables(parent[s], 8)
+        assert st == 0 and depth.max() <= 8
+        row = path[s]
+        L = int(np.argmax(row == -1)) if (row == -1).any() else len(row)
+        assert L >= 1 and (row[L:] == -1).all() and row[0] == 0
+        assert all(parent[s][row[j]] == row[j - 1] for j in range(1, L))
+        lens.append(L)
+    assert len(set(lens)) > 2
+    assert len({tuple(p) for p in parent}) == 16
+
+
 def test_input_bf16_rounding_ties_and_sample():
     """The generator's fp32 -> bf16 rounding against an independent round-half-even
     written with integer division, on edge patterns and a large random sample."""
