@@ -367,23 +367,15 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
     }
 }
 
-// The branched rows live in LDS, one slot per tree level below the deepest:
-// slot L holds, for every lane, its slice of the row after the most recent
-// node of depth L + 1 on the walk.  A node whose parent is the previous node
-// of the walk takes the rows still in registers; any other node reloads its
-// parent's slot (or the checkpoint rows, for a child of the root).
-template <int D>
+// The branched rows are kept per tree level below the deepest: the slot of
+// depth L holds, for every lane, its slice of the row after the most recent
+// node of depth L on the walk.  A node whose parent is the previous node of
+// the walk takes the rows still in registers; any other node reloads its
+// parent's slot.
+template <int D, int LEVELS>
 struct alignas(16) VerifySmem {
-    float4 stack[kMaxDepth - 1][Row<D>::NV][256];
+    float4 stack[LEVELS][Row<D>::NV][256];
 };
-
-constexpr int kRing = 6;   // walk steps of operand prefetch
-
-// Calls f(integral_constant<I>) for I = 0, 1, ... until one returns false.
-template <typename F, int... I>
-__device__ __forceinline__ void walk_all(F& f, std::integer_sequence<int, I...>) {
-    (void)(f(std::integral_constant<int, I>{}) && ...);
-}
 
 template <int D>
 struct NodeOps {
@@ -398,51 +390,41 @@ __device__ __forceinline__ float quad_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), E * 0x55, 0xF, 0xF, true));
 }
 
+// What a verify workgroup knows about itself: its rows, its sequence's tables
+// (built by the prep launch; lane l holds the node at pre-order position l and
+// its depth), and where its node operands and outputs are.
 template <int D>
-__global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restrict__ Sc, int n, TreeWs ws,
-                                                          float* __restrict__ o, int Hk, int Hv,
-                                                          int blocks_per_head) {
+struct VerifyCtx {
     using R = Row<D>;
-    constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
-    constexpr int ROWS = 4 * RPW;
-    __shared__ VerifySmem<D> sm;
+    static constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW, ROWS = 4 * RPW;
+    int h, grp, lane, r, row, m0, n, Hk, Hv, ord_l, dep_l, ok;
+    const float* Sh;
+    float* oh;   // o of this lane's row at node 0 of the sequence
+    TreeWs ws;
 
-    // Workgroups of one (sequence, q/k head) share their node operands; they
-    // are kept on one XCD.
-    const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
-    const int blk = wid % blocks_per_head;
-    const int h = (wid / blocks_per_head) % Hv;
-    const int bq = wid / (blocks_per_head * Hv);
-    const int grp = h / (Hv / Hk);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int r = lane % LPR;
-    const int row = blk * ROWS + wave * RPW + lane / LPR;
-    const int tid = threadIdx.x;
-    const int m0 = bq * n;   // workspace index of the sequence's node 0
-
-    const float* Sh = Sc + (static_cast<size_t>(bq) * Hv + h) * D * D;
-    float4 base[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        base[j] = load_stream(Sh + row * D + R::key(j, r));
-
-    // The sequence's tables, built by the prep launch.  Lane l holds the l-th
-    // node of the pre-order walk and its depth; the loop reads them with
-    // readlane.  Nothing is written for a malformed tree.
-    const int32_t* tab = ws.tab + static_cast<size_t>(bq) * (2 * n + 1);
-    const int ok = tab[2 * n];
-    int ord_l = lane < n ? tab[lane] : 0;
-    ord_l = ord_l < 0 ? 0 : ord_l >= n ? n - 1 : ord_l;
-    const int dep_l = lane < n ? tab[n + lane] : 1;
-    if (!ok)
-        return;
-
-    // Node operands come from the prepared workspace through a ring of kRing
-    // register slots, unrolled so that each slot keeps its registers: a slot
-    // is refilled with the node kRing steps ahead as soon as its node is done,
-    // which hides the cross-XCD fetch.
-    auto load_node = [&](NodeOps<D>& t, int it) {
+    __device__ VerifyCtx(const float* Sc, int n_, TreeWs ws_, float* o, int Hk_, int Hv_, int blocks_per_head)
+        : n(n_), Hk(Hk_), Hv(Hv_), ws(ws_) {
+        // Workgroups of one (sequence, q/k head) share their node operands;
+        // they are kept on one XCD.
+        const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
+        const int blk = wid % blocks_per_head;
+        h = (wid / blocks_per_head) % Hv;
+        const int bq = wid / (blocks_per_head * Hv);
+        grp = h / (Hv / Hk);
+        lane = threadIdx.x & (kWave - 1);
+        r = lane % LPR;
+        row = blk * ROWS + static_cast<int>(threadIdx.x / kWave) * RPW + lane / LPR;
+        m0 = bq * n;
+        Sh = Sc + (static_cast<size_t>(bq) * Hv + h) * D * D;
+        oh = o + (static_cast<size_t>(m0) * Hv + h) * D + row;
+        const int32_t* tab = ws.tab + static_cast<size_t>(bq) * (2 * n + 1);
+        ok = tab[2 * n];
+        ord_l = lane < n ? tab[lane] : 0;
+        ord_l = ord_l < 0 ? 0 : ord_l >= n ? n - 1 : ord_l;
+        dep_l = lane < n ? tab[n + lane] : 1;
+    }
+    // Operands of the node at pre-order position `it` (clamped into the tree).
+    __device__ __forceinline__ void load_node(NodeOps<D>& t, int it) const {
         const int i = m0 + __builtin_amdgcn_readlane(ord_l, it < n ? it : n - 1);
         const float* qk = ws.qk + (static_cast<size_t>(i) * Hk + grp) * 2 * D;
 #pragma unroll
@@ -452,23 +434,82 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
         }
         t.v = ws.v[(static_cast<size_t>(i) * Hv + h) * D + row];
         t.abk = ws.abk[(static_cast<size_t>(i) * Hv + h) * 4 + (lane & 3)];
-    };
-    NodeOps<D> ring[kRing];
+    }
+    // Every lane of a row holds the same sum (the butterfly adds commuted
+    // pairs), so all of them store it: no exec branch.
+    __device__ __forceinline__ void store_o(int it, float v) const {
+        oh[static_cast<size_t>(__builtin_amdgcn_readlane(ord_l, it)) * Hv * D] = v;
+    }
+};
+
+template <int D>
+__device__ __forceinline__ float node_update(float4 (&s)[Row<D>::NV], const NodeOps<D>& t) {
+    return row_update<D>(s, t.k, t.q, quad_bcast<0>(t.abk), quad_bcast<1>(t.abk), t.v, quad_bcast<2>(t.abk));
+}
+
+// Calls f(integral_constant<I>) for I = 0, 1, ... until one returns false.
+template <typename F, int... I>
+__device__ __forceinline__ void walk_all(F& f, std::integer_sequence<int, I...>) {
+    (void)(f(std::integral_constant<int, I>{}) && ...);
+}
+
+// Two forms of the walk.
+//
+// Alone on its CU (a batch of one tree) a workgroup needs a deep operand ring
+// to hide the fetch latency, and has the LDS for every saved level.  Outputs
+// are stored after the walk, so that the waits on the ring count no stores.
+//
+// With several trees per CU the walk is bound by VALU issue, and occupancy
+// hides the latency: four waves per SIMD (at most 128 VGPRs and 40 KB of LDS
+// per workgroup), a 3-slot ring, outputs stored as soon as they are computed.
+// Saved levels are kept for depths 1 .. 5 only; a node whose parent is deeper
+// and is not the previous node replays its ancestors below depth 5 from the
+// depth-5 row, with the same operands and arithmetic, so its row is the same
+// bits.  (In random 32-node trees of depth 8 about one node in sixty does.)
+struct WalkDeep {
+    static constexpr int ring = 6, levels = kMaxDepth - 1, waves = 1;
+    static constexpr bool defer_o = true;
+};
+struct WalkWide {
+    static constexpr int ring = 3, levels = kMaxDepth - 3, waves = 4;
+    static constexpr bool defer_o = false;
+};
+
+template <int D, typename Walk>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves))) void tree_verify_kernel(
+    const float* __restrict__ Sc, int n, TreeWs ws, float* __restrict__ o, int Hk, int Hv, int blocks_per_head) {
+    using R = Row<D>;
+    constexpr int NV = R::NV, RING = Walk::ring, LEVELS = Walk::levels;
+    __shared__ VerifySmem<D, LEVELS> sm;
+    const VerifyCtx<D> c(Sc, n, ws, o, Hk, Hv, blocks_per_head);
+    const int tid = threadIdx.x;
+    float4 base[NV];
 #pragma unroll
-    for (int p = 0; p < kRing; ++p)
-        load_node(ring[p], p);
+    for (int j = 0; j < NV; ++j)
+        base[j] = load_stream(c.Sh + c.row * D + R::key(j, c.r));
+    if (!c.ok)   // nothing is written for a malformed tree
+        return;
+
+    // Node operands stream through a ring of RING register slots, unrolled so
+    // that each slot keeps its registers: a slot is refilled with the node
+    // RING steps ahead as soon as its node is done, which hides the cross-XCD
+    // fetch.
+    NodeOps<D> ring[RING];
+#pragma unroll
+    for (int p = 0; p < RING; ++p)
+        c.load_node(ring[p], p);
     float4 s[NV];
-    float outv[kMaxNodes];   // o of each walk step, stored after the walk
+    float outv[Walk::defer_o ? kMaxNodes : 1];   // o of each walk step, stored after the walk
     int dprev = 0;
     // One walk step per node, expanded at compile time (at most kMaxNodes),
     // so that ring slots are static registers and every wait on a slot counts
     // exactly the loads issued after it.
     auto step = [&](auto itc) -> bool {
         constexpr int it = decltype(itc)::value;
-        constexpr int p = it % kRing;
+        constexpr int p = it % RING;
         if (it >= n)
             return false;
-        const int d = __builtin_amdgcn_readlane(dep_l, it);
+        const int d = __builtin_amdgcn_readlane(c.dep_l, it);
         // A valid tree's pre-order starts at the root, the only node of depth
         // 1, so only the first step starts from the checkpoint rows.
         if constexpr (it == 0) {
@@ -476,30 +517,46 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(const float* __restric
             for (int j = 0; j < NV; ++j)
                 s[j] = base[j];
         } else if (d != dprev + 1) {
+            if (LEVELS == kMaxDepth - 1 || d - 1 <= LEVELS) {
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
-                s[j] = sm.stack[d - 2][j][tid];
+                for (int j = 0; j < NV; ++j)
+                    s[j] = sm.stack[d - 2][j][tid];
+            } else {
+                // Replay the ancestors of depths LEVELS + 1 .. d - 1, each the
+                // latest position before this one with its depth.
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    s[j] = sm.stack[LEVELS - 1][j][tid];
+                for (int e = LEVELS + 1; e < d; ++e) {
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(c.dep_l == e) & ((1ull << it) - 1);
+                    NodeOps<D> anc;
+                    c.load_node(anc, 63 - __builtin_clzll(m));
+                    (void)node_update<D>(s, anc);
+                }
+            }
         }
-        const NodeOps<D>& t = ring[p];
-        outv[it] = row_update<D>(s, t.k, t.q, quad_bcast<0>(t.abk), quad_bcast<1>(t.abk), t.v, quad_bcast<2>(t.abk));
-        if (d < kMaxDepth) {
+        const float out = node_update<D>(s, ring[p]);
+        if constexpr (Walk::defer_o)
+            outv[it] = out;
+        else
+            c.store_o(it, out);
+        if (d <= LEVELS) {
 #pragma unroll
             for (int j = 0; j < NV; ++j)
                 sm.stack[d - 1][j][tid] = s[j];
         }
         dprev = d;
-        if (it + kRing < kMaxNodes)
-            load_node(ring[p], it + kRing);
+        if (it + RING < kMaxNodes)
+            c.load_node(ring[p], it + RING);
         return true;
     };
     walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
-    // Every lane of a row holds the same sum (the butterfly adds commuted
-    // pairs), so all of them store it: no exec branch.
-    float* oh = o + (static_cast<size_t>(m0) * Hv + h) * D + row;
+    if constexpr (Walk::defer_o) {
 #pragma unroll
-    for (int it = 0; it < kMaxNodes; ++it)
-        if (it < n)
-            oh[static_cast<size_t>(__builtin_amdgcn_readlane(ord_l, it)) * Hv * D] = outv[it];
+        for (int it = 0; it < kMaxNodes; ++it)
+            if (it < n)
+                c.store_o(it, outv[it]);
+    }
 }
 
 // Runs f(D, Act) for the geometry's head width and activation type.
@@ -535,8 +592,14 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
     return dispatch(g, [&](auto dtag, auto) {
         constexpr int D = decltype(dtag)::value;
         const int bph = D / (4 * Row<D>::RPW);
-        hipLaunchKernelGGL((tree_verify_kernel<D>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)), dim3(256), 0, s, S, n,
-                           W, o, g.Hk, g.Hv, bph);
+        const unsigned grid = static_cast<unsigned>(g.B * g.Hv * bph);
+        // More workgroups than two per CU: the form for several trees per CU.
+        if (grid > 2u * 256u)
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide>), dim3(grid), dim3(256), 0, s, S, n, W, o, g.Hk,
+                               g.Hv, bph);
+        else
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep>), dim3(grid), dim3(256), 0, s, S, n, W, o, g.Hk,
+                               g.Hv, bph);
     });
 }
 

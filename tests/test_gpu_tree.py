@@ -228,3 +228,18 @@ def test_deep_chain_and_wide_star():
         for node in range(len(parent)):
             o_dec, _, _ = gpu_decode_path(c, gi.path_to(parent, node))
             assert torch.equal(o[node].view(torch.int32), o_dec[-1].view(torch.int32))
+
+
+def test_siblings_at_the_deepest_level():
+    """A depth-7 node with three children at depth 8, and siblings at every level above:
+    the later children restart from the deepest saved row."""
+    parent = np.array([-1, 0, 1, 2, 3, 4, 5, 6, 6, 6, 5, 10, 4, 1, 0], np.int32)
+    assert gi.tree_depths(parent).max() == 8
+    inp = gi.tree_inputs(61, QWEN27B_LAYER, n_nodes=len(parent), max_depth=8)
+    inp.extra["parent"] = parent
+    c = dev_case(inp)
+    o, st = gpu_verify(c, len(parent))
+    assert st == 0
+    for node in range(len(parent)):
+        o_dec, _, _ = gpu_decode_path(c, gi.path_to(parent, node))
+        assert torch.equal(o[node].view(torch.int32), o_dec[-1].view(torch.int32)), f"node {node}"

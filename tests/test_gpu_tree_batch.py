@@ -251,3 +251,37 @@ def test_batch64_full_size_sampled():
     og = o[s].cpu().numpy()
     for node in range(n):
         assert normwise(og[node, lo:hi], ref[node, lo:hi]) < TOL, f"node {node}"
+
+
+def test_siblings_at_the_deepest_level_batched():
+    """The three-wave form (more than two workgroups per CU) on trees whose depth-7 nodes
+    have several children, against batch-1 calls and token-by-token decode."""
+    inp = gi.tree_batch_inputs(85, QWEN27B_LAYER, 3, n_nodes=15, max_depth=8)
+    parent = inp.extra["parent"].copy()
+    parent[0] = [-1, 0, 1, 2, 3, 4, 5, 6, 6, 6, 5, 10, 4, 1, 0]
+    parent[2] = [-1, 0, 1, 2, 3, 4, 5, 6, 6, 0, 9, 10, 11, 12, 13]
+    o, st = verify(batch_case(inp, parent), 3, 15)
+    assert (st == 0).all()
+    for s in range(3):
+        c1 = one_case(inp, s, parent)
+        o1, _ = verify(c1, 1, 15)
+        assert same_bits(o[s], o1[0]), f"sequence {s}"
+        for node in range(15):
+            o_dec, _, _ = decode_path(c1, gi.path_to(parent[s], node))
+            assert same_bits(o[s, node], o_dec[-1]), f"sequence {s} node {node}"
+
+
+def test_narrow_heads_three_wave_form():
+    """Heads of width 32 at 130 sequences (more than two workgroups per CU): sampled
+    sequences against their batch-1 calls bit for bit, and one against the oracle."""
+    B, n = 130, 32
+    inp = gi.tree_batch_inputs(86, TINY, B, n_nodes=n, max_depth=8)
+    o, st = verify(batch_case(inp), B, n)
+    assert (st == 0).all()
+    for s in (0, 77, 129):
+        o1, _ = verify(one_case(inp, s), 1, n)
+        assert same_bits(o[s], o1[0]), f"sequence {s}"
+    s = 101
+    ref = oracle.tree_verify(inp.shape, inp.state[s], inp.tail[s], inp.w, inp.extra["parent"][s], inp.x[:, s],
+                             inp.a[:, s], inp.b[:, s])
+    assert normwise(o[s].cpu().numpy(), ref) < TOL
