@@ -17,8 +17,8 @@ weights, gates, o) over the time.
 Extra rows, each with its own roofline fraction: the same step under a hip
 graph and as two calls, the state step alone, batch-64 decode (ping-pong
 over two batches), 32-node tree verify and path commit at batch 1 and over
-64 sequences' trees, chunked prefill at T = 32,768; and the CPU oracle on a
-bounded sample as the host baseline.
+64 sequences' trees, snapshot and restore of 64 sequences, chunked prefill
+at T = 32,768; and the CPU oracle on a bounded sample as the host baseline.
 Inputs are seeded synthetic tensors of the workload's shapes.
 """
 from __future__ import annotations
@@ -139,7 +139,7 @@ def main():
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--buffers", type=int, default=160, help="independent states rotated through (cold runs)")
-    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,tree64,prefill,hot,cpu or all/none")
+    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,tree64,snapshot,prefill,hot,cpu or all/none")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 512 MiB device copy (for byte counters)")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
     args = ap.parse_args()
@@ -154,7 +154,8 @@ def main():
     import gated_deltanet_decode_amd as gdn
     import gdn_inputs as gi
 
-    rows = set(["graph", "kernel", "b64", "tree", "commit", "tree64", "prefill", "hot", "cpu"]) if args.rows == "all" else \
+    rows = set(["graph", "kernel", "b64", "tree", "commit", "tree64", "snapshot", "prefill", "hot", "cpu"]) \
+        if args.rows == "all" else \
         set() if args.rows == "none" else set(args.rows.split(","))
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -359,6 +360,32 @@ def main():
                                   "committed_tokens_per_s": sum(lens) / (us + res["tree_verify_b64_n32"]["us"]) * 1e6}
         assert int(stB.abs().sum().item()) == 0
         del S2, T2, xB, aB, bB, oB, wsB
+
+    # ---------------------------------------------------------------- snapshot / restore, 64 sequences
+    # Save all 64 sequences of one batch into a blob and restore them into the
+    # other batch; the two batches and the blob (1.2 GB) exceed the cache.
+    if "snapshot" in rows:
+        B = 64
+        pool = gi.decode_inputs(106, shape, 2 * B, 1, state_sigma=0.1, tail_random=True)
+        S2 = f32(pool.state).view(2, B, Hv, D, D)
+        T2 = act(pool.tail).view(2, B, C, 4)
+        del pool
+        dB = gdn.dims(B, 16, 48, 128, 128, 4, "bf16")
+        seqs = torch.arange(B, dtype=torch.int32, device=dev)
+        blobs = [torch.empty(gdn.snapshot_bytes(dB, B), dtype=torch.uint8, device=dev) for _ in range(2)]
+        stS = torch.zeros(1, dtype=torch.int32, device=dev)
+        per_seq = Hv * D * D * 4 + C * 4 * 2
+        moved = 2 * B * per_seq                           # each byte read once and written once
+        us_s = graph_time_us(torch, lambda r: gdn.snapshot(dB, S2[r % 2], T2[r % 2], seqs, blobs[r % 2], stS), 16,
+                             reps=2)
+        us_r = graph_time_us(torch, lambda r: gdn.restore(dB, S2[1 - r % 2], T2[1 - r % 2], seqs, blobs[r % 2], stS),
+                             16, reps=2)
+        assert stS.item() == 0
+        res["snapshot_b64"] = {"us": us_s, "GBps": moved / us_s / 1e3, "frac_hbm": moved / us_s / 1e3 / HBM_PEAK_GBS,
+                               "bytes": moved, "launch": "hipGraph"}
+        res["restore_b64"] = {"us": us_r, "GBps": moved / us_r / 1e3, "frac_hbm": moved / us_r / 1e3 / HBM_PEAK_GBS,
+                              "bytes": moved, "launch": "hipGraph"}
+        del S2, T2, blobs
 
     # ---------------------------------------------------------------- chunked prefill
     if "prefill" in rows:

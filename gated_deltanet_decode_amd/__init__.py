@@ -72,6 +72,10 @@ _sig = {
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
     "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
     "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "gdn_state_signature": ([_D], C.c_uint64),
+    "gdn_snapshot_bytes": ([_D, _I], C.c_size_t),
+    "gdn_snapshot": ([_D, _P, _P, _I, _P, _P, C.c_size_t, _P, _P], C.c_int),
+    "gdn_restore": ([_D, _P, _P, _I, _P, _P, C.c_size_t, _P, _P], C.c_int),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -203,6 +207,44 @@ def tree_tables(parent, depth, order, status, stream=None) -> None:
     _check(_lib.gdn_tree_tables(n, _t(parent, "parent", torch.int32, n), _t(depth, "depth", torch.int32, n),
                                 _t(order, "order", torch.int32, n), _t(status, "tree_status", torch.int32, 1),
                                 _stream(stream)), "gdn_tree_tables")
+
+
+def state_signature(d: Dims) -> int:
+    return _lib.gdn_state_signature(C.byref(d))
+
+
+def snapshot_bytes(d: Dims, count: int) -> int:
+    return _lib.gdn_snapshot_bytes(C.byref(d), count)
+
+
+def _blob(blob, need, name):
+    if not isinstance(blob, torch.Tensor) or blob.device.type != "cuda" or not blob.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    nbytes = blob.numel() * blob.element_size()
+    if nbytes < need:
+        raise ValueError(f"{name} of {nbytes} bytes, need {need}")
+    return blob.data_ptr(), nbytes
+
+
+def snapshot(d: Dims, state, tail, seqs, blob, status, stream=None) -> None:
+    """Copy sequences seqs [count] (int32, device) of (state, tail) into blob (device bytes of at
+    least snapshot_bytes(d, count)); status [1] int32 (device) receives the outcome."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    n = seqs.numel()
+    ptr, nbytes = _blob(blob, snapshot_bytes(d, n), "blob")
+    _check(_lib.gdn_snapshot(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                             _t(tail, "conv_tail", d.act_torch, B * Cc * 4), n, _t(seqs, "seqs", torch.int32, n),
+                             ptr, nbytes, _t(status, "status", torch.int32, 1), _stream(stream)), "gdn_snapshot")
+
+
+def restore(d: Dims, state, tail, seqs, blob, status, stream=None) -> None:
+    """Copy blob slots 0..count-1 into sequences seqs [count] (distinct) of (state, tail)."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    n = seqs.numel()
+    ptr, nbytes = _blob(blob, snapshot_bytes(d, n), "blob")
+    _check(_lib.gdn_restore(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                            _t(tail, "conv_tail", d.act_torch, B * Cc * 4), n, _t(seqs, "seqs", torch.int32, n),
+                            ptr, nbytes, _t(status, "status", torch.int32, 1), _stream(stream)), "gdn_restore")
 
 
 def prefill_chunked(d: Dims, state, tail, w, x, a, b, o, workspace=None, stream=None) -> None:

@@ -69,6 +69,8 @@ const char* gdn_status_str(int status) {
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
         case GDN_ERR_HIP: return "HIP launch failed";
         case GDN_ERR_ALIAS: return "buffers that must be distinct overlap";
+        case GDN_ERR_SIGNATURE: return "snapshot of another layer shape or format";
+        case GDN_ERR_INDEX: return "sequence index out of range or repeated";
         default: return "unknown status";
     }
 }
@@ -188,6 +190,74 @@ gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, con
         return st;
     return launched(gdn::launch_commit(g, state, conv_tail, conv_w, n_nodes, parent, x, a, b, path_len, path, o,
                                        tree_status, as_stream(stream)));
+}
+
+uint64_t gdn_state_signature(const gdn_dims* d) {
+    gdn::Geo g;
+    return check_dims(d, g) == GDN_OK ? gdn::state_signature(g) : 0;
+}
+
+size_t gdn_snapshot_bytes(const gdn_dims* d, int32_t count) {
+    gdn::Geo g;
+    if (check_dims(d, g) != GDN_OK || count < 1 || count > GDN_MAX_TREE_BATCH)
+        return 0;
+    return gdn::snapshot_bytes(g, count);
+}
+
+}  // extern "C"
+
+namespace {
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+gdn_status snapshot_args(const gdn_dims* d, gdn::Geo& g, const void* state, const void* tail, int32_t count,
+                         const int32_t* seqs, const void* blob, size_t blob_bytes, const int32_t* status) {
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
+        st = GDN_ERR_SHAPE;
+    if (st == GDN_OK)
+        st = ptrs_ok({state, tail, seqs, blob, status});
+    if (st == GDN_OK && (reinterpret_cast<uintptr_t>(blob) & 255u))
+        st = GDN_ERR_ALIGN;
+    if (st == GDN_OK && (count < 1 || count > GDN_MAX_TREE_BATCH))
+        st = GDN_ERR_SHAPE;
+    if (st != GDN_OK)
+        return st;
+    const size_t need = gdn::snapshot_bytes(g, count);
+    if (blob_bytes < need)
+        return GDN_ERR_WORKSPACE;
+    const size_t sb = static_cast<size_t>(g.B) * g.Hv * g.D * g.D * 4;
+    const size_t tb = static_cast<size_t>(g.B) * g.C * 4 * (g.bf16 ? 2 : 4);
+    if (overlaps(blob, need, state, sb) || overlaps(blob, need, tail, tb))
+        return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_snapshot(const gdn_dims* d, const float* state, const void* conv_tail, int32_t count,
+                        const int32_t* seqs, void* blob, size_t blob_bytes, int32_t* status, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = snapshot_args(d, g, state, conv_tail, count, seqs, blob, blob_bytes, status);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_snapshot(g, false, const_cast<float*>(state), const_cast<void*>(conv_tail), count,
+                                         seqs, blob, status, as_stream(stream)));
+}
+
+gdn_status gdn_restore(const gdn_dims* d, float* state, void* conv_tail, int32_t count, const int32_t* seqs,
+                       const void* blob, size_t blob_bytes, int32_t* status, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = snapshot_args(d, g, state, conv_tail, count, seqs, blob, blob_bytes, status);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_snapshot(g, true, state, conv_tail, count, seqs, const_cast<void*>(blob), status,
+                                         as_stream(stream)));
 }
 
 size_t gdn_prefill_workspace_bytes(const gdn_dims* d, int32_t T) {

@@ -26,6 +26,10 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
                          int32_t* status, hipStream_t s);
+uint64_t state_signature(const Geo& g);
+size_t snapshot_bytes(const Geo& g, int count);
+hipError_t launch_snapshot(const Geo& g, bool restore, float* S, void* tail, int count, const int32_t* seqs,
+                           void* blob, int32_t* status, hipStream_t s);
 size_t prefill_workspace_bytes(const Geo& g, int T);
 hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int T, const void* x, const float* a,
                           const float* b, float* o, void* ws, hipStream_t s);

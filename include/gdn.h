@@ -66,7 +66,9 @@ typedef enum {
     GDN_ERR_TREE = 5,        /* malformed tree or path (also the device status value) */
     GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
     GDN_ERR_HIP = 7,         /* the HIP runtime refused a launch */
-    GDN_ERR_ALIAS = 8        /* buffers that must be distinct overlap */
+    GDN_ERR_ALIAS = 8,       /* buffers that must be distinct overlap */
+    GDN_ERR_SIGNATURE = 9,   /* a snapshot of another layer shape or format (device status value) */
+    GDN_ERR_INDEX = 10       /* a sequence index out of range, or repeated where it must not be (device status value) */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -222,6 +224,47 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims* d, int32_t T);
 gdn_status gdn_prefill_chunked(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w,
                                int32_t T, const void* x, const float* a, const float* b, float* o,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * State snapshots (repository "Architecture" page: the engine must restore a
+ * recurrent state exactly from a cache, which copies a sequence's state as
+ * sections in a fixed order; a signature over the sections' names, shapes and
+ * dtypes refuses a restore across models).  A sequence's state here has two
+ * sections, in this order:
+ *   "state"      f32 [Hv][dv][dk]
+ *   "conv_tail"  act [C][4]
+ * gdn_state_signature returns the 64-bit FNV-1a hash of the ASCII text
+ *   gdn-state-v1;state:f32[Hv,dv,dk];conv_tail:ACT[C,4]
+ * with the numbers in decimal and ACT "bf16" or "f32" (0 for bad dims).  The
+ * batch size is not part of it.
+ *
+ * A snapshot of `count` sequences is one device blob of
+ * gdn_snapshot_bytes(d, count) bytes: a 256-byte header (little endian: u32
+ * magic GDN_SNAPSHOT_MAGIC, u32 version GDN_SNAPSHOT_VERSION, u64 signature,
+ * u32 count, u32 0, u64 state bytes per sequence, u64 tail bytes per
+ * sequence, zeros), then the "state" section of all count sequences, then
+ * their "conv_tail" section.  The blob can be copied anywhere and back
+ * (host, disk) as plain bytes.
+ *
+ * gdn_snapshot copies sequences seqs[0..count-1] (i32, device, 0 <= seqs[i] <
+ * batch; repeats allowed) of (state, conv_tail) into blob slots 0..count-1.
+ * gdn_restore copies blob slots 0..count-1 into sequences seqs[i], which must
+ * be distinct.  Both write *status (i32, device, required): GDN_OK, or
+ * GDN_ERR_INDEX for a bad seqs array, or (restore) GDN_ERR_SIGNATURE when the
+ * blob's header does not match d and count; on an error nothing is restored,
+ * and a refused snapshot's header has magic 0.  A restored sequence equals,
+ * bit for bit, the one that was saved, so decode continues from it exactly.
+ * 1 <= count <= GDN_MAX_TREE_BATCH; blob 256-byte aligned.
+ */
+#define GDN_SNAPSHOT_MAGIC 0x534E4447u /* "GDNS" */
+#define GDN_SNAPSHOT_VERSION 1
+#define GDN_SNAPSHOT_HEADER_BYTES 256
+uint64_t gdn_state_signature(const gdn_dims* d);
+size_t gdn_snapshot_bytes(const gdn_dims* d, int32_t count);
+gdn_status gdn_snapshot(const gdn_dims* d, const float* state, const void* conv_tail, int32_t count,
+                        const int32_t* seqs, void* blob, size_t blob_bytes, int32_t* status, void* stream);
+gdn_status gdn_restore(const gdn_dims* d, float* state, void* conv_tail, int32_t count, const int32_t* seqs,
+                       const void* blob, size_t blob_bytes, int32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

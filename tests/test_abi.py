@@ -140,6 +140,64 @@ def test_fused_token_refuses_overlapping_tails(lib):
 
 def test_status_strings(lib):
     lib.gdn_status_str.restype = C.c_char_p
-    for s in range(9):
+    for s in range(11):
         assert lib.gdn_status_str(s)
+    assert lib.gdn_status_str(11) == b"unknown status"
     assert lib.gdn_abi_version() == 1
+
+
+def fnv1a64(data: bytes) -> int:
+    h = 0xCBF29CE484222325
+    for byte in data:
+        h ^= byte
+        h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_fnv1a64_reference_vectors():
+    """The published FNV-1a 64-bit test vectors, so the check below pins the definition."""
+    assert fnv1a64(b"") == 0xCBF29CE484222325
+    assert fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_state_signature_is_the_documented_hash(lib):
+    """gdn_state_signature is FNV-1a 64 of the section text the header documents: names,
+    shapes and dtypes of the two sections; the batch size does not enter it."""
+    lib.gdn_state_signature.restype = C.c_uint64
+    lib.gdn_state_signature.argtypes = [C.POINTER(Dims)]
+    cases = [mk(), mk(batch=64), mk(act_dtype=0), mk(num_k_heads=4, num_v_heads=4, head_k_dim=32, head_v_dim=32),
+             mk(num_k_heads=8)]
+    sigs = []
+    for d in cases:
+        Cc = 2 * d.num_k_heads * d.head_k_dim + d.num_v_heads * d.head_v_dim
+        text = (f"gdn-state-v1;state:f32[{d.num_v_heads},{d.head_v_dim},{d.head_k_dim}];"
+                f"conv_tail:{'bf16' if d.act_dtype == 1 else 'f32'}[{Cc},4]")
+        assert lib.gdn_state_signature(C.byref(d)) == fnv1a64(text.encode())
+        sigs.append(lib.gdn_state_signature(C.byref(d)))
+    assert sigs[0] == sigs[1]                      # batch is not part of it
+    assert len({sigs[0], sigs[2], sigs[3], sigs[4]}) == 4
+    assert lib.gdn_state_signature(C.byref(mk(conv_width=3))) == 0
+
+
+def test_snapshot_sizes_and_refusals(lib):
+    P = C.c_void_p
+    lib.gdn_snapshot_bytes.restype = C.c_size_t
+    lib.gdn_snapshot_bytes.argtypes = [C.POINTER(Dims), C.c_int32]
+    for f in (lib.gdn_snapshot, lib.gdn_restore):
+        f.argtypes = [C.POINTER(Dims), P, P, C.c_int32, P, P, C.c_size_t, P, P]
+    d = mk(batch=4)
+    per = 48 * 128 * 128 * 4 + 10240 * 4 * 2
+    assert lib.gdn_snapshot_bytes(C.byref(d), 3) == 256 + 3 * per
+    assert lib.gdn_snapshot_bytes(C.byref(d), 0) == 0
+    assert lib.gdn_snapshot_bytes(C.byref(d), 65536) == 0
+    need = 256 + 2 * per
+    S, T, Q, ST = P(0x10000000), P(0x20000000), P(0x30000000), P(0x30000100)
+    blob = P(0x40000000)
+    for f in (lib.gdn_snapshot, lib.gdn_restore):
+        assert f(C.byref(d), S, T, 2, Q, blob, need, None, None) == 1          # status is required
+        assert f(C.byref(d), S, T, 2, Q, P(0x40000010), need, ST, None) == 4   # blob not 256-byte aligned
+        assert f(C.byref(d), S, T, 2, Q, blob, need - 16, ST, None) == 6       # blob too small
+        assert f(C.byref(d), S, T, 0, Q, blob, need, ST, None) == 2            # count out of range
+        assert f(C.byref(d), S, T, 2, Q, P(0x10000000 + 4096), need, ST, None) == 8   # blob inside the state
+        assert f(C.byref(mk(batch=65536)), S, T, 2, Q, blob, need, ST, None) == 2
