@@ -17,7 +17,8 @@ weights, gates, o) over the time.
 Extra rows, each with its own roofline fraction: the same step under a hip
 graph and as two calls, the state step alone, batch-64 decode (ping-pong
 over two batches), 32-node tree verify and path commit at batch 1 and over
-64 sequences' trees, snapshot and restore of 64 sequences, chunked prefill
+64 sequences' trees, 16-token block verify and commit, snapshot and restore
+of 64 sequences, chunked prefill
 at T = 32,768; and the CPU oracle on a bounded sample as the host baseline.
 Inputs are seeded synthetic tensors of the workload's shapes.
 """
@@ -64,6 +65,14 @@ def tree_bytes(n, shape, B=1):
     checkpoint read once, x, conv tail (bf16), gates, parent and o; the conv weights once."""
     Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
     per_seq = Hv * D * D * 4 + n * C * 2 + C * 4 * 2 + 2 * n * Hv * 4 + n * Hv * D * 4 + n * 4
+    return B * per_seq + C * 4 * 2
+
+
+def block_bytes(k, shape, B=1):
+    """Algorithmic bytes of one block verify of k tokens over B sequences: per sequence the
+    checkpoint read once, the tail, k rows of x, gates and o; the conv weights once."""
+    Hv, D, C = shape.num_v_heads, shape.head_k_dim, shape.conv_channels
+    per_seq = Hv * D * D * 4 + C * 4 * 2 + k * (C * 2 + 2 * Hv * 4 + Hv * D * 4)
     return B * per_seq + C * 4 * 2
 
 
@@ -139,7 +148,7 @@ def main():
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--buffers", type=int, default=160, help="independent states rotated through (cold runs)")
-    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,tree64,snapshot,prefill,hot,cpu or all/none")
+    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,tree64,block,snapshot,prefill,hot,cpu or all/none")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 512 MiB device copy (for byte counters)")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
     args = ap.parse_args()
@@ -154,7 +163,7 @@ def main():
     import gated_deltanet_decode_amd as gdn
     import gdn_inputs as gi
 
-    rows = set(["graph", "kernel", "b64", "tree", "commit", "tree64", "snapshot", "prefill", "hot", "cpu"]) \
+    rows = set(["graph", "kernel", "b64", "tree", "commit", "tree64", "block", "snapshot", "prefill", "hot", "cpu"]) \
         if args.rows == "all" else \
         set() if args.rows == "none" else set(args.rows.split(","))
     dev = "cuda"
@@ -360,6 +369,40 @@ def main():
                                   "committed_tokens_per_s": sum(lens) / (us + res["tree_verify_b64_n32"]["us"]) * 1e6}
         assert int(stB.abs().sum().item()) == 0
         del S2, T2, xB, aB, bB, oB, wsB
+
+    # ---------------------------------------------------------------- block verify + commit, 16 tokens
+    # Batch 1 rotates over the R cold states; batch 64 alternates two batches.
+    if "block" in rows:
+        kb = 16
+        for B, nbuf in ((1, R), (64, 2)):
+            pool = gi.decode_inputs(107, shape, nbuf * B, 1, state_sigma=0.1, tail_random=True)
+            Sb = f32(pool.state).view(nbuf, B, Hv, D, D)
+            Tb = act(pool.tail).view(nbuf, B, C, 4)
+            del pool
+            bi = gi.decode_inputs(8, shape, B, kb, state_sigma=0.0, tail_random=False)
+            seqm = lambda arr: np.ascontiguousarray(np.swapaxes(arr, 0, 1))
+            xB, aB, bB, wB = act(seqm(bi.x)), f32(seqm(bi.a)), f32(seqm(bi.b)), act(bi.w)
+            dB = gdn.dims(B, 16, 48, 128, 128, 4, "bf16")
+            oB = torch.empty(B, kb, Hv, D, device=dev)
+            wsB = torch.empty(gdn.block_workspace_bytes(dB, kb), dtype=torch.uint8, device=dev)
+            n = 256 if B == 1 else 32
+            us = graph_time_us(torch, lambda r: gdn.block_verify(dB, Sb[r % nbuf], Tb[r % nbuf], wB, xB, aB, bB, oB,
+                                                                  wsB), n, reps=2)
+            vb = block_bytes(kb, shape, B)
+            res[f"block_verify_b{B}_k{kb}"] = {"us": us, "GBps": vb / us / 1e3, "frac_hbm": vb / us / 1e3 / HBM_PEAK_GBS,
+                                               "tokens_per_s": B * kb / us * 1e6, "bytes": vb, "launch": "hipGraph"}
+            if B == 64:
+                acc_np = np.array([(7 * s) % (kb + 1) for s in range(B)], np.int32)
+                acc = torch.from_numpy(acc_np).to(dev)
+                stB = torch.zeros(B, dtype=torch.int32, device=dev)
+                us = graph_time_us(torch, lambda r: gdn.block_commit(dB, Sb[r % nbuf], Tb[r % nbuf], wB, xB, aB, bB,
+                                                                      acc, None, stB, wsB), n, reps=2)
+                cb = commit_bytes([int(L) for L in acc_np if L > 0], shape)
+                res[f"block_commit_b{B}_k{kb}"] = {"us": us, "accepted_tokens": int(acc_np.sum()), "GBps": cb / us / 1e3,
+                                                   "frac_hbm": cb / us / 1e3 / HBM_PEAK_GBS, "bytes": cb,
+                                                   "launch": "hipGraph"}
+                assert int(stB.abs().sum().item()) == 0
+            del Sb, Tb, xB, aB, bB, oB, wsB
 
     # ---------------------------------------------------------------- snapshot / restore, 64 sequences
     # Save all 64 sequences of one batch into a blob and restore them into the

@@ -72,6 +72,9 @@ _sig = {
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
     "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
     "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "gdn_block_workspace_bytes": ([_D, _I], C.c_size_t),
+    "gdn_block_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "gdn_block_commit": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_state_signature": ([_D], C.c_uint64),
     "gdn_snapshot_bytes": ([_D, _I], C.c_size_t),
     "gdn_snapshot": ([_D, _P, _P, _I, _P, _P, C.c_size_t, _P, _P], C.c_int),
@@ -207,6 +210,43 @@ def tree_tables(parent, depth, order, status, stream=None) -> None:
     _check(_lib.gdn_tree_tables(n, _t(parent, "parent", torch.int32, n), _t(depth, "depth", torch.int32, n),
                                 _t(order, "order", torch.int32, n), _t(status, "tree_status", torch.int32, 1),
                                 _stream(stream)), "gdn_tree_tables")
+
+
+def block_workspace_bytes(d: Dims, k: int) -> int:
+    return _lib.gdn_block_workspace_bytes(C.byref(d), k)
+
+
+def _block_common(d, x, workspace):
+    B, Cc = d.batch, d.C
+    if x.numel() % (B * Cc):
+        raise ValueError("x must be [B][k][C]")
+    k = x.numel() // (B * Cc)
+    ptr, nbytes = _blob(workspace, block_workspace_bytes(d, k), "workspace")
+    return k, ptr, nbytes
+
+
+def block_verify(d: Dims, state, tail, w, x, a, b, o, workspace, stream=None) -> None:
+    """A block of k tokens per sequence: x [B][k][C], a, b [B][k][Hv], o [B][k][Hv][dv]."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    k, ptr, nbytes = _block_common(d, x, workspace)
+    _check(_lib.gdn_block_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
+                                 _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                                 k, _t(x, "x", d.act_torch, B * k * Cc), _t(a, "a", torch.float32, B * k * Hv),
+                                 _t(b, "b", torch.float32, B * k * Hv), _t(o, "o", torch.float32, B * k * Hv * dv),
+                                 ptr, nbytes, _stream(stream)), "gdn_block_verify")
+
+
+def block_commit(d: Dims, state, tail, w, x, a, b, accepted, o=None, status=None, workspace=None,
+                 stream=None) -> None:
+    """Advance each sequence by its first accepted[seq] (int32 [B], device) block tokens."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    k, ptr, nbytes = _block_common(d, x, workspace)
+    _check(_lib.gdn_block_commit(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                 _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                                 k, _t(x, "x", d.act_torch, B * k * Cc), _t(a, "a", torch.float32, B * k * Hv),
+                                 _t(b, "b", torch.float32, B * k * Hv), _t(accepted, "accepted", torch.int32, B),
+                                 _opt(o, "o", torch.float32, B * k * Hv * dv), _opt(status, "status", torch.int32, B),
+                                 ptr, nbytes, _stream(stream)), "gdn_block_commit")
 
 
 def state_signature(d: Dims) -> int:

@@ -192,6 +192,63 @@ gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, con
                                        tree_status, as_stream(stream)));
 }
 
+size_t gdn_block_workspace_bytes(const gdn_dims* d, int32_t k) {
+    gdn::Geo g;
+    if (check_dims(d, g) != GDN_OK || k < 1 || k > GDN_MAX_TREE_NODES)
+        return 0;
+    return gdn::tree_ws_bytes(g.B, k, g.Hk, g.Hv, g.D);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn_status block_args(const gdn_dims* d, gdn::Geo& g, std::initializer_list<const void*> ptrs, int32_t k,
+                      const void* o, const int32_t* status, const void* workspace, size_t workspace_bytes) {
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
+        st = GDN_ERR_SHAPE;
+    if (st == GDN_OK)
+        st = ptrs_ok(ptrs);
+    if (st == GDN_OK && ((o && !aligned16(o)) || (status && !aligned16(status))))
+        st = GDN_ERR_ALIGN;
+    if (st == GDN_OK && (k < 1 || k > GDN_MAX_TREE_NODES))
+        st = GDN_ERR_SHAPE;
+    if (st != GDN_OK)
+        return st;
+    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, k, g.Hk, g.Hv, g.D))
+        return GDN_ERR_WORKSPACE;
+    return aligned16(workspace) ? GDN_OK : GDN_ERR_ALIGN;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_block_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
+                            int32_t k, const void* x, const float* a, const float* b, float* o, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = block_args(d, g, {state_ckpt, conv_tail, conv_w, x, a, b, o}, k, o, nullptr, workspace,
+                                     workspace_bytes);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_block(g, false, const_cast<float*>(state_ckpt), const_cast<void*>(conv_tail),
+                                      conv_w, k, x, a, b, nullptr, o, nullptr, workspace, as_stream(stream)));
+}
+
+gdn_status gdn_block_commit(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w, int32_t k,
+                            const void* x, const float* a, const float* b, const int32_t* accepted, float* o,
+                            int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = block_args(d, g, {state, conv_tail, conv_w, x, a, b, accepted}, k, o, status, workspace,
+                                     workspace_bytes);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_block(g, true, state, conv_tail, conv_w, k, x, a, b, accepted, o, status, workspace,
+                                      as_stream(stream)));
+}
+
 uint64_t gdn_state_signature(const gdn_dims* d) {
     gdn::Geo g;
     return check_dims(d, g) == GDN_OK ? gdn::state_signature(g) : 0;

@@ -252,7 +252,8 @@ static TreeWs tree_ws_carve(void* base, int B, int n, int Hk, int Hv, int D) {
 // depths) once for every workgroup of the verify kernel, and report the
 // sequence's status.  The others, one per (sequence, q/k head, node): the
 // node's conv window over its q/k head's channels and its value heads'
-// channels, the q/k norm and the gates.
+// channels, the q/k norm and the gates.  With no parent array the nodes are a
+// block, the chain 0 -> 1 -> ... -> n-1 (valid by construction).
 // The ancestor chain is followed at most three links and every link is
 // checked, so a malformed parent array stays in bounds (the verify kernel
 // reports it and writes nothing).
@@ -267,6 +268,17 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
     __shared__ int32_t depth_s[kMaxNodes], order_s[kMaxNodes];
     if (static_cast<int>(blockIdx.x) < B) {
         const int bq = blockIdx.x;
+        if (parent == nullptr) {
+            int32_t* tab = ws.tab + static_cast<size_t>(bq) * (2 * n + 1);
+            const int t = threadIdx.x;
+            if (t < n) {
+                tab[t] = t;
+                tab[n + t] = t + 1;
+            }
+            if (t == 0)
+                tab[2 * n] = 1;
+            return;
+        }
         bool ok = false;
         if (threadIdx.x < kWave)
             ok = tree_tables_wave(n, parent + static_cast<size_t>(bq) * n, depth_s, order_s);
@@ -293,14 +305,13 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
     const int bq = wg / (n * Hk);
     const int G = Hv / Hk;
     const int m0 = bq * n;   // workspace index of the sequence's node 0
-    parent += m0;
     x += static_cast<size_t>(m0) * C;
     a += static_cast<size_t>(m0) * Hv;
     b += static_cast<size_t>(m0) * Hv;
     tail += static_cast<size_t>(bq) * C * 4;
     const int lane = threadIdx.x & (kWave - 1);
-    if (threadIdx.x < kWave) {
-        const int p = lane < n ? parent[lane] : -1;
+    if (threadIdx.x < kWave && parent != nullptr) {
+        const int p = lane < n ? parent[m0 + lane] : -1;
         int cur = i, m = 0;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -313,6 +324,11 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
         }
         if (lane == 0)
             anc_s[3] = m;   // ancestors found (at most 3)
+    } else if (threadIdx.x == 0) {   // a block: the previous positions
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            anc_s[k] = i - 1 - k >= 0 ? i - 1 - k : -1;
+        anc_s[3] = i < 3 ? i : 3;
     }
     __syncthreads();
     const int m = anc_s[3];
@@ -397,7 +413,8 @@ template <int D>
 struct VerifyCtx {
     using R = Row<D>;
     static constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW, ROWS = 4 * RPW;
-    int h, grp, lane, r, row, m0, n, Hk, Hv, ord_l, dep_l, ok;
+    int h, grp, bq, lane, r, row, m0, n, Hk, Hv, ord_l, dep_l, ok;
+    bool first;   // the workgroup of head 0, rows 0.. of its sequence
     const float* Sh;
     float* oh;   // o of this lane's row at node 0 of the sequence
     TreeWs ws;
@@ -409,7 +426,8 @@ struct VerifyCtx {
         const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
         const int blk = wid % blocks_per_head;
         h = (wid / blocks_per_head) % Hv;
-        const int bq = wid / (blocks_per_head * Hv);
+        bq = wid / (blocks_per_head * Hv);
+        first = wid % (blocks_per_head * Hv) == 0;
         grp = h / (Hv / Hk);
         lane = threadIdx.x & (kWave - 1);
         r = lane % LPR;
@@ -475,12 +493,23 @@ struct WalkWide {
     static constexpr bool defer_o = false;
 };
 
-template <int D, typename Walk>
+// What a walk does.  Tree: verify a draft tree (saved levels, reloads).
+// Chain: verify a block, the chain 0 -> 1 -> ... -> n-1 (every node continues
+// from the previous one: no saved levels, no LDS).  ChainCommit: advance each
+// sequence's state in place by the first accepted[seq] nodes of its block.
+enum class WalkKind { Tree, Chain, ChainCommit };
+
+struct NoSmem {};
+
+template <int D, typename Walk, WalkKind KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves))) void tree_verify_kernel(
-    const float* __restrict__ Sc, int n, TreeWs ws, float* __restrict__ o, int Hk, int Hv, int blocks_per_head) {
+    const float* __restrict__ Sc, int n, TreeWs ws, float* __restrict__ o, int Hk, int Hv, int blocks_per_head,
+    const int32_t* __restrict__ accepted, int32_t* __restrict__ status) {
     using R = Row<D>;
     constexpr int NV = R::NV, RING = Walk::ring, LEVELS = Walk::levels;
-    __shared__ VerifySmem<D, LEVELS> sm;
+    constexpr bool TREE = KIND == WalkKind::Tree, COMMIT = KIND == WalkKind::ChainCommit;
+    using Smem = std::conditional_t<TREE, VerifySmem<D, LEVELS>, NoSmem>;
+    __shared__ Smem sm;
     const VerifyCtx<D> c(Sc, n, ws, o, Hk, Hv, blocks_per_head);
     const int tid = threadIdx.x;
     float4 base[NV];
@@ -489,6 +518,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         base[j] = load_stream(c.Sh + c.row * D + R::key(j, c.r));
     if (!c.ok)   // nothing is written for a malformed tree
         return;
+    int len = n;   // walk steps
+    if constexpr (COMMIT) {
+        len = accepted[c.bq];
+        const bool valid = len >= 0 && len <= n;
+        if (status && c.first && c.lane == 0 && threadIdx.x == 0)
+            status[c.bq] = valid ? 0 : 10;   // GDN_ERR_INDEX
+        if (!valid || len == 0)
+            return;
+    }
 
     // Node operands stream through a ring of RING register slots, unrolled so
     // that each slot keeps its registers: a slot is refilled with the node
@@ -500,6 +538,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         c.load_node(ring[p], p);
     float4 s[NV];
     float outv[Walk::defer_o ? kMaxNodes : 1];   // o of each walk step, stored after the walk
+    const bool want_o = !COMMIT || o != nullptr;
     int dprev = 0;
     // One walk step per node, expanded at compile time (at most kMaxNodes),
     // so that ring slots are static registers and every wait on a slot counts
@@ -507,7 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
     auto step = [&](auto itc) -> bool {
         constexpr int it = decltype(itc)::value;
         constexpr int p = it % RING;
-        if (it >= n)
+        if (it >= len)
             return false;
         const int d = __builtin_amdgcn_readlane(c.dep_l, it);
         // A valid tree's pre-order starts at the root, the only node of depth
@@ -516,46 +555,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
 #pragma unroll
             for (int j = 0; j < NV; ++j)
                 s[j] = base[j];
-        } else if (d != dprev + 1) {
-            if (LEVELS == kMaxDepth - 1 || d - 1 <= LEVELS) {
+        } else if constexpr (TREE) {
+            if (d != dprev + 1) {
+                if (LEVELS == kMaxDepth - 1 || d - 1 <= LEVELS) {
 #pragma unroll
-                for (int j = 0; j < NV; ++j)
-                    s[j] = sm.stack[d - 2][j][tid];
-            } else {
-                // Replay the ancestors of depths LEVELS + 1 .. d - 1, each the
-                // latest position before this one with its depth.
+                    for (int j = 0; j < NV; ++j)
+                        s[j] = sm.stack[d - 2][j][tid];
+                } else {
+                    // Replay the ancestors of depths LEVELS + 1 .. d - 1, each
+                    // the latest position before this one with its depth.
 #pragma unroll
-                for (int j = 0; j < NV; ++j)
-                    s[j] = sm.stack[LEVELS - 1][j][tid];
-                for (int e = LEVELS + 1; e < d; ++e) {
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(c.dep_l == e) & ((1ull << it) - 1);
-                    NodeOps<D> anc;
-                    c.load_node(anc, 63 - __builtin_clzll(m));
-                    (void)node_update<D>(s, anc);
+                    for (int j = 0; j < NV; ++j)
+                        s[j] = sm.stack[LEVELS - 1][j][tid];
+                    for (int e = LEVELS + 1; e < d; ++e) {
+                        const uint64_t m = __builtin_amdgcn_ballot_w64(c.dep_l == e) & ((1ull << it) - 1);
+                        NodeOps<D> anc;
+                        c.load_node(anc, 63 - __builtin_clzll(m));
+                        (void)node_update<D>(s, anc);
+                    }
                 }
             }
         }
         const float out = node_update<D>(s, ring[p]);
         if constexpr (Walk::defer_o)
             outv[it] = out;
-        else
+        else if (want_o)
             c.store_o(it, out);
-        if (d <= LEVELS) {
+        if constexpr (TREE) {
+            if (d <= LEVELS) {
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
-                sm.stack[d - 1][j][tid] = s[j];
+                for (int j = 0; j < NV; ++j)
+                    sm.stack[d - 1][j][tid] = s[j];
+            }
         }
         dprev = d;
         if (it + RING < kMaxNodes)
             c.load_node(ring[p], it + RING);
+        // A chain walk has no branches, so without this the scheduler would
+        // sink each refill next to its use and the ring would prefetch nothing.
+        if constexpr (!TREE)
+            __builtin_amdgcn_sched_barrier(0);
         return true;
     };
     walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
     if constexpr (Walk::defer_o) {
+        if (want_o) {
 #pragma unroll
-        for (int it = 0; it < kMaxNodes; ++it)
-            if (it < n)
-                c.store_o(it, outv[it]);
+            for (int it = 0; it < kMaxNodes; ++it)
+                if (it < len)
+                    c.store_o(it, outv[it]);
+        }
+    }
+    if constexpr (COMMIT) {
+        float* Sw = const_cast<float*>(c.Sh);
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            store_stream(Sw + c.row * D + R::key(j, c.r), s[j]);
     }
 }
 
@@ -595,12 +650,77 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
         const unsigned grid = static_cast<unsigned>(g.B * g.Hv * bph);
         // More workgroups than two per CU: the form for several trees per CU.
         if (grid > 2u * 256u)
-            hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide>), dim3(grid), dim3(256), 0, s, S, n, W, o, g.Hk,
-                               g.Hv, bph);
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::Tree>), dim3(grid), dim3(256), 0, s, S, n,
+                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
         else
-            hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep>), dim3(grid), dim3(256), 0, s, S, n, W, o, g.Hk,
-                               g.Hv, bph);
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep, WalkKind::Tree>), dim3(grid), dim3(256), 0, s, S, n,
+                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
     });
+}
+
+// ------------------------------------------------------------ blocks
+
+// The tail after a block commit holds the last four raw inputs of (old tail ++
+// the block's first len tokens); a sequence with an invalid or zero len keeps
+// its tail.  Runs after the prep launch, the only reader of the old tail.
+template <typename Act>
+__global__ __launch_bounds__(256) void block_tail_kernel(Act* __restrict__ tail, const Act* __restrict__ x, int k,
+                                                         const int32_t* __restrict__ accepted, int C) {
+    const int bq = blockIdx.y;
+    const int len = accepted[bq];
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (len <= 0 || len > k || c >= C)
+        return;
+    using Q = Quad<Act>;
+    Act* tc = tail + (static_cast<size_t>(bq) * C + c) * 4;
+    typename Q::raw t = Q::load(tc);
+    const Act* xb = x + static_cast<size_t>(bq) * k * C + c;
+    for (int j = len > 4 ? len - 4 : 0; j < len; ++j)
+        t = Q::push(t, xb[static_cast<size_t>(j) * C]);
+    Q::store(tc, t);
+}
+
+hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const void* w, int k, const void* x,
+                        const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
+                        hipStream_t s) {
+    const TreeWs W = tree_ws_carve(ws, g.B, k, g.Hk, g.Hv, g.D);
+    hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
+        constexpr int D = decltype(dtag)::value;
+        using Act = decltype(atag);
+        hipLaunchKernelGGL((tree_prep_kernel<D, Act>), dim3(static_cast<unsigned>(g.B + g.B * k * g.Hk)), dim3(256),
+                           0, s, static_cast<const Act*>(tail), static_cast<const Act*>(w), k, nullptr,
+                           static_cast<const Act*>(x), a, b, W, nullptr, g.B, g.Hk, g.Hv, g.C);
+    });
+    if (e != hipSuccess)
+        return e;
+    e = dispatch(g, [&](auto dtag, auto) {
+        constexpr int D = decltype(dtag)::value;
+        const int bph = D / (4 * Row<D>::RPW);
+        const unsigned grid = static_cast<unsigned>(g.B * g.Hv * bph);
+        const bool wide = grid > 2u * 256u;
+        if (commit && wide)
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::ChainCommit>), dim3(grid), dim3(256), 0, s,
+                               S, k, W, o, g.Hk, g.Hv, bph, accepted, status);
+        else if (commit)
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep, WalkKind::ChainCommit>), dim3(grid), dim3(256), 0, s,
+                               S, k, W, o, g.Hk, g.Hv, bph, accepted, status);
+        else if (wide)
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::Chain>), dim3(grid), dim3(256), 0, s, S, k,
+                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
+        else
+            hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep, WalkKind::Chain>), dim3(grid), dim3(256), 0, s, S, k,
+                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
+    });
+    if (e != hipSuccess || !commit)
+        return e;
+    const dim3 grid(static_cast<unsigned>((g.C + 255) / 256), static_cast<unsigned>(g.B)), block(256);
+    if (g.bf16)
+        hipLaunchKernelGGL(block_tail_kernel<uint16_t>, grid, block, 0, s, static_cast<uint16_t*>(tail),
+                           static_cast<const uint16_t*>(x), k, accepted, g.C);
+    else
+        hipLaunchKernelGGL(block_tail_kernel<float>, grid, block, 0, s, static_cast<float*>(tail),
+                           static_cast<const float*>(x), k, accepted, g.C);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------ commit

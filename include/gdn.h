@@ -226,6 +226,44 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, float* state, void* conv_tail,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_block_verify -- one read-only pass over a block of k drafted tokens per
+ * sequence (repository "Architecture" page, "The parts": delta-rule kernels
+ * for one token, a block and a tree; drafters that propose a block of tokens
+ * at once): the chain 0 -> 1 -> ... -> k-1 after the checkpoint.  Position t's
+ * output equals, bit for bit, the output of gdn_conv_update + gdn_decode_step
+ * run over positions 0..t from the sequence's checkpoint.  Unlike a tree, a
+ * block has no depth limit below its length.
+ *   state_ckpt f32 [B][Hv][dv][dk], conv_tail act [B][C][4]: read only
+ *   k          1..32 tokens per sequence
+ *   x act [B][k][C];  a, b f32 [B][k][Hv];  o f32 [B][k][Hv][dv] (written)
+ *   workspace  device bytes >= gdn_block_workspace_bytes(d, k), 16-byte aligned
+ * A longer block is verified in parts of up to 32 with gdn_block_commit of
+ * each part in between (on a snapshot, if it may be rejected), or with
+ * gdn_prefill_chunked over a copy of the state, which rounds as the chunked
+ * form does.  1 <= batch <= GDN_MAX_TREE_BATCH.
+ */
+size_t gdn_block_workspace_bytes(const gdn_dims* d, int32_t k);
+gdn_status gdn_block_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
+                            int32_t k, const void* x, const float* a, const float* b, float* o, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_block_commit -- advance each sequence by the first accepted[seq] tokens
+ * of its block, bit-identical to one gdn_conv_update + gdn_decode_step per
+ * token.
+ *   state f32 [B][Hv][dv][dk], conv_tail act [B][C][4]: in/out
+ *   k, x, a, b, workspace: as for gdn_block_verify
+ *   accepted   i32 [B] (device): 0..k tokens; 0 commits nothing
+ *   o          f32 [B][k][Hv][dv] or NULL: outputs of the committed positions
+ *              (later positions are not written)
+ *   status     i32 [B] or NULL: per sequence GDN_OK, or GDN_ERR_INDEX when its
+ *              accepted count is out of range (that sequence is untouched)
+ */
+gdn_status gdn_block_commit(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w, int32_t k,
+                            const void* x, const float* a, const float* b, const int32_t* accepted, float* o,
+                            int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * State snapshots (repository "Architecture" page: the engine must restore a
  * recurrent state exactly from a cache, which copies a sequence's state as
  * sections in a fixed order; a signature over the sections' names, shapes and
