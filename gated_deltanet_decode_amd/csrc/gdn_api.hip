@@ -154,7 +154,7 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
                            float* o, int32_t* tree_status, void* workspace, size_t workspace_bytes, void* stream) {
     gdn::Geo g;
     gdn_status st = check_dims(d, g);
-    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
+    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
         st = GDN_ERR_SHAPE;
     if (st == GDN_OK)
         st = ptrs_ok({state_ckpt, conv_tail, conv_w, parent, x, a, b, o});
@@ -177,7 +177,7 @@ gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, con
                            const int32_t* path, float* o, int32_t* tree_status, void* stream) {
     gdn::Geo g;
     gdn_status st = check_dims(d, g);
-    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
+    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
         st = GDN_ERR_SHAPE;
     if (st == GDN_OK)
         st = ptrs_ok({state, conv_tail, conv_w, parent, x, a, b, path});
@@ -206,7 +206,7 @@ namespace {
 gdn_status block_args(const gdn_dims* d, gdn::Geo& g, std::initializer_list<const void*> ptrs, int32_t k,
                       const void* o, const int32_t* status, const void* workspace, size_t workspace_bytes) {
     gdn_status st = check_dims(d, g);
-    if (st == GDN_OK && g.B > GDN_MAX_TREE_BATCH)
+    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
         st = GDN_ERR_SHAPE;
     if (st == GDN_OK)
         st = ptrs_ok(ptrs);

@@ -253,18 +253,23 @@ static TreeWs tree_ws_carve(void* base, int B, int n, int Hk, int Hv, int D) {
 // sequence's status.  The others, one per (sequence, q/k head, node): the
 // node's conv window over its q/k head's channels and its value heads'
 // channels, the q/k norm and the gates.  With no parent array the nodes are a
-// block, the chain 0 -> 1 -> ... -> n-1 (valid by construction).
+// block, the chain 0 -> 1 -> ... -> n-1 (valid by construction).  Each
+// workgroup prepares NPW consecutive nodes of one (sequence, q/k head), all
+// their window loads in flight together: NPW = 1 when the grid is small (one
+// tree), 4 when it is many workgroups deep, where one node per workgroup would
+// leave each CU waiting through several latency-bound rounds.
 // The ancestor chain is followed at most three links and every link is
 // checked, so a malformed parent array stays in bounds (the verify kernel
 // reports it and writes nothing).
-template <int D, typename Act>
+template <int D, typename Act, int NPW>
 __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
                                                         int n, const int32_t* __restrict__ parent,
                                                         const Act* __restrict__ x, const float* __restrict__ a,
                                                         const float* __restrict__ b, TreeWs ws,
                                                         int32_t* __restrict__ status, int B, int Hk, int Hv, int C) {
-    __shared__ float yqk[2 * D];
-    __shared__ int32_t anc_s[4];
+    static_assert(NPW >= 1 && NPW <= 4, "one wave normalises each node of the workgroup");
+    __shared__ float yqk[NPW][2 * D];
+    __shared__ int32_t anc_s[NPW][4];
     __shared__ int32_t depth_s[kMaxNodes], order_s[kMaxNodes];
     if (static_cast<int>(blockIdx.x) < B) {
         const int bq = blockIdx.x;
@@ -300,9 +305,10 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
         return;
     }
     const int wg = blockIdx.x - B;
-    const int i = wg % n;
-    const int g = (wg / n) % Hk;
-    const int bq = wg / (n * Hk);
+    const int nq = (n + NPW - 1) / NPW;   // node groups per (sequence, q/k head)
+    const int i0 = (wg % nq) * NPW;       // the workgroup's first node
+    const int g = (wg / nq) % Hk;
+    const int bq = wg / (nq * Hk);
     const int G = Hv / Hk;
     const int m0 = bq * n;   // workspace index of the sequence's node 0
     x += static_cast<size_t>(m0) * C;
@@ -312,60 +318,81 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
     const int lane = threadIdx.x & (kWave - 1);
     if (threadIdx.x < kWave && parent != nullptr) {
         const int p = lane < n ? parent[m0 + lane] : -1;
-        int cur = i, m = 0;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int up = __shfl(p, cur >= 0 ? cur : 0, kWave);
-            const bool link = cur >= 0 && up >= 0 && up < cur;
+        for (int u = 0; u < NPW; ++u) {
+            int cur = i0 + u < n ? i0 + u : n - 1, m = 0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int up = __shfl(p, cur >= 0 ? cur : 0, kWave);
+                const bool link = cur >= 0 && up >= 0 && up < cur;
+                if (lane == 0)
+                    anc_s[u][k] = link ? up : -1;
+                m += link ? 1 : 0;
+                cur = link ? up : -1;
+            }
             if (lane == 0)
-                anc_s[k] = link ? up : -1;
-            m += link ? 1 : 0;
-            cur = link ? up : -1;
+                anc_s[u][3] = m;   // ancestors found (at most 3)
         }
-        if (lane == 0)
-            anc_s[3] = m;   // ancestors found (at most 3)
-    } else if (threadIdx.x == 0) {   // a block: the previous positions
+    } else if (parent == nullptr && threadIdx.x < NPW) {   // a block: the previous positions
+        const int u = threadIdx.x;
+        const int i = i0 + u < n ? i0 + u : n - 1;
 #pragma unroll
         for (int k = 0; k < 3; ++k)
-            anc_s[k] = i - 1 - k >= 0 ? i - 1 - k : -1;
-        anc_s[3] = i < 3 ? i : 3;
+            anc_s[u][k] = i - 1 - k >= 0 ? i - 1 - k : -1;
+        anc_s[u][3] = i < 3 ? i : 3;
     }
     __syncthreads();
-    const int m = anc_s[3];
+    // Every window load of the workgroup's nodes is issued before the first is used.
     for (int ch = threadIdx.x; ch < (2 + G) * D; ch += blockDim.x) {
         const int c = ch < D ? g * D + ch : ch < 2 * D ? Hk * D + g * D + (ch - D) : 2 * Hk * D + G * g * D + (ch - 2 * D);
-        float win[4], wf[4];
-        win[3] = widen(x[static_cast<size_t>(i) * C + c]);
+        float win[NPW][4], wf[4];
 #pragma unroll
-        for (int k = 1; k <= 3; ++k) {
-            const Act* src = (k <= m) ? x + static_cast<size_t>(anc_s[k - 1]) * C + c
-                                      : tail + static_cast<size_t>(c) * 4 + (4 + m - k);
-            win[3 - k] = widen(*src);
+        for (int u = 0; u < NPW; ++u) {
+            const int i = i0 + u < n ? i0 + u : n - 1;
+            const int m = anc_s[u][3];
+            win[u][3] = widen(x[static_cast<size_t>(i) * C + c]);
+#pragma unroll
+            for (int k = 1; k <= 3; ++k) {
+                const Act* src = (k <= m) ? x + static_cast<size_t>(anc_s[u][k - 1]) * C + c
+                                          : tail + static_cast<size_t>(c) * 4 + (4 + m - k);
+                win[u][3 - k] = widen(*src);
+            }
         }
         Quad<Act>::to_float(Quad<Act>::load(w + static_cast<size_t>(c) * 4), wf);
-        const float yv = conv_silu(wf, win);
-        if (ch < 2 * D)
-            yqk[ch] = yv;
-        else
-            ws.v[(static_cast<size_t>(m0 + i) * Hv + G * g) * D + (ch - 2 * D)] = yv;
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int i = i0 + u;
+            if (i >= n)
+                break;
+            const float yv = conv_silu(wf, win[u]);
+            if (ch < 2 * D)
+                yqk[u][ch] = yv;
+            else
+                ws.v[(static_cast<size_t>(m0 + i) * Hv + G * g) * D + (ch - 2 * D)] = yv;
+        }
     }
-    if (threadIdx.x < G) {
-        const int h = G * g + threadIdx.x;
-        float al, be;
-        gates(a[static_cast<size_t>(i) * Hv + h], b[static_cast<size_t>(i) * Hv + h], al, be);
-        ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4] = al;
-        ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4 + 1] = be;
-        ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4 + 3] = 0.0f;
+    if (threadIdx.x < NPW * G) {
+        const int u = threadIdx.x / G, i = i0 + u;
+        const int h = G * g + threadIdx.x % G;
+        if (i < n) {
+            float al, be;
+            gates(a[static_cast<size_t>(i) * Hv + h], b[static_cast<size_t>(i) * Hv + h], al, be);
+            ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4] = al;
+            ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4 + 1] = be;
+            ws.abk[(static_cast<size_t>(m0 + i) * Hv + h) * 4 + 3] = 0.0f;
+        }
     }
     __syncthreads();
-    if (threadIdx.x < kWave) {
+    // Wave u normalises node i0 + u.
+    const int u = threadIdx.x / kWave, i = i0 + u;
+    if (u < NPW && i < n) {
         constexpr int J = Prep<D>::J;
         float qv[J], kv[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int e = lane + kWave * j;
-            qv[j] = e < D ? yqk[e] : 0.0f;
-            kv[j] = e < D ? yqk[D + e] : 0.0f;
+            qv[j] = e < D ? yqk[u][e] : 0.0f;
+            kv[j] = e < D ? yqk[u][D + e] : 0.0f;
         }
         float kq;
         prep_qk<D>(qv, kv, kq);
@@ -382,6 +409,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
             ws.abk[(static_cast<size_t>(m0 + i) * Hv + G * g + lane) * 4 + 2] = kq;
     }
 }
+
 
 // The branched rows are kept per tree level below the deepest: the slot of
 // depth L holds, for every lane, its slice of the row after the most recent
@@ -631,6 +659,23 @@ static hipError_t dispatch(const Geo& g, F&& f) {
     return hipGetLastError();
 }
 
+// The prep launch (tables and node operands) of a tree, or of a block when
+// parent is null.
+template <int D, typename Act>
+static void launch_prep(const Geo& g, int n, const void* tail, const void* w, const int32_t* parent, const void* x,
+                        const float* a, const float* b, const TreeWs& W, int32_t* status, hipStream_t s) {
+    const int64_t node_wgs = static_cast<int64_t>(g.B) * n * g.Hk;
+    auto grid = [&](int npw) { return dim3(static_cast<unsigned>(g.B + g.B * g.Hk * ((n + npw - 1) / npw))); };
+    if (node_wgs > 8 * 256)   // more than eight node workgroups per CU
+        hipLaunchKernelGGL((tree_prep_kernel<D, Act, 4>), grid(4), dim3(256), 0, s, static_cast<const Act*>(tail),
+                           static_cast<const Act*>(w), n, parent, static_cast<const Act*>(x), a, b, W, status, g.B,
+                           g.Hk, g.Hv, g.C);
+    else
+        hipLaunchKernelGGL((tree_prep_kernel<D, Act, 1>), grid(1), dim3(256), 0, s, static_cast<const Act*>(tail),
+                           static_cast<const Act*>(w), n, parent, static_cast<const Act*>(x), a, b, W, status, g.B,
+                           g.Hk, g.Hv, g.C);
+}
+
 hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
                               const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                               int32_t* status, void* ws, hipStream_t s) {
@@ -638,9 +683,7 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
-        hipLaunchKernelGGL((tree_prep_kernel<D, Act>), dim3(static_cast<unsigned>(g.B + g.B * n * g.Hk)), dim3(256),
-                           0, s, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                           static_cast<const Act*>(x), a, b, W, status, g.B, g.Hk, g.Hv, g.C);
+        launch_prep<D, Act>(g, n, tail, w, parent, x, a, b, W, status, s);
     });
     if (e != hipSuccess)
         return e;
@@ -687,9 +730,7 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
-        hipLaunchKernelGGL((tree_prep_kernel<D, Act>), dim3(static_cast<unsigned>(g.B + g.B * k * g.Hk)), dim3(256),
-                           0, s, static_cast<const Act*>(tail), static_cast<const Act*>(w), k, nullptr,
-                           static_cast<const Act*>(x), a, b, W, nullptr, g.B, g.Hk, g.Hv, g.C);
+        launch_prep<D, Act>(g, k, tail, w, nullptr, x, a, b, W, nullptr, s);
     });
     if (e != hipSuccess)
         return e;

@@ -143,7 +143,9 @@ gdn_status gdn_decode_token(const gdn_dims* d, float* state, const void* conv_ta
  * node's state is branched from its parent's.  Node n's output equals, bit
  * for bit, the output of gdn_conv_update + gdn_decode_step run over the
  * root-first path to n from the sequence's checkpoint.  1 <= batch <=
- * GDN_MAX_TREE_BATCH; every tree has n_nodes nodes (a smaller tree can be
+ * GDN_MAX_TREE_BATCH and num_v_heads / num_k_heads <= 64 (GDN_ERR_SHAPE
+ * otherwise; this also holds for gdn_commit_path and the block calls); every
+ * tree has n_nodes nodes (a smaller tree can be
  * padded with extra children of its root, whose outputs the caller ignores).
  *   state_ckpt f32 [B][Hv][dv][dk]    checkpoints (read only)
  *   conv_tail  act [B][C][4]          checkpoint tails (read only)

@@ -201,3 +201,14 @@ def test_snapshot_sizes_and_refusals(lib):
         assert f(C.byref(d), S, T, 0, Q, blob, need, ST, None) == 2            # count out of range
         assert f(C.byref(d), S, T, 2, Q, P(0x10000000 + 4096), need, ST, None) == 8   # blob inside the state
         assert f(C.byref(mk(batch=65536)), S, T, 2, Q, blob, need, ST, None) == 2
+
+
+def test_tree_and_block_calls_refuse_more_than_64_value_heads_per_qk_head(lib):
+    P = C.c_void_p
+    fake = P(0x1000)
+    d = mk(num_k_heads=1, num_v_heads=128, head_k_dim=32, head_v_dim=32)
+    lib.gdn_tree_verify.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gdn_block_verify.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, C.c_size_t, P]
+    assert lib.gdn_tree_verify(C.byref(d), fake, fake, fake, 4, fake, fake, fake, fake, fake, None, fake, 1 << 30,
+                               None) == 2
+    assert lib.gdn_block_verify(C.byref(d), fake, fake, fake, 4, fake, fake, fake, fake, fake, 1 << 30, None) == 2

@@ -182,3 +182,14 @@ def test_batch64_full_size_sampled():
         ref_S = c["S"][s] if L == 0 else states[L - 1][s]
         ref_T = c["T"][s] if L == 0 else tails[L - 1][s]
         assert same_bits(S[s], ref_S) and torch.equal(T[s], ref_T), f"sequence {s}"
+
+
+def test_prep_in_groups_of_four_with_a_ragged_tail():
+    """Sixteen 13-token blocks: the prep takes four positions per workgroup, the last group
+    holding one; every position equals decode."""
+    inp = gi.decode_inputs(133, QWEN27B_LAYER, 16, 13, state_sigma=0.1, tail_random=True)
+    c = dev(inp)
+    o = verify(c, 13)
+    outs, _, _ = decode(c, 13)
+    for t in range(13):
+        assert same_bits(o[:, t], outs[t]), f"position {t}"

@@ -285,3 +285,15 @@ def test_narrow_heads_three_wave_form():
     ref = oracle.tree_verify(inp.shape, inp.state[s], inp.tail[s], inp.w, inp.extra["parent"][s], inp.x[:, s],
                              inp.a[:, s], inp.b[:, s])
     assert normwise(o[s].cpu().numpy(), ref) < TOL
+
+
+def test_prep_in_groups_of_four_nodes_with_a_ragged_tail():
+    """Eight 30-node trees: enough prep workgroups that each takes four nodes, the last
+    group of each tree holding two; every sequence equals its own batch-1 call."""
+    B, n = 8, 30
+    inp = gi.tree_batch_inputs(87, QWEN27B_LAYER, B, n_nodes=n, max_depth=8)
+    o, st = verify(batch_case(inp), B, n)
+    assert (st == 0).all()
+    for s in range(B):
+        o1, _ = verify(one_case(inp, s), 1, n)
+        assert same_bits(o[s], o1[0]), f"sequence {s}"
