@@ -16,10 +16,10 @@ import torch
 
 __all__ = [
     "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
-    "prefill_workspace_bytes", "tree_workspace_bytes", "conv_update", "decode_step", "decode_token", "tree_verify",
-    "commit_path",
-    "tree_tables", "prefill_chunked", "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH",
-    "PREFILL_CHUNK", "F32", "BF16",
+    "prefill_workspace_bytes", "tree_workspace_bytes", "block_workspace_bytes", "snapshot_bytes",
+    "conv_update", "decode_step", "decode_token", "tree_verify", "commit_path", "tree_tables",
+    "block_verify", "block_commit", "state_signature", "snapshot", "restore", "prefill_chunked",
+    "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -1,26 +1,35 @@
-// gdn_tree.hip -- tree verify and path commit.
+// gdn_tree.hip -- tree verify, path commit, and block verify / commit.
 //
 // Verify (repository "Architecture" page, decode-loop diagram: one pass over
 // the whole draft tree of up to 32 nodes; "Architecture" section 8.1: the
-// state must be branched for a tree of guesses) reads the checkpoint state
-// once and writes nothing but the per-node outputs, so rejecting the round
-// costs nothing.  Two launches:
-//   tree_prep_kernel    one workgroup per (node, q/k head): conv window over
-//                       the node's ancestors and the tail, q/k norm, gates,
-//                       into a caller-owned workspace;
+// state must be branched for a tree of guesses) reads each sequence's
+// checkpoint state once and writes nothing but the per-node outputs, so
+// rejecting the round costs nothing.  A batch holds one tree per sequence.
+// Two launches:
+//   tree_prep_kernel    one workgroup per sequence builds its tree tables
+//                       (validity, pre-order, depths); the others, one per
+//                       (sequence, q/k head, 1 or 4 nodes), compute the conv
+//                       window over each node's ancestors and the tail, the
+//                       q/k norm and the gates, into a caller-owned workspace;
 //   tree_verify_kernel  each workgroup owns a block of rows of one value head
-//                       and walks the nodes in depth-first pre-order.  A
+//                       and walks its tree in depth-first pre-order.  A
 //                       lane's slice of the current row stays in registers;
 //                       the row after each node is saved in an LDS slot per
 //                       tree level, from which a later sibling's subtree
 //                       restarts.  Node operands stream from the workspace
 //                       through a register ring several nodes ahead.
+// A block (the "Architecture" page's parts list: delta-rule kernels for one
+// token, a block and a tree) is the chain 0 -> 1 -> ... -> k-1: the same two
+// launches with no parent array, no tables to check and no saved levels;
+// committing a block prefix is the same walk writing the rows back, plus a
+// launch that appends the committed inputs to the conv tail.
 //
-// Commit replays the accepted path from the checkpoint with the same per-token
-// arithmetic as decode (gdn_core.hpp), so the committed state is bit-identical
-// to token-by-token decode of the path; the tail is rewritten by a second,
-// stream-ordered launch after every workgroup of the first has read it.
-// Commit's per-token operands are computed per workgroup into LDS.
+// Commit of a tree path replays the accepted path from the checkpoint with
+// the same per-token arithmetic as decode (gdn_core.hpp), so the committed
+// state is bit-identical to token-by-token decode of the path; the tail is
+// rewritten by a second, stream-ordered launch after every workgroup of the
+// first has read it.  Its per-token operands are computed per workgroup into
+// LDS.
 #include "gdn_core.hpp"
 #include "gdn_launch.hpp"
 #include "gdn_tree.hpp"
