@@ -575,6 +575,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         c.load_node(ring[p], p);
     float4 s[NV];
     float outv[Walk::defer_o ? kMaxNodes : 1];   // o of each walk step, stored after the walk
+    // This thread's slot of the level saved after a node of depth e is at
+    // base + (e - 1) * kLevelBytes (+ j * 4 KB for vector j).  Bases biased by
+    // the depth offsets make each access one add of the uniform d * kLevelBytes
+    // (the vector index fits the instruction's unsigned offset).
+    constexpr int kLevelBytes = NV * 256 * 16;
+    char* save_base = nullptr;     // slot of depth d is save_base + d * kLevelBytes
+    char* parent_base = nullptr;   // slot of depth d - 1 is parent_base + d * kLevelBytes
+    if constexpr (TREE) {
+        char* base = reinterpret_cast<char*>(&sm.stack[0][0][tid]);
+        save_base = base - kLevelBytes;
+        parent_base = base - 2 * kLevelBytes;
+    }
     const bool want_o = !COMMIT || o != nullptr;
     int dprev = 0;
     // One walk step per node, expanded at compile time (at most kMaxNodes),
@@ -597,7 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
                 if (LEVELS == kMaxDepth - 1 || d - 1 <= LEVELS) {
 #pragma unroll
                     for (int j = 0; j < NV; ++j)
-                        s[j] = sm.stack[d - 2][j][tid];
+                        s[j] = *reinterpret_cast<const float4*>(parent_base + d * kLevelBytes + j * 256 * 16);
                 } else {
                     // Replay the ancestors of depths LEVELS + 1 .. d - 1, each
                     // the latest position before this one with its depth.
@@ -622,7 +634,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
             if (d <= LEVELS) {
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
-                    sm.stack[d - 1][j][tid] = s[j];
+                    *reinterpret_cast<float4*>(save_base + d * kLevelBytes + j * 256 * 16) = s[j];
             }
         }
         dprev = d;
