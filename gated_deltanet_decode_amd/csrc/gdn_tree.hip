@@ -508,26 +508,24 @@ __device__ __forceinline__ void walk_all(F& f, std::integer_sequence<int, I...>)
     (void)(f(std::integral_constant<int, I>{}) && ...);
 }
 
-// Two forms of the walk.
+// Two forms of the walk.  Both store each node's output as soon as it is
+// computed, so the stores overlap the rest of the walk.
 //
 // Alone on its CU (a batch of one tree) a workgroup needs a deep operand ring
-// to hide the fetch latency, and has the LDS for every saved level.  Outputs
-// are stored after the walk, so that the waits on the ring count no stores.
+// to hide the fetch latency, and has the LDS for every saved level.
 //
-// With several trees per CU the walk is bound by VALU issue, and occupancy
-// hides the latency: four waves per SIMD (at most 128 VGPRs and 40 KB of LDS
-// per workgroup), a 3-slot ring, outputs stored as soon as they are computed.
+// With several trees per CU, occupancy hides the latency, and the walk is
+// bound by issue of the VALU and of the operand loads: four waves per SIMD
+// (at most 128 VGPRs and 40 KB of LDS per workgroup) and a 3-slot ring.
 // Saved levels are kept for depths 1 .. 5 only; a node whose parent is deeper
 // and is not the previous node replays its ancestors below depth 5 from the
 // depth-5 row, with the same operands and arithmetic, so its row is the same
 // bits.  (In random 32-node trees of depth 8 about one node in sixty does.)
 struct WalkDeep {
     static constexpr int ring = 6, levels = kMaxDepth - 1, waves = 1;
-    static constexpr bool defer_o = true;
 };
 struct WalkWide {
     static constexpr int ring = 3, levels = kMaxDepth - 3, waves = 4;
-    static constexpr bool defer_o = false;
 };
 
 // What a walk does.  Tree: verify a draft tree (saved levels, reloads).
@@ -574,7 +572,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
     for (int p = 0; p < RING; ++p)
         c.load_node(ring[p], p);
     float4 s[NV];
-    float outv[Walk::defer_o ? kMaxNodes : 1];   // o of each walk step, stored after the walk
     // This thread's slot of the level saved after a node of depth e is at
     // base + (e - 1) * kLevelBytes (+ j * 4 KB for vector j).  Bases biased by
     // the depth offsets make each access one add of the uniform d * kLevelBytes
@@ -626,9 +623,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
             }
         }
         const float out = node_update<D>(s, ring[p]);
-        if constexpr (Walk::defer_o)
-            outv[it] = out;
-        else if (want_o)
+        if (want_o)
             c.store_o(it, out);
         if constexpr (TREE) {
             if (d <= LEVELS) {
@@ -647,14 +642,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         return true;
     };
     walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
-    if constexpr (Walk::defer_o) {
-        if (want_o) {
-#pragma unroll
-            for (int it = 0; it < kMaxNodes; ++it)
-                if (it < len)
-                    c.store_o(it, outv[it]);
-        }
-    }
     if constexpr (COMMIT) {
         float* Sw = const_cast<float*>(c.Sh);
 #pragma unroll
