@@ -17,8 +17,8 @@ import torch
 __all__ = [
     "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
     "prefill_workspace_bytes", "tree_workspace_bytes", "block_workspace_bytes", "snapshot_bytes",
-    "conv_update", "decode_step", "decode_token", "tree_verify", "commit_path", "tree_tables",
-    "block_verify", "block_commit", "state_signature", "snapshot", "restore", "prefill_chunked",
+    "conv_update", "decode_step", "decode_token", "tree_verify", "tree_verify_ut", "commit_path",
+    "tree_tables", "block_verify", "block_verify_ut", "block_commit", "state_signature", "snapshot", "restore", "prefill_chunked",
     "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
 ]
 
@@ -69,11 +69,13 @@ _sig = {
     "gdn_decode_token": ([_D, _P, _P, _P, _P, _P, _P, _P, _P, _P], C.c_int),
     "gdn_tree_workspace_bytes": ([_D, _I], C.c_size_t),
     "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "gdn_tree_verify_ut": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
     "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
     "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_block_workspace_bytes": ([_D, _I], C.c_size_t),
     "gdn_block_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "gdn_block_verify_ut": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_block_commit": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_state_signature": ([_D], C.c_uint64),
     "gdn_snapshot_bytes": ([_D, _I], C.c_size_t),
@@ -171,6 +173,16 @@ def tree_workspace_bytes(d: Dims, n_nodes: int) -> int:
 def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, workspace=None, stream=None) -> None:
     """One tree of n nodes per sequence: parent [B][n]; workspace: a device byte tensor of at
     least tree_workspace_bytes(d, n) bytes; status [B] or None."""
+    _tree_verify("gdn_tree_verify", d, state, tail, w, parent, x, a, b, o, status, workspace, stream)
+
+
+def tree_verify_ut(d: Dims, state, tail, w, parent, x, a, b, o, status=None, workspace=None, stream=None) -> None:
+    """tree_verify in the UT form (one read of each checkpoint, MFMA products): the same
+    arguments; outputs equal decode's to rounding rather than bit for bit."""
+    _tree_verify("gdn_tree_verify_ut", d, state, tail, w, parent, x, a, b, o, status, workspace, stream)
+
+
+def _tree_verify(name, d, state, tail, w, parent, x, a, b, o, status, workspace, stream) -> None:
     B = d.batch
     if parent.numel() % B:
         raise ValueError("parent must be [B][n_nodes]")
@@ -182,12 +194,12 @@ def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, worksp
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < need:
         raise ValueError(f"workspace of {ws_bytes} bytes, need {need}")
-    _check(_lib.gdn_tree_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
-                                _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
-                                n, _t(parent, "parent", torch.int32, B * n), _t(x, "x", d.act_torch, B * n * Cc),
-                                _t(a, "a", torch.float32, B * n * Hv), _t(b, "b", torch.float32, B * n * Hv),
-                                _t(o, "o", torch.float32, B * n * Hv * dv), _opt(status, "tree_status", torch.int32, B),
-                                workspace.data_ptr(), ws_bytes, _stream(stream)), "gdn_tree_verify")
+    _check(getattr(_lib, name)(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
+                               _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                               n, _t(parent, "parent", torch.int32, B * n), _t(x, "x", d.act_torch, B * n * Cc),
+                               _t(a, "a", torch.float32, B * n * Hv), _t(b, "b", torch.float32, B * n * Hv),
+                               _t(o, "o", torch.float32, B * n * Hv * dv), _opt(status, "tree_status", torch.int32, B),
+                               workspace.data_ptr(), ws_bytes, _stream(stream)), name)
 
 
 def commit_path(d: Dims, state, tail, w, parent, x, a, b, path, o=None, status=None, stream=None) -> None:
@@ -227,13 +239,22 @@ def _block_common(d, x, workspace):
 
 def block_verify(d: Dims, state, tail, w, x, a, b, o, workspace, stream=None) -> None:
     """A block of k tokens per sequence: x [B][k][C], a, b [B][k][Hv], o [B][k][Hv][dv]."""
+    _block_verify("gdn_block_verify", d, state, tail, w, x, a, b, o, workspace, stream)
+
+
+def block_verify_ut(d: Dims, state, tail, w, x, a, b, o, workspace, stream=None) -> None:
+    """block_verify in the UT form: the same arguments; outputs equal decode's to rounding."""
+    _block_verify("gdn_block_verify_ut", d, state, tail, w, x, a, b, o, workspace, stream)
+
+
+def _block_verify(name, d, state, tail, w, x, a, b, o, workspace, stream) -> None:
     B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
     k, ptr, nbytes = _block_common(d, x, workspace)
-    _check(_lib.gdn_block_verify(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
-                                 _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
-                                 k, _t(x, "x", d.act_torch, B * k * Cc), _t(a, "a", torch.float32, B * k * Hv),
-                                 _t(b, "b", torch.float32, B * k * Hv), _t(o, "o", torch.float32, B * k * Hv * dv),
-                                 ptr, nbytes, _stream(stream)), "gdn_block_verify")
+    _check(getattr(_lib, name)(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
+                               _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
+                               k, _t(x, "x", d.act_torch, B * k * Cc), _t(a, "a", torch.float32, B * k * Hv),
+                               _t(b, "b", torch.float32, B * k * Hv), _t(o, "o", torch.float32, B * k * Hv * dv),
+                               ptr, nbytes, _stream(stream)), name)
 
 
 def block_commit(d: Dims, state, tail, w, x, a, b, accepted, o=None, status=None, workspace=None,

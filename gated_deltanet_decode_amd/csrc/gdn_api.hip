@@ -52,6 +52,24 @@ gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HI
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+gdn_status tree_verify_args(const gdn_dims* d, gdn::Geo& g, std::initializer_list<const void*> ptrs, int32_t n_nodes,
+                            const int32_t* tree_status, const void* workspace, size_t workspace_bytes) {
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
+        st = GDN_ERR_SHAPE;
+    if (st == GDN_OK)
+        st = ptrs_ok(ptrs);
+    if (st == GDN_OK && tree_status && !aligned16(tree_status))
+        st = GDN_ERR_ALIGN;
+    if (st == GDN_OK && (n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES))
+        st = GDN_ERR_TREE;
+    if (st != GDN_OK)
+        return st;
+    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D))
+        return GDN_ERR_WORKSPACE;
+    return aligned16(workspace) ? GDN_OK : GDN_ERR_ALIGN;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,23 +171,24 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
                            int32_t n_nodes, const int32_t* parent, const void* x, const float* a, const float* b,
                            float* o, int32_t* tree_status, void* workspace, size_t workspace_bytes, void* stream) {
     gdn::Geo g;
-    gdn_status st = check_dims(d, g);
-    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
-        st = GDN_ERR_SHAPE;
-    if (st == GDN_OK)
-        st = ptrs_ok({state_ckpt, conv_tail, conv_w, parent, x, a, b, o});
-    if (st == GDN_OK && tree_status && !aligned16(tree_status))
-        st = GDN_ERR_ALIGN;
-    if (st == GDN_OK && (n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES))
-        st = GDN_ERR_TREE;
+    const gdn_status st = tree_verify_args(d, g, {state_ckpt, conv_tail, conv_w, parent, x, a, b, o}, n_nodes,
+                                           tree_status, workspace, workspace_bytes);
     if (st != GDN_OK)
         return st;
-    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D))
-        return GDN_ERR_WORKSPACE;
-    if (!aligned16(workspace))
-        return GDN_ERR_ALIGN;
     return launched(gdn::launch_tree_verify(g, state_ckpt, conv_tail, conv_w, n_nodes, parent, x, a, b, o,
                                             tree_status, workspace, as_stream(stream)));
+}
+
+gdn_status gdn_tree_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
+                              int32_t n_nodes, const int32_t* parent, const void* x, const float* a, const float* b,
+                              float* o, int32_t* tree_status, void* workspace, size_t workspace_bytes, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = tree_verify_args(d, g, {state_ckpt, conv_tail, conv_w, parent, x, a, b, o}, n_nodes,
+                                           tree_status, workspace, workspace_bytes);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_tree_verify_ut(g, state_ckpt, conv_tail, conv_w, n_nodes, parent, x, a, b, o,
+                                               tree_status, workspace, as_stream(stream)));
 }
 
 gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w, int32_t n_nodes,
@@ -235,6 +254,18 @@ gdn_status gdn_block_verify(const gdn_dims* d, const float* state_ckpt, const vo
         return st;
     return launched(gdn::launch_block(g, false, const_cast<float*>(state_ckpt), const_cast<void*>(conv_tail),
                                       conv_w, k, x, a, b, nullptr, o, nullptr, workspace, as_stream(stream)));
+}
+
+gdn_status gdn_block_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
+                               int32_t k, const void* x, const float* a, const float* b, float* o, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = block_args(d, g, {state_ckpt, conv_tail, conv_w, x, a, b, o}, k, o, nullptr, workspace,
+                                     workspace_bytes);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_tree_verify_ut(g, state_ckpt, conv_tail, conv_w, k, nullptr, x, a, b, o, nullptr,
+                                               workspace, as_stream(stream)));
 }
 
 gdn_status gdn_block_commit(const gdn_dims* d, float* state, void* conv_tail, const void* conv_w, int32_t k,

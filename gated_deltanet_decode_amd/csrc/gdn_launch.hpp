@@ -23,6 +23,9 @@ size_t tree_ws_bytes(int B, int n, int Hk, int Hv, int D);
 hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, const void* w, int n,
                               const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                               int32_t* status, void* ws, hipStream_t s);
+hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail, const void* w, int n,
+                                 const int32_t* parent, const void* x, const float* a, const float* b, float* o,
+                                 int32_t* status, void* ws, hipStream_t s);
 hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const void* w, int k, const void* x,
                         const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
                         hipStream_t s);

@@ -709,6 +709,395 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
     });
 }
 
+// ------------------------------------------------------------ tree verify, UT form
+//
+// The same outputs as the walk, reached without building any node's state:
+// the tree counterpart of the chunked (WY/UT) form, with "ancestor of" in
+// place of "earlier in the chunk".  Per (sequence, value head), with the
+// nodes in index order (every parent before its children), j <= i meaning
+// "j is i or an ancestor of i", rho(i, j) the product of the gates alpha on
+// the path (j, i] and gamma_i the product over the whole path to i:
+//   S_i = gamma_i S_c + sum_{j <= i} rho(i, j) u_j k_j^T
+//   u_j = beta_j (v_j - gamma_j S_c k_j - sum_{l < j} rho(j, l) (k_l.k_j) u_l)
+// so (I + A) U = diag(beta) (V - diag(gamma) K S_c^T) with
+// A[j][l] = beta_j rho(j, l) (k_j.k_l) over strict ancestors l, and
+//   o_i = s (S_c q_i gamma_i + sum_{j <= i} rho(i, j) (q_i.k_j) u_j).
+// With M[i][j] = rho(i, j) (q_i.k_j) and R = M (I + A)^-1 diag(beta):
+//   o_i = s (S_c e_i + sum_l R[i][l] v_l),   e_i = gamma_i q_i - sum_l R[i][l] gamma_l k_l.
+// Every matrix above is 32 x 32 or 32 x 128, and the checkpoint enters once,
+// as the product E S_c^T: each head's checkpoint is read once and nothing is
+// written but the outputs.  The products run on fp32 MFMA (16x16x4): the
+// Gram matrices, the off-diagonal block of (I + A)^-1, R, E and R V; the
+// large one, E S_c^T, on bf16 MFMA with both operands split into two bf16
+// parts (three products, about 16 significant bits each way).  The diagonal
+// 16 x 16 blocks of (I + A)^-1 are solved by substitution.
+// The arithmetic is reordered against token-by-token decode, so the outputs
+// agree with it to rounding, not bit for bit.
+//
+// One workgroup per (sequence, value head), four waves.  Each wave's share of
+// the checkpoint (D / 4 rows; for D = 32, 16 rows shared by two waves) is
+// loaded first, in the operand layout of the final product, and stays in
+// flight while the small matrices are built.
+template <int D>
+struct UtSmem {
+    static constexpr int P = D + 8;           // bf16 row of D plus 16 bytes: a quarter-wave's reads hit distinct banks
+    static constexpr int PT = kMaxNodes + 2;  // 68-byte rows: the transposing 2-byte writes spread over 32 banks
+    static constexpr int PS = kMaxNodes + 4;  // 16-byte aligned rows of the 32 x 32 matrices
+    __bf16 kh[kMaxNodes][P], kl[kMaxNodes][P];   // k = kh + kl, each part rounded to bf16
+    __bf16 qh[kMaxNodes][P], ql[kMaxNodes][P];   // q, then e
+    __bf16 kth[D][PT], ktl[D][PT];               // k transposed
+    union {
+        float rho[kMaxNodes][PS];   // until A and M are formed
+        float rg[kMaxNodes][PS];    // R diag(gamma), after
+    };
+    float ga[kMaxNodes][PS];   // K K^T, then A
+    float gm[kMaxNodes][PS];   // Q K^T, then M
+    float t[kMaxNodes][PS];    // (I + A)^-1
+    float r[kMaxNodes][PS];    // R
+    float al[kMaxNodes], be[kMaxNodes], gam[kMaxNodes];
+    int32_t par[kMaxNodes];
+};
+
+using ut_f4 = __attribute__((ext_vector_type(4))) float;
+using ut_bf4 = __attribute__((ext_vector_type(4))) __bf16;
+using ut_bf8 = __attribute__((ext_vector_type(8))) __bf16;
+
+// x = hi + lo with hi the bf16 rounding of x and lo that of the remainder.
+__device__ __forceinline__ void ut_split(float x, __bf16& hi, __bf16& lo) {
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+template <typename V>
+__device__ __forceinline__ void ut_split_at(float x, V& hi, V& lo, int e) {
+    const __bf16 h = static_cast<__bf16>(x);
+    hi[e] = h;
+    lo[e] = static_cast<__bf16>(x - static_cast<float>(h));
+}
+__device__ __forceinline__ ut_bf8 ut_cat(const __bf16* p0, const __bf16* p1) {
+    return __builtin_shufflevector(*reinterpret_cast<const ut_bf4*>(p0), *reinterpret_cast<const ut_bf4*>(p1), 0, 1,
+                                   2, 3, 4, 5, 6, 7);
+}
+// The same from two 4-byte aligned halves (ds_read2_b32).
+__device__ __forceinline__ ut_bf8 ut_cat_a4(const __bf16* p0, const __bf16* p1) {
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(p0);
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(p1);
+    using u4 = __attribute__((ext_vector_type(4))) uint32_t;
+    const u4 w = {a[0], a[1], b[0], b[1]};
+    return __builtin_bit_cast(ut_bf8, w);
+}
+// The three-product bf16 MFMA of split operands: a.b to about 16 bits each way.
+__device__ __forceinline__ ut_f4 ut_mma3(ut_bf8 ah, ut_bf8 al, ut_bf8 bh, ut_bf8 bl, ut_f4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tree_ut_kernel(const float* __restrict__ Sc, int n,
+                                                      const int32_t* __restrict__ parent, TreeWs ws,
+                                                      float* __restrict__ o, int Hk, int Hv) {
+    static_assert(D == 32 || D == 128, "head dims 32 and 128");
+    using f4 = ut_f4;
+    using bf8 = ut_bf8;
+    constexpr int NT = kMaxNodes;                 // nodes padded to two tiles of 16
+    constexpr int RT = D >= 64 ? D / 64 : 1;      // row tiles of 16 per wave in the last product
+    constexpr int NTW = D >= 64 ? 2 : 1;          // node tiles per wave in the last product
+    constexpr int KS = D / 16;                    // 16-wide blocks of the key dim
+    constexpr int ET = D / 32;                    // tiles of e per wave
+    __shared__ UtSmem<D> sm;
+
+    const int id = xcd_packed_id(blockIdx.x, gridDim.x);
+    const int bq = id / Hv, h = id % Hv, g = h / (Hv / Hk);
+    const int m0 = bq * n;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int q = lane >> 4, c = lane & 15;
+    const int rb = D >= 64 ? wave * 16 * RT : 16 * (wave >> 1);   // first checkpoint row of this wave
+    const int u0 = D >= 64 ? 0 : (wave & 1);                      // first node tile of this wave
+
+    // Loads, all unconditional (padding nodes read node n - 1 and are zeroed
+    // after): q and k of the q/k head and the gates first, then this wave's
+    // checkpoint rows and values, which stay in flight through the small
+    // matrices.
+    constexpr int QK4 = NT * D / 2 / 256;   // float4 of q|k per thread
+    f4 qk[QK4];
+#pragma unroll
+    for (int e = 0; e < QK4; ++e) {
+        const int idx = tid + 256 * e, node = min(idx / (D / 2), n - 1), f = idx % (D / 2);
+        qk[e] = *reinterpret_cast<const f4*>(ws.qk + (static_cast<size_t>(m0 + node) * Hk + g) * 2 * D + 4 * f);
+    }
+    const int gn = min(lane & (NT - 1), n - 1);
+    const float al_in = ws.abk[(static_cast<size_t>(m0 + gn) * Hv + h) * 4];
+    const float be_in = ws.abk[(static_cast<size_t>(m0 + gn) * Hv + h) * 4 + 1];
+    // (a block has no parent array: read some valid word, keep gn - 1)
+    const int32_t pa_raw = *(parent ? parent + m0 + gn : ws.tab);
+    const int32_t pa_in = parent ? pa_raw : gn - 1;
+    const float* Sh = Sc + (static_cast<size_t>(bq) * Hv + h) * D * D;
+    f4 sv[RT][KS];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+            sv[t][k] = __builtin_nontemporal_load(
+                reinterpret_cast<const f4*>(Sh + static_cast<size_t>(rb + 16 * t + c) * D + 16 * k + 4 * q));
+    float vv[RT][8];   // slot e: node 4 q + e (e < 4), 16 + 4 q + e - 4 (e >= 4)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int node = min(e < 4 ? 4 * q + e : 12 + 4 * q + e, n - 1);
+            vv[t][e] = ws.v[(static_cast<size_t>(m0 + node) * Hv + h) * D + rb + 16 * t + c];
+        }
+
+#pragma unroll
+    for (int e = 0; e < QK4; ++e) {
+        const int idx = tid + 256 * e, node = idx / (D / 2), f = idx % (D / 2);
+        ut_bf4 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ut_split_at(node < n ? qk[e][j] : 0.0f, hi, lo, j);
+        if (f < D / 4) {
+            *reinterpret_cast<ut_bf4*>(&sm.qh[node][4 * f]) = hi;
+            *reinterpret_cast<ut_bf4*>(&sm.ql[node][4 * f]) = lo;
+        } else {
+            const int col = 4 * (f - D / 4);
+            *reinterpret_cast<ut_bf4*>(&sm.kh[node][col]) = hi;
+            *reinterpret_cast<ut_bf4*>(&sm.kl[node][col]) = lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sm.kth[col + j][node] = hi[j];
+                sm.ktl[col + j][node] = lo[j];
+            }
+        }
+    }
+    // rho and gamma, while the q/k loads are in flight: lane i of wave 0
+    // clears row i of rho and walks up from node i (the gates and parents it
+    // reads were written by lanes of the same wave, whose LDS accesses are
+    // processed in order).  A block's path is i, i - 1, ..., 0, so its gate
+    // loads do not wait on one another.
+    if (wave == 0 && lane < NT) {
+        sm.al[lane] = lane < n ? al_in : 1.0f;
+        sm.be[lane] = lane < n ? be_in : 0.0f;
+        sm.par[lane] = lane < n ? pa_in : -1;
+#pragma unroll
+        for (int l = 0; l < NT; l += 4)
+            *reinterpret_cast<f4*>(&sm.rho[lane][l]) = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        float prod = 1.0f;
+        if (parent == nullptr) {
+            if (lane >= n)
+                sm.rho[lane][lane] = 1.0f;
+            for (int l = lane < n ? lane : -1; l >= 0; --l) {
+                sm.rho[lane][l] = prod;
+                prod *= sm.al[l];
+            }
+        } else {
+            int cur = lane;
+            for (int st = 0; st < NT && cur >= 0 && cur < NT; ++st) {
+                sm.rho[lane][cur] = prod;
+                prod *= sm.al[cur];
+                cur = sm.par[cur];
+            }
+        }
+        sm.gam[lane] = prod;
+    }
+    __syncthreads();
+
+    // Every wave takes one 16x16 tile (I, J) of K K^T and of Q K^T, and forms
+    // A and M on it from the gates on the ancestor paths (rho is 0 off them).
+    // Tile (0, 1) lies above the diagonal, where neither has an entry.
+    {
+        const int I = wave >> 1, J = wave & 1;
+        f4 gk0 = {0.0f, 0.0f, 0.0f, 0.0f}, gk1 = gk0, gq0 = gk0, gq1 = gk0;
+        if (!(I == 0 && J == 1)) {
+#pragma unroll
+            for (int m = 0; m < KS / 2; ++m) {
+                const int c0 = 32 * m + 4 * q, c1 = c0 + 16;
+                const bf8 akh = ut_cat(&sm.kh[16 * I + c][c0], &sm.kh[16 * I + c][c1]);
+                const bf8 akl = ut_cat(&sm.kl[16 * I + c][c0], &sm.kl[16 * I + c][c1]);
+                const bf8 aqh = ut_cat(&sm.qh[16 * I + c][c0], &sm.qh[16 * I + c][c1]);
+                const bf8 aql = ut_cat(&sm.ql[16 * I + c][c0], &sm.ql[16 * I + c][c1]);
+                const bf8 bkh = ut_cat(&sm.kh[16 * J + c][c0], &sm.kh[16 * J + c][c1]);
+                const bf8 bkl = ut_cat(&sm.kl[16 * J + c][c0], &sm.kl[16 * J + c][c1]);
+                gk0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akh, bkh, gk0, 0, 0, 0);
+                gq0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqh, bkh, gq0, 0, 0, 0);
+                gk1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akh, bkl, gk1, 0, 0, 0);
+                gq1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqh, bkl, gq1, 0, 0, 0);
+                gk1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akl, bkh, gk1, 0, 0, 0);
+                gq1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aql, bkh, gq1, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * I + 4 * q + v, l = 16 * J + c;
+            const float r = sm.rho[i][l];
+            sm.ga[i][l] = l == i ? 0.0f : sm.be[i] * r * (gk0[v] + gk1[v]);
+            sm.gm[i][l] = r * (gq0[v] + gq1[v]);
+        }
+    }
+    __syncthreads();
+
+    // (I + A)^-1: the two diagonal 16x16 blocks by substitution (wave 0, lane =
+    // (block, column)); the block above the diagonal is 0.
+    if (wave == 0 && lane < NT) {
+        const int b0 = 16 * (lane >> 4), j = lane & 15;
+        float X[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float arow[16];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f4 a4 = *reinterpret_cast<const f4*>(&sm.ga[b0 + i][b0 + 4 * p]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    arow[4 * p + e] = a4[e];
+            }
+            float s = i == j ? 1.0f : 0.0f;
+#pragma unroll
+            for (int k = 0; k < i; ++k)
+                s = __builtin_fmaf(-arow[k], X[k], s);
+            X[i] = s;
+            sm.t[b0 + i][b0 + j] = s;
+        }
+    } else if (wave == 1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            sm.t[4 * q + v][16 + c] = 0.0f;
+    }
+    __syncthreads();
+    // the block below it: T_10 = -T_11 (A_10 T_00)
+    if (wave == 0) {
+        f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ga[16 + c][4 * q + s], sm.t[4 * q + s][c], z, 0, 0, 0);
+        f4 tt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            tt = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.t[16 + c][16 + 4 * q + s], z[s], tt, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            sm.t[16 + 4 * q + v][c] = -tt[v];
+    }
+    __syncthreads();
+
+    // R = M (I + A)^-1 diag(beta) and R diag(gamma), one 16x16 tile per wave.
+    {
+        const int I = wave >> 1, J = wave & 1;
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!(I == 0 && J == 1)) {
+#pragma unroll
+            for (int K = 0; K < 2; ++K)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.gm[16 * I + c][16 * K + 4 * q + s],
+                                                               sm.t[16 * K + 4 * q + s][16 * J + c], acc, 0, 0, 0);
+        }
+        const float bc = sm.be[16 * J + c], gc = sm.gam[16 * J + c];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float rv = acc[v] * bc;
+            sm.r[16 * I + 4 * q + v][16 * J + c] = rv;
+            sm.rg[16 * I + 4 * q + v][16 * J + c] = rv * gc;
+        }
+    }
+    __syncthreads();
+
+    // e = gamma q - (R diag(gamma)) K, written over q; and the accumulators of
+    // the last product start at R V.  Both on split bf16 MFMA with the 32
+    // nodes as k: slot e of lane (q, c) is node 4 q + e, or 16 + 4 q + e - 4.
+    auto row_split = [&](const float (*M)[UtSmem<D>::PS], int row, bf8& hi, bf8& lo) {
+        const f4 x0 = *reinterpret_cast<const f4*>(&M[row][4 * q]);
+        const f4 x1 = *reinterpret_cast<const f4*>(&M[row][16 + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ut_split_at(x0[e], hi, lo, e);
+            ut_split_at(x1[e], hi, lo, 4 + e);
+        }
+    };
+#pragma unroll
+    for (int e = 0; e < ET; ++e) {
+        const int tau = wave * ET + e, U = tau & 1, Ct = tau >> 1, col = 16 * Ct + c;
+        bf8 ah, al;
+        row_split(sm.rg, 16 * U + c, ah, al);
+        const bf8 bh = ut_cat_a4(&sm.kth[col][4 * q], &sm.kth[col][16 + 4 * q]);
+        const bf8 bl = ut_cat_a4(&sm.ktl[col][4 * q], &sm.ktl[col][16 + 4 * q]);
+        const f4 z = ut_mma3(ah, al, bh, bl, f4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * U + 4 * q + v;
+            const float qv = static_cast<float>(sm.qh[i][col]) + static_cast<float>(sm.ql[i][col]);
+            ut_split(sm.gam[i] * qv - z[v], sm.qh[i][col], sm.ql[i][col]);
+        }
+    }
+    f4 acc[RT][NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+        bf8 ah, al;
+        row_split(sm.r, 16 * (u0 + u) + c, ah, al);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            bf8 vh, vl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ut_split_at(vv[t][e] * ((e < 4 ? 4 * q + e : 12 + 4 * q + e) < n ? 1.0f : 0.0f), vh, vl, e);
+            acc[t][u] = ut_mma3(ah, al, vh, vl, f4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+    }
+    __syncthreads();
+
+    // o = s (E S_c^T + R V) over this wave's rows, E and the checkpoint rows
+    // split alike.  Lane (q, c) holds, for k-step m, the columns 32 m + 4 q +
+    // 0..3 and 32 m + 16 + 4 q + 0..3 of its row, in both operands.
+#pragma unroll
+    for (int m = 0; m < KS / 2; ++m) {
+        bf8 shi[RT], slo[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ut_split_at(sv[t][2 * m + e / 4][e % 4], shi[t], slo[t], e);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            const int row = 16 * (u0 + u) + c, c0 = 32 * m + 4 * q;
+            const bf8 ah = ut_cat(&sm.qh[row][c0], &sm.qh[row][c0 + 16]);
+            const bf8 al = ut_cat(&sm.ql[row][c0], &sm.ql[row][c0 + 16]);
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                acc[t][u] = ut_mma3(ah, al, shi[t], slo[t], acc[t][u]);
+        }
+    }
+    if (ws.tab[static_cast<size_t>(bq) * (2 * n + 1) + 2 * n] == 0)
+        return;   // malformed tree (reported by the prep): nothing is written
+#pragma unroll
+    for (int u = 0; u < NTW; ++u)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int node = 16 * (u0 + u) + 4 * q + v;
+                if (node < n)
+                    o[(static_cast<size_t>(m0 + node) * Hv + h) * D + rb + 16 * t + c] = Scale<D>::value * acc[t][u][v];
+            }
+}
+
+// The UT-form verify of a tree, or of a block when parent is null.
+hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail, const void* w, int n,
+                                 const int32_t* parent, const void* x, const float* a, const float* b, float* o,
+                                 int32_t* status, void* ws, hipStream_t s) {
+    const TreeWs W = tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D);
+    hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
+        constexpr int D = decltype(dtag)::value;
+        using Act = decltype(atag);
+        launch_prep<D, Act>(g, n, tail, w, parent, x, a, b, W, status, s);
+    });
+    if (e != hipSuccess)
+        return e;
+    return dispatch(g, [&](auto dtag, auto) {
+        constexpr int D = decltype(dtag)::value;
+        hipLaunchKernelGGL((tree_ut_kernel<D>), dim3(static_cast<unsigned>(g.B * g.Hv)), dim3(256), 0, s, S, n,
+                           parent, W, o, g.Hk, g.Hv);
+    });
+}
+
 // ------------------------------------------------------------ blocks
 
 // The tail after a block commit holds the last four raw inputs of (old tail ++

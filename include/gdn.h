@@ -172,6 +172,24 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
                            void* stream);
 
 /*
+ * gdn_tree_verify_ut -- gdn_tree_verify in the UT form, the tree counterpart
+ * of the chunked form's WY/UT representation (chunked prefill: intra-chunk
+ * WY/UT contractions, inter-chunk carry; here "ancestor of" takes the place of
+ * "earlier in the chunk").  No node's state is built: each sequence's
+ * checkpoint enters once, as one product with 32 derived query vectors per
+ * value head, and the small per-head matrices run on fp32 MFMA.  The same
+ * arguments, workspace, status and error behaviour as gdn_tree_verify; the
+ * outputs agree with token-by-token decode to rounding (within 1e-4 normwise
+ * of the sequential definition), not bit for bit.  A commit of the accepted
+ * path (gdn_commit_path) is exact either way: it replays the path.
+ */
+gdn_status gdn_tree_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
+                              const void* conv_w, int32_t n_nodes, const int32_t* parent,
+                              const void* x, const float* a, const float* b, float* o,
+                              int32_t* tree_status, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * gdn_commit_path -- commit the accepted root-first path of each sequence's
  * verified tree (decode-loop diagram: commit the accepted path's recurrent
  * state; section 8.1: exact undo).  A sequence's new (state, tail) is
@@ -248,6 +266,15 @@ size_t gdn_block_workspace_bytes(const gdn_dims* d, int32_t k);
 gdn_status gdn_block_verify(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
                             int32_t k, const void* x, const float* a, const float* b, float* o, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_block_verify_ut -- gdn_block_verify in the UT form (a block is the chain
+ * tree; see gdn_tree_verify_ut): the same arguments and errors, outputs equal
+ * to decode's to rounding.
+ */
+gdn_status gdn_block_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
+                               const void* conv_w, int32_t k, const void* x, const float* a, const float* b,
+                               float* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_block_commit -- advance each sequence by the first accepted[seq] tokens

@@ -1,0 +1,118 @@
+"""GPU tree and block verify in the UT form (gdn_tree_verify_ut, gdn_block_verify_ut).
+
+The UT form reorders the arithmetic, so it is held to the oracle's per-node
+path replay within 1e-4 normwise (per sequence, over all nodes and heads), not
+to decode bit for bit; the exact walk (gdn_tree_verify) is the second check,
+to the same bar.  Also: ragged node counts (1, 17), blocks of 1 and 32 (a
+chain of depth 32, past the trees' depth limit), a malformed tree in one
+sequence of a batch (status set, its outputs unwritten, the others verified),
+the checkpoint left untouched, and the full-size batch of 64 sampled against
+the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from gdn_inputs import QWEN27B_LAYER, TINY
+from tests.conftest import normwise
+from tests.test_gpu_tree_batch import batch_case, seq_major
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def verify(c, B, n, ut=True):
+    import gated_deltanet_decode_amd as gdn
+    d = c["d"]
+    o = torch.full((B, n, d.num_v_heads, d.head_v_dim), float("nan"), device="cuda")
+    st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gdn.tree_workspace_bytes(d, n), dtype=torch.uint8, device="cuda")
+    f = gdn.tree_verify_ut if ut else gdn.tree_verify
+    f(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"], c["b"], o, st, ws)
+    torch.cuda.synchronize()
+    return o, st.cpu().numpy()
+
+
+def oracle_tree(inp, s, parent=None):
+    parent = inp.extra["parent"][s] if parent is None else parent
+    return oracle.tree_verify(inp.shape, inp.state[s], inp.tail[s], inp.w, parent, inp.x[:, s], inp.a[:, s],
+                              inp.b[:, s])
+
+
+@pytest.mark.parametrize("shape,B,n,seed", [(QWEN27B_LAYER, 1, 32, 200), (QWEN27B_LAYER, 3, 32, 201),
+                                            (TINY, 4, 32, 202), (TINY, 2, 17, 203), (QWEN27B_LAYER, 2, 1, 204),
+                                            (TINY, 3, 9, 205)],
+                         ids=["27b_B1", "27b_B3", "tiny_B4", "tiny_n17", "27b_n1", "tiny_n9"])
+def test_ut_verify_matches_oracle(shape, B, n, seed):
+    inp = gi.tree_batch_inputs(seed, shape, B, n)
+    c = batch_case(inp)
+    S0, T0 = c["S"].clone(), c["tail"].clone()
+    o, st = verify(c, B, n)
+    assert (st == 0).all()
+    assert torch.equal(c["S"], S0) and torch.equal(c["tail"], T0), "verify wrote the checkpoint"
+    og = o.cpu().numpy()
+    for s in range(B):
+        assert normwise(og[s], oracle_tree(inp, s)) < TOL, f"sequence {s}"
+
+
+@pytest.mark.parametrize("shape", [QWEN27B_LAYER, TINY], ids=["27b", "tiny"])
+def test_ut_verify_matches_the_exact_walk(shape):
+    B, n = 4, 32
+    inp = gi.tree_batch_inputs(210, shape, B, n)
+    c = batch_case(inp)
+    o_ut, _ = verify(c, B, n)
+    o_w, _ = verify(c, B, n, ut=False)
+    for s in range(B):
+        assert normwise(o_ut[s].cpu().numpy(), o_w[s].cpu().numpy().astype(np.float64)) < TOL
+
+
+def test_malformed_tree_in_one_sequence():
+    B, n = 3, 32
+    inp = gi.tree_batch_inputs(211, QWEN27B_LAYER, B, n)
+    parent = inp.extra["parent"].copy()
+    parent[1, 7] = 9                       # a parent after its child
+    c = batch_case(inp, parent)
+    o, st = verify(c, B, n)
+    assert list(st) == [0, 5, 0]
+    assert torch.isnan(o[1]).all(), "a malformed tree's outputs were written"
+    og = o.cpu().numpy()
+    for s in (0, 2):
+        assert normwise(og[s], oracle_tree(inp, s)) < TOL
+
+
+@pytest.mark.parametrize("shape,B,k", [(QWEN27B_LAYER, 2, 32), (TINY, 3, 32), (QWEN27B_LAYER, 2, 1),
+                                       (TINY, 2, 13)], ids=["27b_k32", "tiny_k32", "27b_k1", "tiny_k13"])
+def test_ut_block_verify_matches_oracle(shape, B, k):
+    import gated_deltanet_decode_amd as gdn
+    from tests.gpu_util import act_to_dev, dims_of, f32_to_dev
+    inp = gi.decode_inputs(220 + k, shape, B, k, state_sigma=0.1, tail_random=True)
+    d = dims_of(shape, B)
+    S, T = f32_to_dev(inp.state), act_to_dev(inp.tail)
+    o = torch.full((B, k, shape.num_v_heads, shape.head_v_dim), float("nan"), device="cuda")
+    ws = torch.empty(gdn.block_workspace_bytes(d, k), dtype=torch.uint8, device="cuda")
+    gdn.block_verify_ut(d, S, T, act_to_dev(inp.w), act_to_dev(seq_major(inp.x)), f32_to_dev(seq_major(inp.a)),
+                        f32_to_dev(seq_major(inp.b)), o, ws)
+    torch.cuda.synchronize()
+    og = o.cpu().numpy()
+    for s in range(B):
+        o_r, _, _ = oracle.run(shape, inp.state[s], inp.tail[s], inp.w, inp.x[:, s], inp.a[:, s], inp.b[:, s])
+        assert normwise(og[s], o_r) < TOL, f"sequence {s}"
+
+
+def test_batch64_full_size_sampled():
+    """The 27B-class layer, 64 trees of 32 nodes (the launch the bench times): four
+    sequences against the oracle; all 64 against the exact walk."""
+    B, n = 64, 32
+    inp = gi.tree_batch_inputs(230, QWEN27B_LAYER, B, n)
+    c = batch_case(inp)
+    o, st = verify(c, B, n)
+    assert (st == 0).all()
+    og = o.cpu().numpy()
+    for s in (0, 21, 42, 63):
+        assert normwise(og[s], oracle_tree(inp, s)) < TOL, f"sequence {s}"
+    o_w, _ = verify(c, B, n, ut=False)
+    ow = o_w.cpu().numpy().astype(np.float64)
+    for s in range(B):
+        assert normwise(og[s], ow[s]) < TOL, f"sequence {s}"
