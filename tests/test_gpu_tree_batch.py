@@ -92,7 +92,10 @@ def row_len(row):
     return int(ends[0]) if len(ends) else len(row)
 
 
-@pytest.fixture(scope="module", params=[("27b", 3), ("tiny", 5)], ids=["27b_B3", "tiny_B5"])
+# Batches of 6 (27B-class) and 20 (tiny) take the prep launch with four nodes
+# per workgroup; 3 and 5 the one-node form, as batch-1 calls do.
+@pytest.fixture(scope="module", params=[("27b", 3), ("tiny", 5), ("27b", 6), ("tiny", 20)],
+                ids=["27b_B3", "tiny_B5", "27b_B6", "tiny_B20"])
 def bcase(request):
     name, B = request.param
     shape = QWEN27B_LAYER if name == "27b" else TINY
