@@ -740,20 +740,22 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
 // flight while the small matrices are built.
 template <int D>
 struct UtSmem {
-    static constexpr int P = D + 8;           // bf16 row of D plus 16 bytes: a quarter-wave's reads hit distinct banks
-    static constexpr int PT = kMaxNodes + 2;  // 68-byte rows: the transposing 2-byte writes spread over 32 banks
+    static constexpr int P = D + 4;           // bf16 row of D plus 8 bytes: a quarter-wave's reads hit distinct banks
     static constexpr int PS = kMaxNodes + 4;  // 16-byte aligned rows of the 32 x 32 matrices
     __bf16 kh[kMaxNodes][P], kl[kMaxNodes][P];   // k = kh + kl, each part rounded to bf16
     __bf16 qh[kMaxNodes][P], ql[kMaxNodes][P];   // q, then e
-    __bf16 kth[D][PT], ktl[D][PT];               // k transposed
+    // Each 32 x 32 buffer holds two matrices whose lifetimes are separated by
+    // a barrier, so that three workgroups fit in a CU's LDS.
     union {
         float rho[kMaxNodes][PS];   // until A and M are formed
-        float rg[kMaxNodes][PS];    // R diag(gamma), after
+        float t[kMaxNodes][PS];     // (I + A)^-1, after
     };
-    float ga[kMaxNodes][PS];   // K K^T, then A
-    float gm[kMaxNodes][PS];   // Q K^T, then M
-    float t[kMaxNodes][PS];    // (I + A)^-1
-    float r[kMaxNodes][PS];    // R
+    union {
+        float ga[kMaxNodes][PS];    // A, until (I + A)^-1 is complete
+        float r[kMaxNodes][PS];     // R, after
+    };
+    float gm[kMaxNodes][PS];   // M
+    float rg[kMaxNodes][PS];   // R diag(gamma)
     float al[kMaxNodes], be[kMaxNodes], gam[kMaxNodes];
     int32_t par[kMaxNodes];
 };
@@ -777,14 +779,6 @@ __device__ __forceinline__ ut_bf8 ut_cat(const __bf16* p0, const __bf16* p1) {
     return __builtin_shufflevector(*reinterpret_cast<const ut_bf4*>(p0), *reinterpret_cast<const ut_bf4*>(p1), 0, 1,
                                    2, 3, 4, 5, 6, 7);
 }
-// The same from two 4-byte aligned halves (ds_read2_b32).
-__device__ __forceinline__ ut_bf8 ut_cat_a4(const __bf16* p0, const __bf16* p1) {
-    const uint32_t* a = reinterpret_cast<const uint32_t*>(p0);
-    const uint32_t* b = reinterpret_cast<const uint32_t*>(p1);
-    using u4 = __attribute__((ext_vector_type(4))) uint32_t;
-    const u4 w = {a[0], a[1], b[0], b[1]};
-    return __builtin_bit_cast(ut_bf8, w);
-}
 // The three-product bf16 MFMA of split operands: a.b to about 16 bits each way.
 __device__ __forceinline__ ut_f4 ut_mma3(ut_bf8 ah, ut_bf8 al, ut_bf8 bh, ut_bf8 bl, ut_f4 acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
@@ -793,7 +787,7 @@ __device__ __forceinline__ ut_f4 ut_mma3(ut_bf8 ah, ut_bf8 al, ut_bf8 bh, ut_bf8
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void tree_ut_kernel(const float* __restrict__ Sc, int n,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tree_ut_kernel(const float* __restrict__ Sc, int n,
                                                       const int32_t* __restrict__ parent, TreeWs ws,
                                                       float* __restrict__ o, int Hk, int Hv) {
     static_assert(D == 32 || D == 128, "head dims 32 and 128");
@@ -862,11 +856,6 @@ __global__ __launch_bounds__(256) void tree_ut_kernel(const float* __restrict__ 
             const int col = 4 * (f - D / 4);
             *reinterpret_cast<ut_bf4*>(&sm.kh[node][col]) = hi;
             *reinterpret_cast<ut_bf4*>(&sm.kl[node][col]) = lo;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sm.kth[col + j][node] = hi[j];
-                sm.ktl[col + j][node] = lo[j];
-            }
         }
     }
     // rho and gamma, while the q/k loads are in flight: lane i of wave 0
@@ -1018,8 +1007,13 @@ __global__ __launch_bounds__(256) void tree_ut_kernel(const float* __restrict__ 
         const int tau = wave * ET + e, U = tau & 1, Ct = tau >> 1, col = 16 * Ct + c;
         bf8 ah, al;
         row_split(sm.rg, 16 * U + c, ah, al);
-        const bf8 bh = ut_cat_a4(&sm.kth[col][4 * q], &sm.kth[col][16 + 4 * q]);
-        const bf8 bl = ut_cat_a4(&sm.ktl[col][4 * q], &sm.ktl[col][16 + 4 * q]);
+        bf8 bh, bl;   // k of the slot nodes, one column: 2-byte reads down the rows
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int l = e < 4 ? 4 * q + e : 12 + 4 * q + e;
+            bh[e] = sm.kh[l][col];
+            bl[e] = sm.kl[l][col];
+        }
         const f4 z = ut_mma3(ah, al, bh, bl, f4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
