@@ -7,7 +7,8 @@ to the same bar.  Also: ragged node counts (1, 17), blocks of 1 and 32 (a
 chain of depth 32, past the trees' depth limit), a malformed tree in one
 sequence of a batch (status set, its outputs unwritten, the others verified),
 the checkpoint left untouched, and the full-size batch of 64 sampled against
-the oracle.
+the oracle.  Batches of 6 (27B-class) and 70 (tiny) also run the prep
+launch with four nodes per workgroup and two or more UT workgroups per CU.
 """
 import numpy as np
 import pytest
@@ -43,8 +44,9 @@ def oracle_tree(inp, s, parent=None):
 
 @pytest.mark.parametrize("shape,B,n,seed", [(QWEN27B_LAYER, 1, 32, 200), (QWEN27B_LAYER, 3, 32, 201),
                                             (TINY, 4, 32, 202), (TINY, 2, 17, 203), (QWEN27B_LAYER, 2, 1, 204),
-                                            (TINY, 3, 9, 205)],
-                         ids=["27b_B1", "27b_B3", "tiny_B4", "tiny_n17", "27b_n1", "tiny_n9"])
+                                            (TINY, 3, 9, 205), (QWEN27B_LAYER, 6, 32, 206), (TINY, 70, 23, 207)],
+                         ids=["27b_B1", "27b_B3", "tiny_B4", "tiny_n17", "27b_n1", "tiny_n9", "27b_B6",
+                              "tiny_B70"])
 def test_ut_verify_matches_oracle(shape, B, n, seed):
     inp = gi.tree_batch_inputs(seed, shape, B, n)
     c = batch_case(inp)
@@ -68,22 +70,24 @@ def test_ut_verify_matches_the_exact_walk(shape):
         assert normwise(o_ut[s].cpu().numpy(), o_w[s].cpu().numpy().astype(np.float64)) < TOL
 
 
-def test_malformed_tree_in_one_sequence():
-    B, n = 3, 32
+@pytest.mark.parametrize("B", [3, 6], ids=["B3", "B6"])
+def test_malformed_tree_in_one_sequence(B):
+    n = 32
     inp = gi.tree_batch_inputs(211, QWEN27B_LAYER, B, n)
     parent = inp.extra["parent"].copy()
     parent[1, 7] = 9                       # a parent after its child
     c = batch_case(inp, parent)
     o, st = verify(c, B, n)
-    assert list(st) == [0, 5, 0]
+    assert list(st) == [0, 5] + [0] * (B - 2)
     assert torch.isnan(o[1]).all(), "a malformed tree's outputs were written"
     og = o.cpu().numpy()
-    for s in (0, 2):
+    for s in [0] + list(range(2, B)):
         assert normwise(og[s], oracle_tree(inp, s)) < TOL
 
 
 @pytest.mark.parametrize("shape,B,k", [(QWEN27B_LAYER, 2, 32), (TINY, 3, 32), (QWEN27B_LAYER, 2, 1),
-                                       (TINY, 2, 13)], ids=["27b_k32", "tiny_k32", "27b_k1", "tiny_k13"])
+                                       (TINY, 2, 13), (QWEN27B_LAYER, 6, 32)],
+                         ids=["27b_k32", "tiny_k32", "27b_k1", "tiny_k13", "27b_B6_k32"])
 def test_ut_block_verify_matches_oracle(shape, B, k):
     import gated_deltanet_decode_amd as gdn
     from tests.gpu_util import act_to_dev, dims_of, f32_to_dev
