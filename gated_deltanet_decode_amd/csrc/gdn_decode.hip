@@ -59,6 +59,9 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
     constexpr int ROWS_PASS = 4 * RPW;
     constexpr int J = Prep<D>::J;
 
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together (one kernel-argument round trip).
+    asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(y), "s"(a), "s"(b), "s"(o), "s"(Hk), "s"(Hv), "s"(C));
     const int blk = blockIdx.x % blocks_per_head;
     const int bh = blockIdx.x / blocks_per_head;  // sequence * Hv + head
     const int h = bh % Hv;

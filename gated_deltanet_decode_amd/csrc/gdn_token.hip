@@ -36,8 +36,14 @@ __global__ __launch_bounds__(256) void token_kernel(float* __restrict__ S, const
     constexpr int SLOTS = (NCH + 255) / 256;         // channels per thread
     constexpr int J = Prep<D>::J;
 
-    const int blk = blockIdx.x % blocks_per_head;
-    const int bh = blockIdx.x / blocks_per_head;  // sequence * Hv + head
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together and the input loads wait for one
+    // kernel-argument round trip, not two.
+    int bph = blocks_per_head;
+    asm volatile("" : "+s"(bph) : "s"(S), "s"(tail_in), "s"(tail_out), "s"(w), "s"(x), "s"(a), "s"(b), "s"(o),
+                 "s"(Hk), "s"(Hv), "s"(C));
+    const int blk = blockIdx.x % bph;
+    const int bh = blockIdx.x / bph;  // sequence * Hv + head
     const int h = bh % Hv;
     const int seq = bh / Hv;
     const int G = Hv / Hk;

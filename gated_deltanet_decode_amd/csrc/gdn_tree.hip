@@ -277,6 +277,10 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ 
                                                         const float* __restrict__ b, TreeWs ws,
                                                         int32_t* __restrict__ status, int B, int Hk, int Hv, int C) {
     static_assert(NPW >= 1 && NPW <= 4, "one wave normalises each node of the workgroup");
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together (one kernel-argument round trip).
+    asm volatile("" : "+s"(B) : "s"(tail), "s"(w), "s"(n), "s"(parent), "s"(x), "s"(a), "s"(b), "s"(ws.qk),
+                 "s"(ws.v), "s"(ws.abk), "s"(ws.tab), "s"(status), "s"(Hk), "s"(Hv), "s"(C));
     __shared__ float yqk[NPW][2 * D];
     __shared__ int32_t anc_s[NPW][4];
     __shared__ int32_t depth_s[kMaxNodes], order_s[kMaxNodes];
@@ -545,6 +549,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
     constexpr bool TREE = KIND == WalkKind::Tree, COMMIT = KIND == WalkKind::ChainCommit;
     using Smem = std::conditional_t<TREE, VerifySmem<D, LEVELS>, NoSmem>;
     __shared__ Smem sm;
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together (one kernel-argument round trip).
+    asm volatile("" : "+s"(blocks_per_head) : "s"(Sc), "s"(n), "s"(ws.qk), "s"(ws.v), "s"(ws.abk), "s"(ws.tab), "s"(o),
+                 "s"(Hk), "s"(Hv), "s"(accepted), "s"(status));
     const VerifyCtx<D> c(Sc, n, ws, o, Hk, Hv, blocks_per_head);
     const int tid = threadIdx.x;
     float4 base[NV];
@@ -800,6 +808,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     constexpr int ET = D / 32;                    // tiles of e per wave
     __shared__ UtSmem<D> sm;
 
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together (one kernel-argument round trip).
+    asm volatile("" : "+s"(Hv) : "s"(Sc), "s"(n), "s"(parent), "s"(ws.qk), "s"(ws.v), "s"(ws.abk), "s"(ws.tab), "s"(o),
+                 "s"(Hk));
     const int id = xcd_packed_id(blockIdx.x, gridDim.x);
     const int bq = id / Hv, h = id % Hv, g = h / (Hv / Hk);
     const int m0 = bq * n;
@@ -1171,6 +1183,10 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     constexpr int ROWS = 4 * RPW;
     __shared__ NodeSmem<D, ROWS, kMaxDepth, Act> sm;
 
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together (one kernel-argument round trip).
+    asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(tail), "s"(w), "s"(n), "s"(parent), "s"(x), "s"(a), "s"(b),
+                 "s"(L), "s"(path), "s"(o), "s"(status), "s"(Hk), "s"(Hv), "s"(C));
     // Workgroups of one (sequence, q/k head) share their token inputs; they
     // are kept on one XCD.
     const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
