@@ -212,3 +212,31 @@ def test_tree_and_block_calls_refuse_more_than_64_value_heads_per_qk_head(lib):
     assert lib.gdn_tree_verify(C.byref(d), fake, fake, fake, 4, fake, fake, fake, fake, fake, None, fake, 1 << 30,
                                None) == 2
     assert lib.gdn_block_verify(C.byref(d), fake, fake, fake, 4, fake, fake, fake, fake, fake, 1 << 30, None) == 2
+
+
+def test_ut_form_calls_refuse_what_the_exact_calls_refuse(lib):
+    """gdn_tree_verify_ut and gdn_block_verify_ut share the exact calls' argument checks:
+    node counts, batch limit, workspace size, heads per q/k head, null pointers."""
+    P = C.c_void_p
+    fake = P(0x1000)
+    lib.gdn_tree_verify_ut.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gdn_block_verify_ut.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, C.c_size_t, P]
+    d = mk()
+    for n in (0, 33):
+        assert lib.gdn_tree_verify_ut(C.byref(d), fake, fake, fake, n, fake, fake, fake, fake, fake, None, fake,
+                                      1 << 30, None) == 5
+        assert lib.gdn_block_verify_ut(C.byref(d), fake, fake, fake, n, fake, fake, fake, fake, fake, 1 << 30,
+                                       None) == 2
+    big = mk(batch=65536)
+    assert lib.gdn_tree_verify_ut(C.byref(big), fake, fake, fake, 4, fake, fake, fake, fake, fake, None, fake,
+                                  1 << 40, None) == 2
+    assert lib.gdn_tree_verify_ut(C.byref(d), fake, fake, fake, 4, fake, fake, fake, fake, fake, None, fake, 1024,
+                                  None) == 6
+    assert lib.gdn_block_verify_ut(C.byref(d), fake, fake, fake, 4, fake, fake, fake, fake, fake, 1024, None) == 6
+    assert lib.gdn_tree_verify_ut(C.byref(d), None, fake, fake, 4, fake, fake, fake, fake, fake, None, fake, 1 << 30,
+                                  None) == 1
+    wide = mk(num_k_heads=1, num_v_heads=128, head_k_dim=32, head_v_dim=32)
+    assert lib.gdn_tree_verify_ut(C.byref(wide), fake, fake, fake, 4, fake, fake, fake, fake, fake, None, fake,
+                                  1 << 30, None) == 2
+    assert lib.gdn_block_verify_ut(C.byref(wide), fake, fake, fake, 4, fake, fake, fake, fake, fake, 1 << 30,
+                                   None) == 2
