@@ -734,18 +734,18 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
 //   o_i = s (S_c e_i + sum_l R[i][l] v_l),   e_i = gamma_i q_i - sum_l R[i][l] gamma_l k_l.
 // Every matrix above is 32 x 32 or 32 x 128, and the checkpoint enters once,
 // as the product E S_c^T: each head's checkpoint is read once and nothing is
-// written but the outputs.  The products run on fp32 MFMA (16x16x4): the
-// Gram matrices, the off-diagonal block of (I + A)^-1, R, E and R V; the
-// large one, E S_c^T, on bf16 MFMA with both operands split into two bf16
-// parts (three products, about 16 significant bits each way).  The diagonal
-// 16 x 16 blocks of (I + A)^-1 are solved by substitution.
+// written but the outputs.  The Gram matrices, E, R V and E S_c^T run on
+// bf16 MFMA (16x16x32) with both operands split into two bf16 parts (x = hi
+// + lo; three products, about 16 significant bits each way); the
+// off-diagonal block of (I + A)^-1 and R on fp32 MFMA (16x16x4); the
+// diagonal 16 x 16 blocks of (I + A)^-1 by substitution.
 // The arithmetic is reordered against token-by-token decode, so the outputs
 // agree with it to rounding, not bit for bit.
 //
 // One workgroup per (sequence, value head), four waves.  Each wave's share of
 // the checkpoint (D / 4 rows; for D = 32, 16 rows shared by two waves) is
-// loaded first, in the operand layout of the final product, and stays in
-// flight while the small matrices are built.
+// loaded right after the q/k rows, in the operand layout of the final
+// product, and stays in flight while the small matrices are built.
 template <int D>
 struct UtSmem {
     static constexpr int P = D + 4;           // bf16 row of D plus 8 bytes: a quarter-wave's reads hit distinct banks
