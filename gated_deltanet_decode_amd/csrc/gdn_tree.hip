@@ -271,7 +271,7 @@ static TreeWs tree_ws_carve(void* base, int B, int n, int Hk, int Hv, int D) {
 // checked, so a malformed parent array stays in bounds (the verify kernel
 // reports it and writes nothing).
 template <int D, typename Act, int NPW>
-__global__ __launch_bounds__(256) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
                                                         int n, const int32_t* __restrict__ parent,
                                                         const Act* __restrict__ x, const float* __restrict__ a,
                                                         const float* __restrict__ b, TreeWs ws,
