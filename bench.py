@@ -338,6 +338,13 @@ def main():
                                   "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt, "launch": "hipGraph"}
             if "tree_verify_n32" in res:
                 res["commit_path"]["committed_tokens_per_s"] = L / (us + res["tree_verify_n32"]["us"]) * 1e6
+            # the same commit reading the path's operands from the verify's workspace (the
+            # workspace holds the last verify's; the work per call is the same)
+            us = graph_time_us(torch, lambda r: gdn.commit_path_prepared(d1, Sp[r % R], Tp[r % R], parent, xt, path,
+                                                                          tws, None, st), nrep)
+            res["commit_path_prepared"] = {"us": us, "path_len": L, "GBps": cbt / us / 1e3,
+                                           "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt,
+                                           "launch": "hipGraph", "call": "gdn_commit_path_prepared"}
         assert st.item() == 0
         del Sp, Tp
 
@@ -378,6 +385,11 @@ def main():
         res["commit_path_b64"] = {"us": us, "accepted_tokens": sum(lens), "GBps": cbt / us / 1e3,
                                   "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt, "launch": "hipGraph",
                                   "committed_tokens_per_s": sum(lens) / (us + res["tree_verify_b64_n32"]["us"]) * 1e6}
+        us = graph_time_us(torch, lambda r: gdn.commit_path_prepared(dB, S2[r % 2], T2[r % 2], parentB, xB, pathB, wsB,
+                                                                      None, stB), 32, reps=2)
+        res["commit_path_prepared_b64"] = {"us": us, "accepted_tokens": sum(lens), "GBps": cbt / us / 1e3,
+                                           "frac_hbm": cbt / us / 1e3 / HBM_PEAK_GBS, "bytes": cbt,
+                                           "launch": "hipGraph", "call": "gdn_commit_path_prepared"}
         assert int(stB.abs().sum().item()) == 0
         del S2, T2, xB, aB, bB, oB, wsB
 

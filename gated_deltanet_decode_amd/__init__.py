@@ -18,6 +18,7 @@ __all__ = [
     "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
     "prefill_workspace_bytes", "tree_workspace_bytes", "block_workspace_bytes", "snapshot_bytes",
     "conv_update", "decode_step", "decode_token", "tree_verify", "tree_verify_ut", "commit_path",
+    "commit_path_prepared",
     "tree_tables", "block_verify", "block_verify_ut", "block_commit", "state_signature", "snapshot", "restore", "prefill_chunked",
     "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
 ]
@@ -71,6 +72,7 @@ _sig = {
     "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_tree_verify_ut": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
+    "gdn_commit_path_prepared": ([_D, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
     "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_block_workspace_bytes": ([_D, _I], C.c_size_t),
@@ -215,6 +217,27 @@ def commit_path(d: Dims, state, tail, w, parent, x, a, b, path, o=None, status=N
                                 _t(a, "a", torch.float32, B * n * Hv), _t(b, "b", torch.float32, B * n * Hv),
                                 L, _t(path, "path", torch.int32, B * L), _opt(o, "o", torch.float32, B * L * Hv * dv),
                                 _opt(status, "tree_status", torch.int32, B), _stream(stream)), "gdn_commit_path")
+
+
+def commit_path_prepared(d: Dims, state, tail, parent, x, path, workspace, o=None, status=None,
+                         stream=None) -> None:
+    """commit_path for the trees just verified with `workspace` (tree_verify or
+    tree_verify_ut on the same inputs): the path's operands are read from it."""
+    B = d.batch
+    if parent.numel() % B or path.numel() % B:
+        raise ValueError("parent must be [B][n_nodes] and path [B][path_len]")
+    n, L = parent.numel() // B, path.numel() // B
+    Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    if workspace is None or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("commit_path_prepared needs the verify's contiguous device workspace tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.gdn_commit_path_prepared(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                         _t(tail, "conv_tail", d.act_torch, B * Cc * 4), n,
+                                         _t(parent, "parent", torch.int32, B * n), _t(x, "x", d.act_torch, B * n * Cc),
+                                         L, _t(path, "path", torch.int32, B * L),
+                                         _opt(o, "o", torch.float32, B * L * Hv * dv),
+                                         _opt(status, "tree_status", torch.int32, B), workspace.data_ptr(), ws_bytes,
+                                         _stream(stream)), "gdn_commit_path_prepared")
 
 
 def tree_tables(parent, depth, order, status, stream=None) -> None:

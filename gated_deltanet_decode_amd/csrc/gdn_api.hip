@@ -208,7 +208,32 @@ gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, con
     if (st != GDN_OK)
         return st;
     return launched(gdn::launch_commit(g, state, conv_tail, conv_w, n_nodes, parent, x, a, b, path_len, path, o,
-                                       tree_status, as_stream(stream)));
+                                       tree_status, nullptr, as_stream(stream)));
+}
+
+gdn_status gdn_commit_path_prepared(const gdn_dims* d, float* state, void* conv_tail, int32_t n_nodes,
+                                    const int32_t* parent, const void* x, int32_t path_len, const int32_t* path,
+                                    float* o, int32_t* tree_status, const void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    gdn::Geo g;
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
+        st = GDN_ERR_SHAPE;
+    if (st == GDN_OK)
+        st = ptrs_ok({state, conv_tail, parent, x, path});
+    if (st == GDN_OK && ((o && !aligned16(o)) || (tree_status && !aligned16(tree_status))))
+        st = GDN_ERR_ALIGN;
+    if (st == GDN_OK && (n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES || path_len < 1 ||
+                         path_len > GDN_MAX_TREE_DEPTH || path_len > n_nodes))
+        st = GDN_ERR_TREE;
+    if (st != GDN_OK)
+        return st;
+    if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D))
+        return GDN_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return GDN_ERR_ALIGN;
+    return launched(gdn::launch_commit(g, state, conv_tail, nullptr, n_nodes, parent, x, nullptr, nullptr, path_len,
+                                       path, o, tree_status, const_cast<void*>(workspace), as_stream(stream)));
 }
 
 size_t gdn_block_workspace_bytes(const gdn_dims* d, int32_t k) {

@@ -31,7 +31,7 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
                         hipStream_t s);
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
-                         int32_t* status, hipStream_t s);
+                         int32_t* status, void* ws, hipStream_t s);
 uint64_t state_signature(const Geo& g);
 size_t snapshot_bytes(const Geo& g, int count);
 hipError_t launch_snapshot(const Geo& g, bool restore, float* S, void* tail, int count, const int32_t* seqs,

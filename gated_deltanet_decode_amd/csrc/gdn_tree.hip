@@ -1169,7 +1169,7 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
 
 // ------------------------------------------------------------ commit
 
-template <int D, typename Act>
+template <int D, typename Act, bool PREPARED>
 __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S, const Act* __restrict__ tail,
                                                            const Act* __restrict__ w, int n,
                                                            const int32_t* __restrict__ parent,
@@ -1177,7 +1177,7 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
                                                            const float* __restrict__ b, int L,
                                                            const int32_t* __restrict__ path, float* __restrict__ o,
                                                            int32_t* __restrict__ status, int Hk, int Hv, int C,
-                                                           int blocks_per_head) {
+                                                           int blocks_per_head, TreeWs ws) {
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
     constexpr int ROWS = 4 * RPW;
@@ -1235,9 +1235,7 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     __syncthreads();
     const int len = sm.len;
     const int cnt = len > 0 ? len : 1;   // tokens loaded and convolved (in bounds for the empty path)
-    FillRegs<D, ROWS, kMaxDepth, Act> fr;
-    fill_issue<D, ROWS, kMaxDepth, Act>(fr, sm, cnt, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
-    if (wave == 0) {   // validation overlaps the loads just issued
+    auto validate = [&]() {   // wave 0; overlaps the loads just issued
         bool ok = tree_tables_wave(n, parent, nullptr, nullptr);
         ok = ok && path_check_wave(n, parent, L, path);
         if (lane == 0) {
@@ -1245,8 +1243,48 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
             if (status && wid % (blocks_per_head * Hv) == 0)
                 status[bq] = ok ? 0 : 5;
         }
+    };
+    if constexpr (!PREPARED) {
+        FillRegs<D, ROWS, kMaxDepth, Act> fr;
+        fill_issue<D, ROWS, kMaxDepth, Act>(fr, sm, cnt, x, tail, w, a, b, Hk, Hv, C, grp, h, row0);
+        if (wave == 0)
+            validate();
+        fill_finish<D, ROWS, kMaxDepth, Act>(fr, sm, cnt);
+    } else {
+        // The path's operands as the verify's prep launch left them in the
+        // workspace (normalised q|k, v of this workgroup's rows, alpha, beta,
+        // k.q): every token's loads in flight at once, then into LDS.
+        constexpr int U = D / 2 + ROWS / 4 + 1;              // 16-byte units per token
+        constexpr int NL = (kMaxDepth * U + 255) / 256;      // units per thread
+        float4 un[NL];
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+            const int idx = min(static_cast<int>(threadIdx.x) + 256 * e, cnt * U - 1), i = idx / U, f = idx % U;
+            const size_t m = static_cast<size_t>(bq) * n + sm.node[i];
+            const float* src = f < D / 2 ? ws.qk + (m * Hk + grp) * 2 * D + 4 * f
+                               : f < D / 2 + ROWS / 4 ? ws.v + (m * Hv + h) * D + row0 + 4 * (f - D / 2)
+                                                      : ws.abk + (m * Hv + h) * 4;
+            un[e] = *reinterpret_cast<const float4*>(src);
+        }
+        if (wave == 0)
+            validate();
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+            const int idx = threadIdx.x + 256 * e, i = idx / U, f = idx % U;
+            if (idx < cnt * U) {
+                if (f < D / 2) {
+                    *reinterpret_cast<float4*>(&sm.qk[i][4 * f]) = un[e];
+                } else if (f < D / 2 + ROWS / 4) {
+                    *reinterpret_cast<float4*>(&sm.v[i][4 * (f - D / 2)]) = un[e];
+                } else {
+                    sm.alpha[i] = un[e].x;
+                    sm.beta[i] = un[e].y;
+                    sm.kq[i] = un[e].z;
+                }
+            }
+        }
+        __syncthreads();
     }
-    fill_finish<D, ROWS, kMaxDepth, Act>(fr, sm, cnt);
     if (!sm.ok || len == 0)
         return;
 
@@ -1310,16 +1348,24 @@ __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail
     Q::store(tail + static_cast<size_t>(c) * 4, t);
 }
 
+// With a workspace the path's operands come from the preceding verify's prep
+// launch instead of being convolved again.
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
-                         int32_t* status, hipStream_t s) {
+                         int32_t* status, void* ws, hipStream_t s) {
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
         const int bph = D / (4 * Row<D>::RPW);
-        hipLaunchKernelGGL((commit_state_kernel<D, Act>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)), dim3(256), 0,
-                           s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                           static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph);
+        if (ws == nullptr)
+            hipLaunchKernelGGL((commit_state_kernel<D, Act, false>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)),
+                               dim3(256), 0, s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                               static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph, TreeWs{});
+        else
+            hipLaunchKernelGGL((commit_state_kernel<D, Act, true>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)),
+                               dim3(256), 0, s, S, static_cast<const Act*>(tail), nullptr, n, parent,
+                               static_cast<const Act*>(x), nullptr, nullptr, L, path, o, status, g.Hk, g.Hv, g.C, bph,
+                               tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D));
     });
     if (e != hipSuccess)
         return e;

@@ -216,6 +216,26 @@ gdn_status gdn_commit_path(const gdn_dims* d, float* state, void* conv_tail, con
                            const int32_t* path, float* o, int32_t* tree_status, void* stream);
 
 /*
+ * gdn_commit_path_prepared -- gdn_commit_path for the tree just verified with
+ * this workspace (decode-loop diagram: verify, then commit the accepted
+ * path): the path's normalised q/k, v and gates are read from the workspace
+ * that gdn_tree_verify or gdn_tree_verify_ut filled for the same trees
+ * instead of being convolved again.  The caller guarantees that the
+ * workspace still holds that call's operands (same batch, n_nodes, parent, x,
+ * a, b, conv tail and weights; nothing else written to it in between);
+ * otherwise the committed state is wrong, though every access stays in
+ * bounds.  The result is bit-identical to gdn_commit_path, and so to
+ * gdn_conv_update + gdn_decode_step per path token.  Argument checks, path
+ * rows, statuses and the tail update are gdn_commit_path's.
+ *   workspace  the verify's workspace, >= gdn_tree_workspace_bytes(d, n_nodes)
+ *              bytes, 16-byte aligned (read only)
+ */
+gdn_status gdn_commit_path_prepared(const gdn_dims* d, float* state, void* conv_tail, int32_t n_nodes,
+                                    const int32_t* parent, const void* x, int32_t path_len, const int32_t* path,
+                                    float* o, int32_t* tree_status, const void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * gdn_tree_tables -- the device-side tree analysis the two calls above use,
  * exposed so its integer results can be checked exactly.
  *   depth  i32 [n_nodes] root = 1;  order i32 [n_nodes]: depth-first pre-order

@@ -240,3 +240,23 @@ def test_ut_form_calls_refuse_what_the_exact_calls_refuse(lib):
                                   1 << 30, None) == 2
     assert lib.gdn_block_verify_ut(C.byref(wide), fake, fake, fake, 4, fake, fake, fake, fake, fake, 1 << 30,
                                    None) == 2
+
+
+def test_prepared_commit_refuses_a_missing_or_short_workspace(lib):
+    P = C.c_void_p
+    fake = P(0x1000)
+    lib.gdn_commit_path_prepared.argtypes = [C.POINTER(Dims), P, P, C.c_int32, P, P, C.c_int32, P, P, P, P,
+                                             C.c_size_t, P]
+    lib.gdn_tree_workspace_bytes.restype = C.c_size_t
+    lib.gdn_tree_workspace_bytes.argtypes = [C.POINTER(Dims), C.c_int32]
+    d = mk()
+    need = lib.gdn_tree_workspace_bytes(C.byref(d), 8)
+    assert lib.gdn_commit_path_prepared(C.byref(d), fake, fake, 8, fake, fake, 3, fake, None, None, None, 0,
+                                        None) == 6
+    assert lib.gdn_commit_path_prepared(C.byref(d), fake, fake, 8, fake, fake, 3, fake, None, None, fake, need - 1,
+                                        None) == 6
+    for n, L in ((32, 9), (4, 5), (4, 0), (0, 1)):
+        assert lib.gdn_commit_path_prepared(C.byref(d), fake, fake, n, fake, fake, L, fake, None, None, fake, need,
+                                            None) == 5
+    assert lib.gdn_commit_path_prepared(C.byref(d), None, fake, 8, fake, fake, 3, fake, None, None, fake, need,
+                                        None) == 1

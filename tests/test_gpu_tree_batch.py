@@ -300,3 +300,38 @@ def test_prep_in_groups_of_four_nodes_with_a_ragged_tail():
     for s in range(B):
         o1, _ = verify(one_case(inp, s), 1, n)
         assert same_bits(o[s], o1[0]), f"sequence {s}"
+
+
+@pytest.mark.parametrize("shape,B,ut", [(QWEN27B_LAYER, 3, False), (QWEN27B_LAYER, 6, True), (TINY, 20, False),
+                                        (TINY, 4, True)],
+                         ids=["27b_B3_walk", "27b_B6_ut", "tiny_B20_walk", "tiny_B4_ut"])
+def test_prepared_commit_equals_commit_bitwise(shape, B, ut):
+    """A commit that reads the path's operands from the verify's workspace leaves the same
+    state, tail and outputs, bit for bit, as the commit that convolves them again; an empty
+    and a malformed path row behave the same way too."""
+    import gated_deltanet_decode_amd as gdn
+    from tests.gpu_util import i32_to_dev
+    n = 32
+    inp = gi.tree_batch_inputs(240 + B, shape, B, n)
+    c = batch_case(inp)
+    d = c["d"]
+    path = inp.extra["path"].copy()
+    path[1] = -1                              # the empty commit
+    if B > 2:
+        path[2, 1] = 31 if inp.extra["parent"][2][31] != path[2, 0] else 30   # not a child of path[0]
+    o = torch.empty(B, n, d.num_v_heads, d.head_v_dim, device="cuda")
+    st = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gdn.tree_workspace_bytes(d, n), dtype=torch.uint8, device="cuda")
+    (gdn.tree_verify_ut if ut else gdn.tree_verify)(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"],
+                                                    c["b"], o, st, ws)
+    L = path.shape[1]
+    S1, T1 = c["S"].clone(), c["tail"].clone()
+    o1 = torch.full((B, L, d.num_v_heads, d.head_v_dim), float("nan"), device="cuda")
+    st1 = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    gdn.commit_path_prepared(d, S1, T1, c["parent"], c["x"], i32_to_dev(path), ws, o1, st1)
+    o2, S2, T2, st2 = commit(c, B, path)
+    torch.cuda.synchronize()
+    assert list(st1.cpu().numpy()) == list(st2)
+    assert same_bits(S1, S2) and torch.equal(T1, T2)
+    assert torch.equal(torch.isnan(o1), torch.isnan(o2))
+    assert same_bits(torch.nan_to_num(o1), torch.nan_to_num(o2))
