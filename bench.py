@@ -430,6 +430,12 @@ def main():
                 res[f"block_commit_b{B}_k{kb}"] = {"us": us, "accepted_tokens": int(acc_np.sum()), "GBps": cb / us / 1e3,
                                                    "frac_hbm": cb / us / 1e3 / HBM_PEAK_GBS, "bytes": cb,
                                                    "launch": "hipGraph"}
+                us = graph_time_us(torch, lambda r: gdn.block_commit_prepared(dB, Sb[r % nbuf], Tb[r % nbuf], xB, acc, wsB,
+                                                                               None, stB), n, reps=2)
+                res[f"block_commit_prepared_b{B}_k{kb}"] = {"us": us, "accepted_tokens": int(acc_np.sum()),
+                                                            "GBps": cb / us / 1e3,
+                                                            "frac_hbm": cb / us / 1e3 / HBM_PEAK_GBS, "bytes": cb,
+                                                            "launch": "hipGraph", "call": "gdn_block_commit_prepared"}
                 assert int(stB.abs().sum().item()) == 0
             del Sb, Tb, xB, aB, bB, oB, wsB
 

@@ -19,7 +19,7 @@ __all__ = [
     "prefill_workspace_bytes", "tree_workspace_bytes", "block_workspace_bytes", "snapshot_bytes",
     "conv_update", "decode_step", "decode_token", "tree_verify", "tree_verify_ut", "commit_path",
     "commit_path_prepared",
-    "tree_tables", "block_verify", "block_verify_ut", "block_commit", "state_signature", "snapshot", "restore", "prefill_chunked",
+    "tree_tables", "block_verify", "block_verify_ut", "block_commit", "block_commit_prepared", "state_signature", "snapshot", "restore", "prefill_chunked",
     "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
 ]
 
@@ -72,6 +72,7 @@ _sig = {
     "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_tree_verify_ut": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_commit_path": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P], C.c_int),
+    "gdn_block_commit_prepared": ([_D, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_commit_path_prepared": ([_D, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_tree_tables": ([_I, _P, _P, _P, _P, _P], C.c_int),
     "gdn_prefill_chunked": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
@@ -291,6 +292,19 @@ def block_commit(d: Dims, state, tail, w, x, a, b, accepted, o=None, status=None
                                  _t(b, "b", torch.float32, B * k * Hv), _t(accepted, "accepted", torch.int32, B),
                                  _opt(o, "o", torch.float32, B * k * Hv * dv), _opt(status, "status", torch.int32, B),
                                  ptr, nbytes, _stream(stream)), "gdn_block_commit")
+
+
+def block_commit_prepared(d: Dims, state, tail, x, accepted, workspace, o=None, status=None, stream=None) -> None:
+    """block_commit for the blocks just verified with `workspace` (block_verify or
+    block_verify_ut on the same inputs): the operands are read from it."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    k, ptr, nbytes = _block_common(d, x, workspace)
+    _check(_lib.gdn_block_commit_prepared(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                          _t(tail, "conv_tail", d.act_torch, B * Cc * 4), k,
+                                          _t(x, "x", d.act_torch, B * k * Cc), _t(accepted, "accepted", torch.int32, B),
+                                          _opt(o, "o", torch.float32, B * k * Hv * dv),
+                                          _opt(status, "status", torch.int32, B), ptr, nbytes, _stream(stream)),
+           "gdn_block_commit_prepared")
 
 
 def state_signature(d: Dims) -> int:

@@ -278,7 +278,8 @@ gdn_status gdn_block_verify(const gdn_dims* d, const float* state_ckpt, const vo
     if (st != GDN_OK)
         return st;
     return launched(gdn::launch_block(g, false, const_cast<float*>(state_ckpt), const_cast<void*>(conv_tail),
-                                      conv_w, k, x, a, b, nullptr, o, nullptr, workspace, as_stream(stream)));
+                                      conv_w, k, x, a, b, nullptr, o, nullptr, workspace, false,
+                                      as_stream(stream)));
 }
 
 gdn_status gdn_block_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail, const void* conv_w,
@@ -302,7 +303,18 @@ gdn_status gdn_block_commit(const gdn_dims* d, float* state, void* conv_tail, co
     if (st != GDN_OK)
         return st;
     return launched(gdn::launch_block(g, true, state, conv_tail, conv_w, k, x, a, b, accepted, o, status, workspace,
-                                      as_stream(stream)));
+                                      false, as_stream(stream)));
+}
+
+gdn_status gdn_block_commit_prepared(const gdn_dims* d, float* state, void* conv_tail, int32_t k, const void* x,
+                                     const int32_t* accepted, float* o, int32_t* status, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    gdn::Geo g;
+    const gdn_status st = block_args(d, g, {state, conv_tail, x, accepted}, k, o, status, workspace, workspace_bytes);
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_block(g, true, state, conv_tail, nullptr, k, x, nullptr, nullptr, accepted, o, status,
+                                      workspace, true, as_stream(stream)));
 }
 
 uint64_t gdn_state_signature(const gdn_dims* d) {

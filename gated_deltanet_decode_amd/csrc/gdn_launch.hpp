@@ -28,7 +28,7 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
                                  int32_t* status, void* ws, hipStream_t s);
 hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const void* w, int k, const void* x,
                         const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
-                        hipStream_t s);
+                        bool prepared, hipStream_t s);
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
                          int32_t* status, void* ws, hipStream_t s);

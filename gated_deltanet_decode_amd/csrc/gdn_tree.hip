@@ -1126,11 +1126,13 @@ __global__ __launch_bounds__(256) void block_tail_kernel(Act* __restrict__ tail,
     Q::store(tc, t);
 }
 
+// prepared: the workspace already holds the block's operands (from the
+// verify of the same block), so the prep launch is skipped.
 hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const void* w, int k, const void* x,
                         const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
-                        hipStream_t s) {
+                        bool prepared, hipStream_t s) {
     const TreeWs W = tree_ws_carve(ws, g.B, k, g.Hk, g.Hv, g.D);
-    hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
+    hipError_t e = prepared ? hipSuccess : dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
         launch_prep<D, Act>(g, k, tail, w, nullptr, x, a, b, W, nullptr, s);

@@ -313,6 +313,21 @@ gdn_status gdn_block_commit(const gdn_dims* d, float* state, void* conv_tail, co
                             int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_block_commit_prepared -- gdn_block_commit for the blocks just verified
+ * with this workspace (gdn_block_verify or gdn_block_verify_ut on the same
+ * inputs): the positions' normalised q/k, v and gates are read from the
+ * workspace instead of being prepared again.  The caller guarantees that the
+ * workspace still holds that call's operands; otherwise the committed state
+ * is wrong, though every access stays in bounds.  The result is
+ * bit-identical to gdn_block_commit; arguments, counts, statuses and the tail
+ * update are its.
+ *   workspace  the verify's workspace, >= gdn_block_workspace_bytes(d, k) bytes
+ */
+gdn_status gdn_block_commit_prepared(const gdn_dims* d, float* state, void* conv_tail, int32_t k, const void* x,
+                                     const int32_t* accepted, float* o, int32_t* status, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * State snapshots (repository "Architecture" page: the engine must restore a
  * recurrent state exactly from a cache, which copies a sequence's state as
  * sections in a fixed order; a signature over the sections' names, shapes and

@@ -260,3 +260,15 @@ def test_prepared_commit_refuses_a_missing_or_short_workspace(lib):
                                             None) == 5
     assert lib.gdn_commit_path_prepared(C.byref(d), None, fake, 8, fake, fake, 3, fake, None, None, fake, need,
                                         None) == 1
+
+
+def test_prepared_block_commit_refuses_what_block_commit_refuses(lib):
+    P = C.c_void_p
+    fake = P(0x1000)
+    lib.gdn_block_commit_prepared.argtypes = [C.POINTER(Dims), P, P, C.c_int32, P, P, P, P, P, C.c_size_t, P]
+    d = mk()
+    for k in (0, 33):
+        assert lib.gdn_block_commit_prepared(C.byref(d), fake, fake, k, fake, fake, None, None, fake, 1 << 30,
+                                             None) == 2
+    assert lib.gdn_block_commit_prepared(C.byref(d), fake, fake, 4, fake, fake, None, None, fake, 1024, None) == 6
+    assert lib.gdn_block_commit_prepared(C.byref(d), fake, fake, 4, None, fake, None, None, fake, 1 << 30, None) == 1

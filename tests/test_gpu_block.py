@@ -193,3 +193,30 @@ def test_prep_in_groups_of_four_with_a_ragged_tail():
     outs, _, _ = decode(c, 13)
     for t in range(13):
         assert same_bits(o[:, t], outs[t]), f"position {t}"
+
+
+@pytest.mark.parametrize("shape,B,k,ut", [(QWEN27B_LAYER, 3, 12, False), (QWEN27B_LAYER, 16, 13, True),
+                                          (TINY, 5, 32, True)], ids=["27b_B3_walk", "27b_B16_ut", "tiny_B5_ut"])
+def test_prepared_block_commit_equals_block_commit_bitwise(shape, B, k, ut):
+    """A block commit that reads the operands from the verify's workspace leaves the same
+    state, tail, outputs and statuses, bit for bit, as the one that prepares them again
+    (counts of 0, k and out of range included)."""
+    import gated_deltanet_decode_amd as gdn
+    from tests.gpu_util import i32_to_dev
+    inp = gi.decode_inputs(150 + B, shape, B, k, state_sigma=0.1, tail_random=True)
+    c = dev(inp)
+    d = c["d"]
+    ws = torch.empty(gdn.block_workspace_bytes(d, k), dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, k, d.num_v_heads, d.head_v_dim, device="cuda")
+    (gdn.block_verify_ut if ut else gdn.block_verify)(d, c["S"], c["T"], c["w"], c["x"], c["a"], c["b"], o, ws)
+    accepted = [(5 * s + 2) % (k + 1) for s in range(B)]
+    accepted[0], accepted[-1] = k, k + 3
+    S1, T1 = c["S"].clone(), c["T"].clone()
+    o1 = torch.full((B, k, d.num_v_heads, d.head_v_dim), float("nan"), device="cuda")
+    st1 = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    gdn.block_commit_prepared(d, S1, T1, c["x"], i32_to_dev(np.array(accepted, np.int32)), ws, o1, st1)
+    o2, S2, T2, st2 = commit(c, k, accepted)
+    assert list(st1.cpu().numpy()) == list(st2)
+    assert same_bits(S1, S2) and torch.equal(T1, T2)
+    assert torch.equal(torch.isnan(o1), torch.isnan(o2))
+    assert same_bits(torch.nan_to_num(o1), torch.nan_to_num(o2))
