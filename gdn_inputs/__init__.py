@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "LayerShape", "TINY", "QWEN27B_LAYER", "normal_rows", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "random_tree", "random_leaf_path", "tree_depths",
-    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "Inputs",
+    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "Inputs", "GATE_REGIMES",
 ]
 
 BF16 = "bf16"
@@ -175,12 +175,36 @@ class Inputs:
     extra: dict = field(default_factory=dict)
 
 
-def _common(seed, shape, batch, steps, state_sigma, tail_random):
+# Gate regimes: the means of the gate inputs a and b (each drawn as mean + N(0,1)).
+# The pages' workloads draw both from N(0,1) ("normal": median alpha = beta = 1/2,
+# so the state forgets within a few tokens); the others push each gate to an end
+# of its range, where chunked and tree forms round differently from token order:
+#   long_memory   a ~ N(-6,1): alpha close to 1, the state remembers for thousands of tokens
+#   strong_decay  a ~ N(+6,1): alpha close to 0, products of gates underflow within a chunk
+#   beta_one      b ~ N(+6,1): beta close to 1, each key's old value is fully replaced
+#   beta_zero     b ~ N(-6,1): beta close to 0, writes almost vanish
+#   long_beta_one long memory and beta close to 1 together
+GATE_REGIMES = {
+    "normal": (0.0, 0.0),
+    "long_memory": (-6.0, 0.0),
+    "strong_decay": (6.0, 0.0),
+    "beta_one": (0.0, 6.0),
+    "beta_zero": (0.0, -6.0),
+    "long_beta_one": (-6.0, 6.0),
+}
+
+
+def _common(seed, shape, batch, steps, state_sigma, tail_random, gates="normal"):
     C, W = shape.conv_channels, shape.conv_width
     Hv, dk, dv = shape.num_v_heads, shape.head_k_dim, shape.head_v_dim
+    a_mean, b_mean = GATE_REGIMES[gates]
     x = _act(normal_rows(seed, S_X, steps * batch, C), shape.act).reshape(steps, batch, C)
     a = normal_rows(seed, S_A, steps * batch, Hv).reshape(steps, batch, Hv)
     b = normal_rows(seed, S_B, steps * batch, Hv).reshape(steps, batch, Hv)
+    if a_mean:
+        a += np.float32(a_mean)
+    if b_mean:
+        b += np.float32(b_mean)
     w = _act(normal_rows(seed, S_W, C, W, sigma=0.5), shape.act)
     if state_sigma:
         state = normal_rows(seed, S_STATE, batch * Hv * dv, dk, sigma=state_sigma).reshape(batch, Hv, dv, dk)
@@ -194,17 +218,18 @@ def _common(seed, shape, batch, steps, state_sigma, tail_random):
 
 
 def decode_inputs(seed: int, shape: LayerShape, batch: int, steps: int,
-                  state_sigma: float = 0.1, tail_random: bool = True) -> Inputs:
+                  state_sigma: float = 0.1, tail_random: bool = True, gates: str = "normal") -> Inputs:
     """Chained decode: `steps` tokens per sequence, q|k|v raw activations ~ N(0,1),
-    gate inputs a, b ~ N(0,1), conv weights ~ N(0, 0.5^2), state ~ N(0, state_sigma^2)."""
-    x, a, b, w, state, tail = _common(seed, shape, batch, steps, state_sigma, tail_random)
+    gate inputs a, b ~ N(0,1) shifted per the gate regime, conv weights ~ N(0, 0.5^2),
+    state ~ N(0, state_sigma^2)."""
+    x, a, b, w, state, tail = _common(seed, shape, batch, steps, state_sigma, tail_random, gates)
     return Inputs(shape, batch, steps, x, a, b, w, state, tail)
 
 
 def tree_inputs(seed: int, shape: LayerShape, n_nodes: int = 32, max_depth: int = 8,
-                state_sigma: float = 0.1, tail_random: bool = True) -> Inputs:
+                state_sigma: float = 0.1, tail_random: bool = True, gates: str = "normal") -> Inputs:
     """One draft tree of n_nodes over a batch-1 checkpoint; x/a/b hold one row per node."""
-    x, a, b, w, state, tail = _common(seed, shape, 1, n_nodes, state_sigma, tail_random)
+    x, a, b, w, state, tail = _common(seed, shape, 1, n_nodes, state_sigma, tail_random, gates)
     rng = _gen(seed, S_TREE, 0)
     parent = random_tree(rng, n_nodes, max_depth)
     path = random_leaf_path(rng, parent)
@@ -213,13 +238,13 @@ def tree_inputs(seed: int, shape: LayerShape, n_nodes: int = 32, max_depth: int 
 
 
 def tree_batch_inputs(seed: int, shape: LayerShape, batch: int, n_nodes: int = 32, max_depth: int = 8,
-                      state_sigma: float = 0.1, tail_random: bool = True) -> Inputs:
+                      state_sigma: float = 0.1, tail_random: bool = True, gates: str = "normal") -> Inputs:
     """One draft tree of n_nodes per sequence over `batch` checkpoints; x/a/b hold one row
     per (node, sequence), [n_nodes][batch][...].  extra["parent"] is [batch][n_nodes] (an
     independent tree per sequence); extra["path"] is [batch][max_depth]: per row a
     root-first prefix of the path to a uniformly chosen leaf, of uniform length between 1
     and that path's length, padded with -1."""
-    x, a, b, w, state, tail = _common(seed, shape, batch, n_nodes, state_sigma, tail_random)
+    x, a, b, w, state, tail = _common(seed, shape, batch, n_nodes, state_sigma, tail_random, gates)
     parent = np.empty((batch, n_nodes), dtype=np.int32)
     path = np.full((batch, max_depth), -1, dtype=np.int32)
     for s in range(batch):
@@ -233,7 +258,7 @@ def tree_batch_inputs(seed: int, shape: LayerShape, batch: int, n_nodes: int = 3
 
 
 def prefill_inputs(seed: int, shape: LayerShape, T: int, batch: int = 1,
-                   state_sigma: float = 0.0, tail_random: bool = False) -> Inputs:
+                   state_sigma: float = 0.0, tail_random: bool = False, gates: str = "normal") -> Inputs:
     """A prompt of T tokens; by default from a fresh (zero) state and zero conv tail."""
-    x, a, b, w, state, tail = _common(seed, shape, batch, T, state_sigma, tail_random)
+    x, a, b, w, state, tail = _common(seed, shape, batch, T, state_sigma, tail_random, gates)
     return Inputs(shape, batch, T, x, a, b, w, state, tail)

@@ -128,6 +128,41 @@ def run(shape, state, tail, w, x, a, b, h_range=None, rows=None, want_o=True):
     return o, S, t
 
 
+def run_parallel(shape, state, tail, w, x, a, b, want_o=True, threads=None):
+    """run() over all value heads, split by q/k head group over host threads.
+
+    The heads are independent (each keeps its own token order), so every
+    thread runs the unchanged oracle on its own head range, into disjoint
+    slices of one state and output array; each thread shifts a private copy
+    of the tail, which all end equal.  Returns what run() returns."""
+    import concurrent.futures as fut
+    Hk, Hv, dk, dv, W = shape.num_k_heads, shape.num_v_heads, shape.head_k_dim, shape.head_v_dim, shape.conv_width
+    G = Hv // Hk
+    S = f64(state)
+    t0 = f64(tail)
+    w, wb = _act(w)
+    x, xb = _act(x)
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    T = x.shape[0] if x.ndim == 2 else x.size // shape.conv_channels
+    o = np.zeros((T, Hv, dv), dtype=np.float64) if want_o else None
+    n = max(1, min(Hk, threads or os.cpu_count() or 1))
+    bounds = [(Hk * i // n * G, Hk * (i + 1) // n * G) for i in range(n)]
+    tails = [t0.copy() for _ in bounds]
+
+    def one(i):
+        lo, hi = bounds[i]
+        return lib().oracle_run(Hk, Hv, dk, dv, W, _p(S), _p(tails[i]), _p(w), wb, T, _p(x), xb, None,
+                                _p(a), _p(b), _p(o), lo, hi)
+
+    with fut.ThreadPoolExecutor(max_workers=n) as ex:
+        for rc in ex.map(one, range(n)):
+            _check(rc, "oracle_run")
+    for t in tails[1:]:
+        assert np.array_equal(t, tails[0])
+    return o, S, tails[0]
+
+
 def recur(shape, state, y, a, b):
     """One token of the recurrence from a conv output y[C]; returns (o [Hv][dv], S)."""
     Hk, Hv, dk, dv = shape.num_k_heads, shape.num_v_heads, shape.head_k_dim, shape.head_v_dim

@@ -95,29 +95,31 @@ def test_crosses_segment_boundary():
 
 
 def test_27b_layer_32768_tokens():
-    """The long-prompt workload: T = 32,768 from a fresh state.  o is checked on the
-    first 2,048 tokens for every head; the final state for q/k heads 0 and 9
-    (value heads 0-2 and 27-29) against the oracle over all 32,768 tokens."""
+    """The long-prompt workload: T = 32,768 from a fresh state.  o on the first
+    2,048 tokens and the whole final state (all 48 value heads) and tail against
+    the oracle over all 32,768 tokens (the oracle's heads split over host
+    threads; each keeps its token order)."""
     from tests.gpu_util import act_to_host
     T = 32768
     inp = gi.prefill_inputs(4, QWEN27B_LAYER, T)
     o, S, tail = gpu_prefill(inp)
     og = o[0, :2048].cpu().numpy()
+    assert torch.isfinite(o).all()
+    del o
     Sg = S.cpu().numpy()[0]
     tg = act_to_host(tail)[0]
-    o_r, _, _ = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:2048, 0], inp.a[:2048, 0],
-                           inp.b[:2048, 0])
+    o_r, _, _ = oracle.run_parallel(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:2048, 0],
+                                    inp.a[:2048, 0], inp.b[:2048, 0], threads=16)
     err = normwise(og, o_r)
     print(f"[prefill parity] T=32768: o[0:2048] error {err:.3e}")
     assert err < TOL, f"o[0:2048] error {err:.3e}"
-    for hr in ((0, 3), (27, 30)):
-        _, S_r, t_r = oracle.run(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:, 0], inp.a[:, 0],
-                                 inp.b[:, 0], h_range=hr, want_o=False)
-        err = normwise(Sg[hr[0]:hr[1]], S_r[hr[0]:hr[1]])
-        print(f"[prefill parity] T=32768: final state heads {hr} error {err:.3e}")
-        assert err < TOL, f"final state heads {hr}: error {err:.3e}"
-        assert np.array_equal(oracle.f64(tg), t_r)
-    assert torch.isfinite(o).all()
+    _, S_r, t_r = oracle.run_parallel(QWEN27B_LAYER, inp.state[0], inp.tail[0], inp.w, inp.x[:, 0], inp.a[:, 0],
+                                      inp.b[:, 0], want_o=False, threads=16)
+    err = normwise(Sg, S_r)
+    worst_head = max(range(48), key=lambda h: normwise(Sg[h], S_r[h]))
+    print(f"[prefill parity] T=32768: final state (48 heads) error {err:.3e}, worst head {worst_head}")
+    assert err < TOL, f"final state error {err:.3e}"
+    assert np.array_equal(oracle.f64(tg), t_r)
 
 
 @pytest.mark.parametrize("split", [64, 128, 2048])
