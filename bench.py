@@ -142,6 +142,22 @@ def graph_time_us(torch, fn, n, reps=4):
     return tm.ms * 1e3 / (reps * n)
 
 
+def cold_graph_ms(torch, fn, n, evict):
+    """Capture fn(0..n-1) into one hip graph, replay it twice untimed, evict the caches
+    with evict(), then time one replay on the current stream; milliseconds."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    g.replay()
+    evict()
+    with Timer(torch) as tm:
+        g.replay()
+    del g
+    return tm.ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,8 +232,16 @@ def main():
     dec_b, conv_b = step_bytes(1, shape)
 
     # ---------------------------------------------------------------- headline: cold, eager launches
+    evict_src = torch.empty(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
+    evict_dst = torch.empty_like(evict_src)
+
+    def evict():
+        """Push every earlier state out of the 256 MB Infinity Cache (outside any timed region)."""
+        evict_dst.copy_(evict_src)
+
     for t in range(W):
         step(t, t % R)
+    evict()
     with Timer(torch) as tm:
         for t in range(W, W + K):
             step(t, t % R)
@@ -226,18 +250,28 @@ def main():
                                    "tokens_per_s": K / cold_ms * 1e3}
 
     # ---------------------------------------------------------------- same steps under a hip graph
-    # 2R steps per graph: every state advances twice per replay, so its tail
-    # parity is the same at every replay boundary.
+    # One graph of exactly the K timed steps, step t on state t % R.  It is
+    # replayed twice untimed (an even number, so every state's tail is back in
+    # the buffer the captured steps read first), then the 256 MB Infinity Cache
+    # is evicted by a 1 GiB device copy, and one replay is timed: every state
+    # the timed steps touch is read from HBM.
     graph_ms = None
     if "graph" in rows:
-        chunk = min(K, 2 * R)
-        us = graph_time_us(torch, lambda t: step(W + t % K, t % R), chunk, reps=max(1, K // chunk))
-        graph_ms = us * K / 1e3
-        res["decode_b1_cold_graph"] = {"ms_per_step": us / 1e3, "GBps": per_step / us / 1e3,
-                                       "tokens_per_s": 1e6 / us, "graph_steps": chunk}
-        us2 = graph_time_us(torch, lambda t: step_two_calls(W + t % K, t % R), chunk, reps=max(1, K // chunk))
+        ms = cold_graph_ms(torch, lambda t: step(W + t, t % R), K, evict)
+        graph_ms = ms
+        res["decode_b1_cold_graph"] = {"ms_per_step": ms / K, "GBps": per_step * K / ms / 1e6,
+                                       "tokens_per_s": K / ms * 1e3, "graph_steps": K,
+                                       "distinct_states": min(K, R)}
+        # The same steps rotated over all R states twice (2R steps), whatever K is.
+        ms2 = cold_graph_ms(torch, lambda t: step(W + t % K, t % R), 2 * R, evict)
+        res["decode_b1_cold_graph_all_states"] = {"ms_per_step": ms2 / (2 * R), "GBps": per_step * 2 * R / ms2 / 1e6,
+                                                  "tokens_per_s": 2 * R / ms2 * 1e3, "graph_steps": 2 * R,
+                                                  "distinct_states": R,
+                                                  "states_bytes": R * Hv * D * D * 4}
+        us2 = graph_time_us(torch, lambda t: step_two_calls(W + t % K, t % R), 2 * R, reps=2)
         res["decode_b1_two_calls_graph"] = {"ms_per_step": us2 / 1e3, "GBps": (dec_b + conv_b) / us2 / 1e3,
-                                            "tokens_per_s": 1e6 / us2, "calls": "gdn_conv_update + gdn_decode_step"}
+                                            "tokens_per_s": 1e6 / us2, "calls": "gdn_conv_update + gdn_decode_step",
+                                            "graph_steps": 2 * R}
 
     # ---------------------------------------------------------------- the state-step kernel alone
     if "kernel" in rows:
@@ -501,26 +535,48 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- CPU oracle on a bounded sample
+    # The oracle (fp64 scalar C, unchanged) runs chained batch-1 decode steps of
+    # the same layer, all 48 heads, cycling over the drawn tokens: first on one
+    # host core (this thread pinned to one CPU), then on every core the process
+    # may use, its heads split by q/k head group over threads (each head keeps
+    # its own token order, so the results are the same numbers).
     cpu = None
     if "cpu" in rows:
         import oracle
         oracle.build(force=False)
-        budget_s = 12.0
-        tok = 0
-        S0 = inp.state[0]
-        tail0 = inp.tail[0]
-        t0 = time.time()
-        chunk = 8
-        while time.time() - t0 < budget_s:
-            j = tok % (steps_total - steps_total % chunk)   # chained steps, cycling over the drawn tokens
-            _, S0, tail0 = oracle.run(shape, S0, tail0, inp.w, inp.x[j:j + chunk, 0], inp.a[j:j + chunk, 0],
-                                      inp.b[j:j + chunk, 0])
-            tok += chunk
-        el = time.time() - t0
-        cpu = {"value": per_step * tok / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{tok} chained decode steps of the batch-1 27B-class layer (all 48 heads, fp64 "
-                         f"scalar C, cycling over the {steps_total} drawn tokens), {el:.1f} s on one host core; "
-                         f"tokens/s {tok / el:.1f}"}
+        cpus = sorted(os.sched_getaffinity(0))
+        host = {"nproc": len(cpus), "cpu_model": _cpu_model(), "oracle_cflags": " ".join(oracle.CFLAGS),
+                "compiler": _gcc_version()}
+
+        def leg(budget_s, threads):
+            tok, S0, tail0 = 0, inp.state[0], inp.tail[0]
+            chunk = 8 if threads == 1 else 64
+            t0 = time.time()
+            while time.time() - t0 < budget_s:
+                j = tok % (steps_total - steps_total % chunk) if steps_total >= chunk else 0
+                xs, as_, bs = inp.x[j:j + chunk, 0], inp.a[j:j + chunk, 0], inp.b[j:j + chunk, 0]
+                if threads == 1:
+                    _, S0, tail0 = oracle.run(shape, S0, tail0, inp.w, xs, as_, bs)
+                else:
+                    _, S0, tail0 = oracle.run_parallel(shape, S0, tail0, inp.w, xs, as_, bs, threads=threads)
+                tok += xs.shape[0]
+            return tok, time.time() - t0
+
+        os.sched_setaffinity(0, {cpus[0]})
+        try:
+            tok1, el1 = leg(10.0, 1)
+        finally:
+            os.sched_setaffinity(0, set(cpus))
+        nthr = min(len(cpus), shape.num_k_heads)
+        tokn, eln = leg(10.0, nthr)
+        one = {"value": round(per_step * tok1 / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "tokens_per_s": round(tok1 / el1, 1), "tokens": tok1, "seconds": round(el1, 1)}
+        cpu = {"value": round(per_step * tokn / eln / 1e9, 3), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+               "tokens_per_s": round(tokn / eln, 1),
+               "sample": f"{tokn} chained decode steps of the batch-1 27B-class layer (all 48 heads, fp64 scalar "
+                         f"C, cycling over the {steps_total} drawn tokens) in {eln:.1f} s, the heads split by q/k "
+                         f"head group over {nthr} host threads; the one-core leg ran {tok1} steps in {el1:.1f} s",
+               "one_core": one, "host": host}
 
     # ---------------------------------------------------------------- the line
     best_ms = cold_ms if graph_ms is None else min(cold_ms, graph_ms)
@@ -539,8 +595,11 @@ def main():
         "ms_per_step": round(best_ms / K, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "tokens_per_s_per_layer": round(K / best_ms * 1e3, 1),
-        "config": {"workload": "decode_b1_27b_layer_4096_steps", "batch": 1, **SHAPE_DESC,
-                   "state_bytes": 3_145_728, "act": "bf16", "state_buffers_rotated": R, "launch": launch,
+        "config": {"workload": f"decode_b1_27b_layer_{K}_steps", "batch": 1, **SHAPE_DESC,
+                   "state_bytes": 3_145_728, "act": "bf16", "state_buffers_rotated": min(K, R),
+                   "states_touched_bytes": min(K, R) * 3_145_728,
+                   "cache": "Infinity Cache evicted (1 GiB device copy) just before the timed steps",
+                   "launch": launch,
                    "bytes_per_step": per_step},
         "roofline": roof, "cpu_baseline": cpu, "rows": {k: _round(v) for k, v in res.items()},
         "input_gen_s": round(gen_s, 1),
@@ -559,6 +618,25 @@ def prefill_flops(T, shape):
     per_qk = 2 * (2 * Cc * Cc * D)
     per_v = 3 * (2 * Cc * Cc * D) + 3 * (2 * Cc * D * D) + Cc ** 3 // 3
     return nchunks * (shape.num_k_heads * per_qk + shape.num_v_heads * per_v)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _gcc_version():
+    import subprocess
+    try:
+        return subprocess.run(["gcc", "--version"], capture_output=True, text=True).stdout.splitlines()[0]
+    except (OSError, IndexError):
+        return "unknown"
 
 
 def _round(v):

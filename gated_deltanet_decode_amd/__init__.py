@@ -20,6 +20,7 @@ __all__ = [
     "conv_update", "decode_step", "decode_token", "tree_verify", "tree_verify_ut", "commit_path",
     "commit_path_prepared",
     "tree_tables", "block_verify", "block_verify_ut", "block_commit", "block_commit_prepared", "state_signature", "snapshot", "restore", "prefill_chunked",
+    "self_check_workspace_bytes", "self_check", "SELF_CHECK_PERTURB",
     "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
 ]
 
@@ -29,6 +30,7 @@ MAX_TREE_NODES = 32
 MAX_TREE_DEPTH = 8
 PREFILL_CHUNK = 64
 F32, BF16 = 0, 1
+SELF_CHECK_PERTURB = 1
 _STATUS_TREE = 5
 
 if not os.path.exists(LIB_PATH):
@@ -84,6 +86,8 @@ _sig = {
     "gdn_snapshot_bytes": ([_D, _I], C.c_size_t),
     "gdn_snapshot": ([_D, _P, _P, _I, _P, _P, C.c_size_t, _P, _P], C.c_int),
     "gdn_restore": ([_D, _P, _P, _I, _P, _P, C.c_size_t, _P, _P], C.c_int),
+    "gdn_self_check_workspace_bytes": ([_D], C.c_size_t),
+    "gdn_self_check": ([_D, C.c_uint32, _I, _P, C.c_size_t, _P, _P], C.c_int),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -364,3 +368,16 @@ def prefill_chunked(d: Dims, state, tail, w, x, a, b, o, workspace=None, stream=
                                     _t(a, "a", torch.float32, B * T * Hv), _t(b, "b", torch.float32, B * T * Hv),
                                     _t(o, "o", torch.float32, B * T * Hv * dv), ws_ptr, ws_bytes, _stream(stream)),
            "gdn_prefill_chunked")
+
+
+def self_check_workspace_bytes(d: Dims) -> int:
+    return _lib.gdn_self_check_workspace_bytes(C.byref(d))
+
+
+def self_check(d: Dims, result, workspace, seed: int = 0x5EED, flags: int = 0, stream=None) -> None:
+    """Queue the load-time self-check for d's layer shape; result [4] int32 (device) receives
+    the verdict: result[0] == 0 when verify and commit rows equal decode's bit for bit."""
+    ptr, nbytes = _blob(workspace, self_check_workspace_bytes(d), "workspace")
+    _check(_lib.gdn_self_check(C.byref(d), seed & 0xFFFFFFFF, flags, ptr, nbytes,
+                               _t(result, "result", torch.int32, 4), _stream(stream)), "gdn_self_check")
+

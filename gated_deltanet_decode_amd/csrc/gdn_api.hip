@@ -89,6 +89,7 @@ const char* gdn_status_str(int status) {
         case GDN_ERR_ALIAS: return "buffers that must be distinct overlap";
         case GDN_ERR_SIGNATURE: return "snapshot of another layer shape or format";
         case GDN_ERR_INDEX: return "sequence index out of range or repeated";
+        case GDN_ERR_SELF_CHECK: return "self-check: verify or commit rows differ from decode";
         default: return "unknown status";
     }
 }
@@ -411,6 +412,33 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, float* state, void* conv_tail,
     if (need > 0 && !aligned16(workspace))
         return GDN_ERR_ALIGN;
     return launched(gdn::launch_prefill(g, state, conv_tail, conv_w, T, x, a, b, o, workspace, as_stream(stream)));
+}
+
+size_t gdn_self_check_workspace_bytes(const gdn_dims* d) {
+    gdn::Geo g;
+    if (check_dims(d, g) != GDN_OK || g.Hv / g.Hk > 64)
+        return 0;
+    return gdn::self_check_ws_bytes(g);
+}
+
+gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void* workspace, size_t workspace_bytes,
+                          int32_t* result, void* stream) {
+    gdn::Geo g;
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK && g.Hv / g.Hk > 64)
+        st = GDN_ERR_SHAPE;
+    if (st == GDN_OK)
+        st = ptrs_ok({result});
+    if (st == GDN_OK && (flags & ~GDN_SELF_CHECK_PERTURB))
+        st = GDN_ERR_SHAPE;
+    if (st != GDN_OK)
+        return st;
+    if (!workspace || workspace_bytes < gdn::self_check_ws_bytes(g))
+        return GDN_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return GDN_ERR_ALIGN;
+    return launched(gdn::launch_self_check(g, workspace, seed, flags & GDN_SELF_CHECK_PERTURB, result,
+                                           as_stream(stream)));
 }
 
 }  // extern "C"

@@ -40,4 +40,7 @@ size_t prefill_workspace_bytes(const Geo& g, int T);
 hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int T, const void* x, const float* a,
                           const float* b, float* o, void* ws, hipStream_t s);
 
+size_t self_check_ws_bytes(const Geo& g);
+hipError_t launch_self_check(const Geo& g, void* ws, uint32_t seed, int perturb, int32_t* result, hipStream_t s);
+
 }  // namespace gdn

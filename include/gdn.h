@@ -68,7 +68,8 @@ typedef enum {
     GDN_ERR_HIP = 7,         /* the HIP runtime refused a launch */
     GDN_ERR_ALIAS = 8,       /* buffers that must be distinct overlap */
     GDN_ERR_SIGNATURE = 9,   /* a snapshot of another layer shape or format (device status value) */
-    GDN_ERR_INDEX = 10       /* a sequence index out of range, or repeated where it must not be (device status value) */
+    GDN_ERR_INDEX = 10,      /* a sequence index out of range, or repeated where it must not be (device status value) */
+    GDN_ERR_SELF_CHECK = 11  /* the self-check found verify or commit rows that differ from decode (device value) */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -367,6 +368,40 @@ gdn_status gdn_snapshot(const gdn_dims* d, const float* state, const void* conv_
                         const int32_t* seqs, void* blob, size_t blob_bytes, int32_t* status, void* stream);
 gdn_status gdn_restore(const gdn_dims* d, float* state, void* conv_tail, int32_t count, const int32_t* seqs,
                        const void* blob, size_t blob_bytes, int32_t* status, void* stream);
+
+/*
+ * gdn_self_check -- the load-time self-check that gates speculation
+ * (repository "Architecture" page, "Kernels and devices, then the mesh": an
+ * exact model serves plain decode until a row-invariant kernel exists, and a
+ * self-check at load decides whether speculation may run).  It checks, on the
+ * device, that tree verify and commit are row-invariant against decode for
+ * the layer shape d (d->batch is not used):
+ *   - a seeded 32-node tree of depth 8 (a chain of 8 from the root and 24
+ *     nodes under its first seven, so siblings sit at the deepest level) is
+ *     verified by gdn_tree_verify from a seeded checkpoint;
+ *   - 32 copies of the checkpoint replay the root-first paths to the 32
+ *     nodes with gdn_decode_token, 8 steps (a shorter path repeats its last
+ *     token afterwards);
+ *   - every node's output row must equal, bit for bit, its replay's output at
+ *     the end of its path, and gdn_commit_path of the depth-8 path must leave
+ *     the state and tail that its 8-step replay leaves, bit for bit.
+ * Every input is drawn on the device from `seed` (a counter-based hash), so
+ * nothing crosses from the host.  The verdict is written, stream-ordered and
+ * without synchronising, to result, i32 [4] (device, 16-byte aligned):
+ *   result[0]  GDN_OK if every row and word is equal, else GDN_ERR_SELF_CHECK
+ *   result[1]  number of output values that differ
+ *   result[2]  number of committed state and tail words that differ
+ *   result[3]  GDN_OK, or the first non-OK tree or path status of the case
+ * flags: 0, or GDN_SELF_CHECK_PERTURB, which flips one input bit of one
+ * node's last token in the decode replay only, so that result[0] must come
+ * back GDN_ERR_SELF_CHECK (a check of the check).
+ *   workspace  device bytes >= gdn_self_check_workspace_bytes(d), caller-owned
+ *              (about 120 MB at 48 value heads of 128: the 32 replayed states)
+ */
+#define GDN_SELF_CHECK_PERTURB 1
+size_t gdn_self_check_workspace_bytes(const gdn_dims* d);
+gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void* workspace, size_t workspace_bytes,
+                          int32_t* result, void* stream);
 
 #ifdef __cplusplus
 }

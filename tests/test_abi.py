@@ -140,9 +140,9 @@ def test_fused_token_refuses_overlapping_tails(lib):
 
 def test_status_strings(lib):
     lib.gdn_status_str.restype = C.c_char_p
-    for s in range(11):
-        assert lib.gdn_status_str(s)
-    assert lib.gdn_status_str(11) == b"unknown status"
+    for s in range(12):
+        assert lib.gdn_status_str(s) and lib.gdn_status_str(s) != b"unknown status"
+    assert lib.gdn_status_str(12) == b"unknown status"
     assert lib.gdn_abi_version() == 1
 
 
@@ -272,3 +272,26 @@ def test_prepared_block_commit_refuses_what_block_commit_refuses(lib):
                                              None) == 2
     assert lib.gdn_block_commit_prepared(C.byref(d), fake, fake, 4, fake, fake, None, None, fake, 1024, None) == 6
     assert lib.gdn_block_commit_prepared(C.byref(d), fake, fake, 4, None, fake, None, None, fake, 1 << 30, None) == 1
+
+
+def test_self_check_refusals(lib):
+    """gdn_self_check refuses bad dims, a null or misaligned result word, unknown flags and a
+    short workspace before anything is queued (fake pointers are never touched)."""
+    lib.gdn_self_check_workspace_bytes.restype = C.c_size_t
+    lib.gdn_self_check.argtypes = [C.POINTER(Dims), C.c_uint32, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p,
+                                   C.c_void_p]
+    d = mk()
+    need = lib.gdn_self_check_workspace_bytes(C.byref(d))
+    # 32 replayed states of 3.15 MB dominate; the rest is a few MB
+    assert 32 * 3_145_728 < need < 160 * 1024 * 1024
+    assert lib.gdn_self_check_workspace_bytes(C.byref(mk(head_k_dim=64, head_v_dim=64))) == 0
+    ws, res = 1 << 20, 1 << 12   # non-null, aligned fake addresses
+    call = lambda dd, flags=0, w=ws, n=need, r=res: lib.gdn_self_check(C.byref(dd), 7, flags, w, n, r, None)
+    assert call(mk(num_v_heads=40)) == 2
+    assert call(mk(act_dtype=9)) == 3
+    assert call(d, r=None) == 1
+    assert call(d, r=res + 4) == 4
+    assert call(d, flags=2) == 2
+    assert call(d, w=None) == 6
+    assert call(d, n=need - 1) == 6
+    assert call(d, w=ws + 8) == 4
