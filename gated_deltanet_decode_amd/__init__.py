@@ -20,7 +20,8 @@ __all__ = [
     "conv_update", "decode_step", "decode_token", "tree_verify", "tree_verify_ut", "commit_path",
     "commit_path_prepared",
     "tree_tables", "block_verify", "block_verify_ut", "block_commit", "block_commit_prepared", "state_signature", "snapshot", "restore", "prefill_chunked",
-    "self_check_workspace_bytes", "self_check", "SELF_CHECK_PERTURB",
+    "self_check_workspace_bytes", "self_check", "SELF_CHECK_PERTURB", "tree_verify_ut_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
 ]
 
@@ -31,6 +32,7 @@ MAX_TREE_DEPTH = 8
 PREFILL_CHUNK = 64
 F32, BF16 = 0, 1
 SELF_CHECK_PERTURB = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20
 _STATUS_TREE = 5
 
 if not os.path.exists(LIB_PATH):
@@ -88,6 +90,7 @@ _sig = {
     "gdn_restore": ([_D, _P, _P, _I, _P, _P, C.c_size_t, _P, _P], C.c_int),
     "gdn_self_check_workspace_bytes": ([_D], C.c_size_t),
     "gdn_self_check": ([_D, C.c_uint32, _I, _P, C.c_size_t, _P, _P], C.c_int),
+    "gdn_tree_verify_ut_noalloc": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P], C.c_int),
 }
 for _name, (_args, _res) in _sig.items():
     _f = getattr(_lib, _name)
@@ -381,3 +384,21 @@ def self_check(d: Dims, result, workspace, seed: int = 0x5EED, flags: int = 0, s
     _check(_lib.gdn_self_check(C.byref(d), seed & 0xFFFFFFFF, flags, ptr, nbytes,
                                _t(result, "result", torch.int32, 4), _stream(stream)), "gdn_self_check")
 
+
+def tree_verify_ut_noalloc(d: Dims, state, tail, w, parent, x, a, b, o, status=None, stream=None) -> None:
+    """tree_verify_ut with no workspace argument: the library's per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES) holds the prepared operands; calls on one GPU must not overlap."""
+    B = d.batch
+    if parent.numel() % B:
+        raise ValueError("parent must be [B][n_nodes]")
+    n = parent.numel() // B
+    Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_tree_verify_ut_noalloc(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
+                                           _t(tail, "conv_tail", d.act_torch, B * Cc * 4),
+                                           _t(w, "conv_w", d.act_torch, Cc * 4), n,
+                                           _t(parent, "parent", torch.int32, B * n),
+                                           _t(x, "x", d.act_torch, B * n * Cc), _t(a, "a", torch.float32, B * n * Hv),
+                                           _t(b, "b", torch.float32, B * n * Hv),
+                                           _t(o, "o", torch.float32, B * n * Hv * dv),
+                                           _opt(status, "tree_status", torch.int32, B), _stream(stream)),
+           "gdn_tree_verify_ut_noalloc")

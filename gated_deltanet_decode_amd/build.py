@@ -31,7 +31,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_token.hip", "gdn_tree.hip", "gdn_prefill.hip", "gdn_state.hip",
-           "gdn_selfcheck.hip"]
+           "gdn_selfcheck.hip", "gdn_noalloc.hip"]
 # The prefill kernels keep their MFMA accumulators in ordinary VGPRs: the scan
 # scales and converts its state accumulators every chunk, which would otherwise
 # cost a copy out of and back into the accumulation registers each time.

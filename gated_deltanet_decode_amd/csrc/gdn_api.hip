@@ -441,4 +441,28 @@ gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void*
                                            as_stream(stream)));
 }
 
+gdn_status gdn_tree_verify_ut_noalloc(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
+                                      const void* conv_w, int32_t n_nodes, const int32_t* parent, const void* x,
+                                      const float* a, const float* b, float* o, int32_t* tree_status, void* stream) {
+    gdn::Geo g;
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
+        st = GDN_ERR_SHAPE;
+    if (st == GDN_OK)
+        st = ptrs_ok({state_ckpt, conv_tail, conv_w, parent, x, a, b, o});
+    if (st == GDN_OK && tree_status && !aligned16(tree_status))
+        st = GDN_ERR_ALIGN;
+    if (st == GDN_OK && (n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES))
+        st = GDN_ERR_TREE;
+    if (st != GDN_OK)
+        return st;
+    if (gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D) > GDN_NOALLOC_SCRATCH_BYTES)
+        return GDN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (gdn::noalloc_scratch(&ws) != hipSuccess)
+        return GDN_ERR_HIP;
+    return launched(gdn::launch_tree_verify_ut(g, state_ckpt, conv_tail, conv_w, n_nodes, parent, x, a, b, o,
+                                               tree_status, ws, as_stream(stream)));
+}
+
 }  // extern "C"

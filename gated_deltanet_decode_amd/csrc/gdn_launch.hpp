@@ -42,5 +42,7 @@ hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int
 
 size_t self_check_ws_bytes(const Geo& g);
 hipError_t launch_self_check(const Geo& g, void* ws, uint32_t seed, int perturb, int32_t* result, hipStream_t s);
+// Device address of the library-held scratch array on the current device.
+hipError_t noalloc_scratch(void** out);
 
 }  // namespace gdn

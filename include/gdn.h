@@ -403,6 +403,30 @@ size_t gdn_self_check_workspace_bytes(const gdn_dims* d);
 gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void* workspace, size_t workspace_bytes,
                           int32_t* result, void* stream);
 
+/*
+ * gdn_tree_verify_ut_noalloc -- gdn_tree_verify_ut for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: the prepared operands go to a
+ * library-held device array of GDN_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU,
+ * held from the library's first use on that GPU until the process ends.  The
+ * caller still passes inputs and outputs; arguments, outputs, statuses and
+ * errors are gdn_tree_verify_ut's, and the outputs are bit-identical to it.
+ *   GDN_ERR_WORKSPACE  gdn_tree_workspace_bytes(d, n_nodes) exceeds the array
+ *                      (at 16 q/k and 48 value heads of 128 and 32 nodes: more
+ *                      than 12 sequences)
+ *   GDN_ERR_HIP        the array's device address could not be looked up
+ * The call allocates nothing.  Every call on one GPU shares that GPU's array,
+ * so calls that may overlap on one GPU (different streams, or host threads)
+ * race and must be ordered by the caller.  Each call writes every scratch
+ * word it reads before reading it, so what an earlier call left is never used.
+ * gdn_commit_path_prepared cannot read this array: commit with
+ * gdn_commit_path after it.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (16u << 20)
+gdn_status gdn_tree_verify_ut_noalloc(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
+                                      const void* conv_w, int32_t n_nodes, const int32_t* parent, const void* x,
+                                      const float* a, const float* b, float* o, int32_t* tree_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -295,3 +295,20 @@ def test_self_check_refusals(lib):
     assert call(d, w=None) == 6
     assert call(d, n=need - 1) == 6
     assert call(d, w=ws + 8) == 4
+
+
+def test_tree_verify_ut_noalloc_refusals(lib):
+    """The no-workspace tree verify refuses bad dims, null pointers, bad node counts and a
+    batch whose operands exceed its fixed scratch before any device call."""
+    P = C.c_void_p
+    lib.gdn_tree_verify_ut_noalloc.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, P, P]
+    lib.gdn_tree_workspace_bytes.restype = C.c_size_t
+    f = P(1 << 20)
+    call = lambda d, n=32, o=f: lib.gdn_tree_verify_ut_noalloc(C.byref(d), f, f, f, n, f, f, f, f, o, None, None)
+    assert call(mk(num_v_heads=40)) == 2
+    assert call(mk(), o=None) == 1
+    assert call(mk(), n=0) == 5 and call(mk(), n=33) == 5
+    scratch = 16 << 20
+    assert lib.gdn_tree_workspace_bytes(C.byref(mk(batch=12)), 32) <= scratch
+    assert lib.gdn_tree_workspace_bytes(C.byref(mk(batch=13)), 32) > scratch
+    assert call(mk(batch=13)) == 6
