@@ -103,15 +103,23 @@ def counter_traffic():
 
 
 class Timer:
-    """HIP events on the stream the work is launched on."""
+    """HIP events on the stream the work is launched on.  With lead_in (a function that
+    queues a long device operation, such as the cache eviction), the start event is queued
+    behind it without a host synchronisation in between: while the GPU runs the lead-in,
+    the host queues the start event and the timed launches, so the events time the device
+    work of the timed steps, not the host's submission of them.  The region is still
+    bracketed by synchronisations."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, lead_in=None):
         self.torch = torch
+        self.lead_in = lead_in
         self.s = torch.cuda.Event(enable_timing=True)
         self.e = torch.cuda.Event(enable_timing=True)
 
     def __enter__(self):
         self.torch.cuda.synchronize()
+        if self.lead_in is not None:
+            self.lead_in()
         self.s.record(self.torch.cuda.current_stream())
         return self
 
@@ -143,16 +151,15 @@ def graph_time_us(torch, fn, n, reps=4):
 
 
 def cold_graph_ms(torch, fn, n, evict):
-    """Capture fn(0..n-1) into one hip graph, replay it twice untimed, evict the caches
-    with evict(), then time one replay on the current stream; milliseconds."""
+    """Capture fn(0..n-1) into one hip graph, replay it twice untimed, then time one replay
+    on the current stream right behind a cache eviction (evict() queues it); milliseconds."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(n):
             fn(i)
     g.replay()
     g.replay()
-    evict()
-    with Timer(torch) as tm:
+    with Timer(torch, lead_in=evict) as tm:
         g.replay()
     del g
     return tm.ms
@@ -241,8 +248,7 @@ def main():
 
     for t in range(W):
         step(t, t % R)
-    evict()
-    with Timer(torch) as tm:
+    with Timer(torch, lead_in=evict) as tm:
         for t in range(W, W + K):
             step(t, t % R)
     cold_ms = tm.ms

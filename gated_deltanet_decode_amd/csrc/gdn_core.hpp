@@ -139,7 +139,10 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // One wave normalises one token's q~ and k~ of one q/k head.  Lane l holds
 // elements l + 64*j (j < J); lanes past D hold zeros.  On return they hold q^,
-// k^ and every lane holds kq = k^.q^.
+// k^ and every lane holds kq = k^.q^.  The three sums (|q~|^2, |k~|^2, q~.k~)
+// are reduced together, and kq is formed from q~.k~ and the two reciprocal
+// norms, so one wave reduction stands between the conv outputs and the row
+// update instead of two.
 template <int D>
 struct Prep {
     static constexpr int J = D >= kWave ? D / kWave : 1;
@@ -148,24 +151,24 @@ struct Prep {
 template <int D>
 __device__ __forceinline__ void prep_qk(float (&q)[Prep<D>::J], float (&k)[Prep<D>::J], float& kq) {
     constexpr int J = Prep<D>::J;
-    float nq = 0.0f, nk = 0.0f;
+    float nq = 0.0f, nk = 0.0f, d = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         nq = __builtin_fmaf(q[j], q[j], nq);
         nk = __builtin_fmaf(k[j], k[j], nk);
+        d = __builtin_fmaf(q[j], k[j], d);
     }
     nq = group_sum<kWave>(nq);
     nk = group_sum<kWave>(nk);
-    const float rq = 1.0f / sqrtf(nq + kEps);
-    const float rk = 1.0f / sqrtf(nk + kEps);
-    float d = 0.0f;
+    d = group_sum<kWave>(d);
+    const float rq = __builtin_amdgcn_rsqf(nq + kEps);   // hardware reciprocal square root, about 1 ulp
+    const float rk = __builtin_amdgcn_rsqf(nk + kEps);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         q[j] = q[j] * rq;
         k[j] = k[j] * rk;
-        d = __builtin_fmaf(q[j], k[j], d);
     }
-    kq = group_sum<kWave>(d);
+    kq = d * rq * rk;
 }
 
 // ------------------------------------------------------------ the row update
