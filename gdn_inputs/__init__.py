@@ -29,7 +29,8 @@ import numpy as np
 __all__ = [
     "LayerShape", "TINY", "QWEN27B_LAYER", "normal_rows", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "random_tree", "random_leaf_path", "tree_depths",
-    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "Inputs", "GATE_REGIMES",
+    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "kda_inputs", "Inputs",
+    "GATE_REGIMES",
 ]
 
 BF16 = "bf16"
@@ -61,7 +62,7 @@ TINY = LayerShape(4, 4, 32, 32, 4, F32)
 QWEN27B_LAYER = LayerShape(16, 48, 128, 128, 4, BF16)
 
 # Stream identifiers: one per tensor role, fixed forever.
-S_X, S_A, S_B, S_W, S_STATE, S_TAIL, S_TREE = 1, 2, 3, 4, 5, 6, 7
+S_X, S_A, S_B, S_W, S_STATE, S_TAIL, S_TREE, S_A_CHANNEL = 1, 2, 3, 4, 5, 6, 7, 8
 
 _ROWS_PER_BLOCK = 64
 _POOL = None
@@ -262,3 +263,18 @@ def prefill_inputs(seed: int, shape: LayerShape, T: int, batch: int = 1,
     """A prompt of T tokens; by default from a fresh (zero) state and zero conv tail."""
     x, a, b, w, state, tail = _common(seed, shape, batch, T, state_sigma, tail_random, gates)
     return Inputs(shape, batch, T, x, a, b, w, state, tail)
+
+
+def kda_inputs(seed: int, shape: LayerShape, batch: int, steps: int, state_sigma: float = 0.1,
+               tail_random: bool = True, gates: str = "normal") -> Inputs:
+    """Chained decode with a per-channel forget gate: as decode_inputs, except that a is
+    [steps][batch][Hv][dk], one gate input per (value head, key channel), each drawn
+    from N(0,1) shifted by the regime's mean (its own stream, so a and b keep their
+    meaning in every regime)."""
+    x, _, b, w, state, tail = _common(seed, shape, batch, steps, state_sigma, tail_random, gates)
+    Hv, dk = shape.num_v_heads, shape.head_k_dim
+    a_mean, _ = GATE_REGIMES[gates]
+    a = normal_rows(seed, S_A_CHANNEL, steps * batch * Hv, dk).reshape(steps, batch, Hv, dk)
+    if a_mean:
+        a += np.float32(a_mean)
+    return Inputs(shape, batch, steps, x, a, b, w, state, tail)

@@ -52,8 +52,10 @@ def lib():
         L.oracle_tree_tables.argtypes = [I, P, I, P, P]
         L.oracle_tree_verify.argtypes = [I, I, I, I, I, P, P, P, I, I, P, I, P, I, P, P, P, I, I]
         L.oracle_commit_path.argtypes = [I, I, I, I, I, P, P, P, I, I, P, I, P, I, P, P, I, P, P, I, I]
+        L.oracle_run_kda.argtypes = [I, I, I, I, I, P, P, P, I, I, P, I, P, P, P]
+        L.oracle_recur_kda.argtypes = [I, I, I, I, P, P, P, P, P]
         for f in ("oracle_run", "oracle_recur", "oracle_conv", "oracle_tree_tables",
-                  "oracle_tree_verify", "oracle_commit_path"):
+                  "oracle_tree_verify", "oracle_commit_path", "oracle_run_kda", "oracle_recur_kda"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -128,6 +130,26 @@ def run(shape, state, tail, w, x, a, b, h_range=None, rows=None, want_o=True):
     return o, S, t
 
 
+def run_kda(shape, state, tail, w, x, a, b, want_o=True):
+    """T tokens of one sequence with the per-channel forget gate (oracle_run_kda).
+    state [Hv][dv][dk], tail [C][W], x [T][C], a [T][Hv][dk], b [T][Hv].
+    Returns (o [T][Hv][dv] or None, S, tail) in fp64."""
+    Hk, Hv, dk, dv, W = shape.num_k_heads, shape.num_v_heads, shape.head_k_dim, shape.head_v_dim, shape.conv_width
+    S = f64(state)
+    t = f64(tail)
+    w, wb = _act(w)
+    x, xb = _act(x)
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    T = x.shape[0] if x.ndim == 2 else x.size // shape.conv_channels
+    if a.size != T * Hv * dk or b.size != T * Hv:
+        raise ValueError("run_kda: a must be [T][Hv][dk] and b [T][Hv]")
+    o = np.zeros((T, Hv, dv), dtype=np.float64) if want_o else None
+    rc = lib().oracle_run_kda(Hk, Hv, dk, dv, W, _p(S), _p(t), _p(w), wb, T, _p(x), xb, _p(a), _p(b), _p(o))
+    _check(rc, "oracle_run_kda")
+    return o, S, t
+
+
 def run_parallel(shape, state, tail, w, x, a, b, want_o=True, threads=None):
     """run() over all value heads, split by q/k head group over host threads.
 
@@ -172,6 +194,21 @@ def recur(shape, state, y, a, b):
     b = np.ascontiguousarray(b, dtype=np.float64)
     o = np.zeros((Hv, dv), dtype=np.float64)
     _check(lib().oracle_recur(Hk, Hv, dk, dv, _p(S), _p(y), _p(a), _p(b), _p(o)), "oracle_recur")
+    return o, S
+
+
+def recur_kda(shape, state, y, a, b):
+    """One token of the per-channel-decay recurrence from a conv output y[C], gate
+    inputs a [Hv][dk] and b [Hv]; returns (o [Hv][dv], S)."""
+    Hk, Hv, dk, dv = shape.num_k_heads, shape.num_v_heads, shape.head_k_dim, shape.head_v_dim
+    S = f64(state)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    if a.size != Hv * dk or b.size != Hv:
+        raise ValueError("recur_kda: a must be [Hv][dk] and b [Hv]")
+    o = np.zeros((Hv, dv), dtype=np.float64)
+    _check(lib().oracle_recur_kda(Hk, Hv, dk, dv, _p(S), _p(y), _p(a), _p(b), _p(o)), "oracle_recur_kda")
     return o, S
 
 

@@ -36,6 +36,10 @@
  * a brute-force unrolled product of transition matrices; closed forms at
  * beta = 0, at alpha = beta = 1 and at T = 1; group mapping; tree and path
  * invariants; the chunked (WY) form derived independently in NumPy.
+ * The per-channel-decay variant (oracle_run_kda) is pinned in
+ * tests/test_oracle_kda.py: scalar gates equal oracle_run bit for bit, beta = 0
+ * leaves S0 diag(prod alpha), a worked one-hot-key step, and the brute-force
+ * product of its transition matrices.
  */
 #include <math.h>
 #include <stdint.h>
@@ -246,6 +250,131 @@ int oracle_recur(int Hk, int Hv, int dk, int dv, double* S, const double* y,
     for (int h = 0; h < Hv; ++h) { ah[h] = a[h]; bh[h] = b[h]; }
     recur_token(&g, S, y, ah, bh, o, 0, Hv, qh, kh);
     free(qh); free(kh); free(ah); free(bh);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------ per-channel decay */
+
+/*
+ * The per-channel-decay delta rule (the model-arch page's module list names a
+ * Kimi Delta Attention mixer with a CPU reference and GPU launches, and does
+ * not define it).  Reading taken here: the conv, the q/k norm, beta and the
+ * output are those of the gated delta rule above; only the forget gate
+ * changes, from one scalar per value head to one value per (value head, key
+ * channel):
+ *   alpha[c] = exp(-softplus(a[h][c]))
+ *   S <- S diag(alpha);  p = S k^;  S <- S + beta*(v - p) k^T;  o = S q^ / sqrt(dk)
+ * so column c of every row (key channel c) decays by its own alpha[c] before
+ * the delta correction.  With all alpha[c] equal this is recur_token's step,
+ * operation for operation.
+ *   a  double [Hv][dk] (this token's per-channel gate inputs)
+ */
+static void recur_token_kda(const geom* g, double* S, const double* y, const double* a, const double* b,
+                            double* o, double* qh, double* kh, double* al)
+{
+    const double scale = 1.0 / sqrt((double)g->dk);
+    for (int h = 0; h < g->Hv; ++h) {
+        const int grp = h / g->G;
+        const double* q = y + (size_t)grp * g->dk;
+        const double* k = y + (size_t)g->Hk * g->dk + (size_t)grp * g->dk;
+        const double* v = y + (size_t)2 * g->Hk * g->dk + (size_t)h * g->dv;
+
+        double nq = 0.0, nk = 0.0;
+        for (int c = 0; c < g->dk; ++c) {
+            nq = nq + q[c] * q[c];
+            nk = nk + k[c] * k[c];
+        }
+        const double rq = 1.0 / sqrt(nq + ORACLE_EPS);
+        const double rk = 1.0 / sqrt(nk + ORACLE_EPS);
+        for (int c = 0; c < g->dk; ++c) {
+            qh[c] = q[c] * rq;
+            kh[c] = k[c] * rk;
+            al[c] = exp(-softplus(a[(size_t)h * g->dk + c]));
+        }
+        const double beta = sigmoid(b[h]);
+
+        for (int i = 0; i < g->dv; ++i) {
+            double* row = S + ((size_t)h * g->dv + i) * g->dk;
+            for (int c = 0; c < g->dk; ++c)
+                row[c] = al[c] * row[c];
+            double p = 0.0;
+            for (int c = 0; c < g->dk; ++c)
+                p = p + row[c] * kh[c];
+            const double u = beta * (v[i] - p);
+            for (int c = 0; c < g->dk; ++c)
+                row[c] = row[c] + u * kh[c];
+            if (o) {
+                double r = 0.0;
+                for (int c = 0; c < g->dk; ++c)
+                    r = r + row[c] * qh[c];
+                o[(size_t)h * g->dv + i] = scale * r;
+            }
+        }
+    }
+}
+
+/*
+ * oracle_run_kda (same passages as recur_token_kda and conv_token): T tokens
+ * of one sequence with the per-channel forget gate, in place, all heads.
+ *   S     double [Hv][dv][dk]   in/out
+ *   tail  double [C][W]         in/out
+ *   w, x  act as in oracle_run (x token t at row t)
+ *   a     float  [T][Hv][dk]    per-channel gate inputs
+ *   b     float  [T][Hv]
+ *   o     double [T][Hv][dv]    (nullable)
+ */
+int oracle_run_kda(int Hk, int Hv, int dk, int dv, int W,
+                   double* S, double* tail, const void* w, int w_bf16,
+                   int T, const void* x, int x_bf16,
+                   const float* a, const float* b, double* o)
+{
+    geom g;
+    if (make_geom(&g, Hk, Hv, dk, dv, W) != ORACLE_OK || T < 0)
+        return ORACLE_ERR_ARG;
+    unsigned char* need = malloc((size_t)g.C);
+    double* y = calloc((size_t)g.C, sizeof(double));
+    double* qh = malloc((size_t)dk * sizeof(double));
+    double* kh = malloc((size_t)dk * sizeof(double));
+    double* al = malloc((size_t)dk * sizeof(double));
+    double* ah = malloc((size_t)Hv * dk * sizeof(double));
+    double* bh = malloc((size_t)Hv * sizeof(double));
+    if (!need || !y || !qh || !kh || !al || !ah || !bh) {
+        free(need); free(y); free(qh); free(kh); free(al); free(ah); free(bh);
+        return ORACLE_ERR_ARG;
+    }
+    memset(need, 1, (size_t)g.C);
+    for (int t = 0; t < T; ++t) {
+        conv_token(&g, tail, w, w_bf16, x, x_bf16, (size_t)t * g.C, need, y);
+        for (size_t i = 0; i < (size_t)Hv * dk; ++i)
+            ah[i] = (double)a[(size_t)t * Hv * dk + i];
+        for (int h = 0; h < Hv; ++h)
+            bh[h] = (double)b[(size_t)t * Hv + h];
+        recur_token_kda(&g, S, y, ah, bh, o ? o + (size_t)t * Hv * dv : NULL, qh, kh, al);
+    }
+    free(need); free(y); free(qh); free(kh); free(al); free(ah); free(bh);
+    return ORACLE_OK;
+}
+
+/*
+ * oracle_recur_kda (same passages as recur_token_kda): one token of the
+ * per-channel-decay recurrence alone, from a given conv output y[C] and gate
+ * inputs a[Hv][dk], b[Hv].  All heads.
+ */
+int oracle_recur_kda(int Hk, int Hv, int dk, int dv, double* S, const double* y,
+                     const double* a, const double* b, double* o)
+{
+    geom g;
+    if (make_geom(&g, Hk, Hv, dk, dv, 1) != ORACLE_OK)
+        return ORACLE_ERR_ARG;
+    double* qh = malloc((size_t)dk * sizeof(double));
+    double* kh = malloc((size_t)dk * sizeof(double));
+    double* al = malloc((size_t)dk * sizeof(double));
+    if (!qh || !kh || !al) {
+        free(qh); free(kh); free(al);
+        return ORACLE_ERR_ARG;
+    }
+    recur_token_kda(&g, S, y, a, b, o, qh, kh, al);
+    free(qh); free(kh); free(al);
     return ORACLE_OK;
 }
 

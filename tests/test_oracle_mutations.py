@@ -35,14 +35,31 @@ MUTATIONS = {
     "depth_off_by_one": ("        depth[i] = depth[parent[i]] + 1;\n", "        depth[i] = depth[parent[i]];\n"),
 }
 
+# Slips in the per-channel-decay step (recur_token_kda), which comes after the
+# scalar step in the file: these edit the LAST occurrence of their anchor and run
+# against the variant's own pins.
+KDA_MUTATIONS = {
+    "kda_decay_after_correction": (
+        "            for (int c = 0; c < g->dk; ++c)\n                row[c] = al[c] * row[c];\n",
+        "",
+        "                row[c] = row[c] + u * kh[c];\n",
+        "                row[c] = al[c] * (row[c] + u * kh[c]);\n"),
+    "kda_one_gate_per_head": ("al[c] = exp(-softplus(a[(size_t)h * g->dk + c]));",
+                              "al[c] = exp(-softplus(a[(size_t)h * g->dk]));"),
+    "kda_decays_value_rows": ("row[c] = al[c] * row[c];", "row[c] = al[i % g->dk] * row[c];"),
+    "kda_gate_sign": ("al[c] = exp(-softplus(a[(size_t)h * g->dk + c]));",
+                      "al[c] = exp(-softplus(-a[(size_t)h * g->dk + c]));"),
+    "kda_channel_reversed": ("al[c] = exp(-softplus(a[(size_t)h * g->dk + c]));",
+                             "al[c] = exp(-softplus(a[(size_t)h * g->dk + (g->dk - 1 - c)]));"),
+    "kda_sign_of_correction": ("const double u = beta * (v[i] - p);", "const double u = beta * (v[i] + p);"),
+}
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake(name, tmp_path):
+
+def _mutant_fails_pins(name, edits, last, pin_files, tmp_path):
     src = open(SRC).read()
-    edits = MUTATIONS[name]
     for old, new in zip(edits[::2], edits[1::2]):
         assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
-        src = src.replace(old, new, 1)
+        src = new.join(src.rsplit(old, 1)) if last else src.replace(old, new, 1)
     c = tmp_path / "mutant.c"
     c.write_text(src)
     so = tmp_path / "libmutant.so"
@@ -50,7 +67,16 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                            "-o", str(so), str(c), "-lm"])
     env = dict(os.environ, GDN_ORACLE_LIB=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_chunk_algebra.py")],
+                        *[os.path.join(ROOT, "tests", f) for f in pin_files]],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"planted mistake {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    _mutant_fails_pins(name, MUTATIONS[name], False, ["test_oracle_pins.py", "test_chunk_algebra.py"], tmp_path)
+
+
+@pytest.mark.parametrize("name", sorted(KDA_MUTATIONS))
+def test_kda_pins_catch_planted_mistake(name, tmp_path):
+    _mutant_fails_pins(name, KDA_MUTATIONS[name], True, ["test_oracle_kda.py"], tmp_path)
