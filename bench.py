@@ -60,6 +60,13 @@ def token_bytes(B, shape):
     return B * per_seq + C * 4 * 2
 
 
+def kda_token_bytes(B, shape):
+    """gdn_kda_decode_token: token_bytes with the forget-gate input a widened from one value
+    per value head to one per (value head, key channel)."""
+    Hv, D = shape.num_v_heads, shape.head_k_dim
+    return token_bytes(B, shape) + B * Hv * (D - 1) * 4
+
+
 def tree_bytes(n, shape, B=1):
     """Algorithmic bytes of one tree verify over B sequences' trees of n nodes: per sequence the
     checkpoint read once, x, conv tail (bf16), gates, parent and o; the conv weights once."""
@@ -171,7 +178,7 @@ def main():
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--buffers", type=int, default=160, help="independent states rotated through (cold runs)")
-    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,tree,commit,tree64,block,snapshot,prefill,hot,cpu or all/none")
+    ap.add_argument("--rows", default="all", help="comma list of extra rows: graph,kernel,b64,kda,tree,commit,tree64,block,snapshot,prefill,hot,cpu or all/none")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 512 MiB device copy (for byte counters)")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
     args = ap.parse_args()
@@ -186,7 +193,7 @@ def main():
     import gated_deltanet_decode_amd as gdn
     import gdn_inputs as gi
 
-    rows = set(["graph", "kernel", "b64", "tree", "commit", "tree64", "block", "snapshot", "prefill", "hot", "cpu"]) \
+    rows = set(["graph", "kernel", "b64", "kda", "tree", "commit", "tree64", "block", "snapshot", "prefill", "hot", "cpu"]) \
         if args.rows == "all" else \
         set() if args.rows == "none" else set(args.rows.split(","))
     dev = "cuda"
@@ -303,6 +310,27 @@ def main():
         res["decode_b1_hot_eager"] = {"ms_per_step": tm.ms / K, "GBps": per_step * K / tm.ms / 1e6,
                                       "note": "one 3.15 MB state: served from cache, not HBM"}
 
+    # ---------------------------------------------------------------- per-channel decay at batch 1
+    # The same cold graph as decode_b1_cold_graph_all_states (2R steps over the R
+    # states, Infinity Cache evicted before the timed replay), through
+    # gdn_kda_decode_token with one gate input per (value head, key channel).
+    if "kda" in rows:
+        ak = f32(gi.channel_gates(5, shape, 1, 2 * R)[:, 0])
+        kb = kda_token_bytes(1, shape)
+
+        def kda_step(t, r):
+            i = cnt[r] % 2
+            gdn.kda_decode_token(d1, S_pool[r], tails[i][r], tails[1 - i][r], w, x[W + t % K], ak[t],
+                                 b[W + t % K], o)
+            cnt[r] += 1
+
+        ms = cold_graph_ms(torch, lambda t: kda_step(t, t % R), 2 * R, evict)
+        res["kda_decode_b1_cold_graph"] = {"ms_per_step": ms / (2 * R), "GBps": kb * 2 * R / ms / 1e6,
+                                           "tokens_per_s": 2 * R / ms * 1e3, "graph_steps": 2 * R,
+                                           "distinct_states": R, "bytes_per_token": kb,
+                                           "call": "gdn_kda_decode_token"}
+        del ak
+
     # ---------------------------------------------------------------- batch 64, ping-pong over two batches
     if "b64" in rows:
         B = 64
@@ -342,6 +370,23 @@ def main():
         res["decode_b64"]["kernel_us"] = us
         res["decode_b64"]["kernel_GBps"] = db / us / 1e3
         res["decode_b64"]["kernel_frac_hbm"] = db / us / 1e3 / HBM_PEAK_GBS
+        if "kda" in rows:
+            ak64 = f32(gi.channel_gates(6, shape, B, steps64 + 16))
+
+            def kda64(t):
+                p = t % 2
+                i = cnt64[p] % 2
+                gdn.kda_decode_token(d64, S64[p], tails64[i][p], tails64[1 - i][p], w64, x64[t], ak64[t], b64[t],
+                                     o64)
+                cnt64[p] += 1
+
+            kb = kda_token_bytes(B, shape)
+            us = graph_time_us(torch, lambda t: kda64(16 + t), steps64, reps=2)
+            res["kda_decode_b64"] = {"ms_per_step": us / 1e3, "GBps": kb / us / 1e3,
+                                     "tokens_per_s": B / us * 1e6, "frac_hbm": kb / us / 1e3 / HBM_PEAK_GBS,
+                                     "launch": "hipGraph", "call": "gdn_kda_decode_token",
+                                     "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
+            del ak64
         del S64, T64, tails64, x64, a64, b64, y64, o64
 
     # ---------------------------------------------------------------- tree verify + commit

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "GdnError", "Dims", "dims", "conv_channels", "state_bytes", "conv_tail_bytes",
     "prefill_workspace_bytes", "tree_workspace_bytes", "block_workspace_bytes", "snapshot_bytes",
-    "conv_update", "decode_step", "decode_token", "tree_verify", "tree_verify_ut", "commit_path",
+    "conv_update", "decode_step", "decode_token", "kda_decode_step", "kda_decode_token", "tree_verify",
+    "tree_verify_ut", "commit_path",
     "commit_path_prepared",
     "tree_tables", "block_verify", "block_verify_ut", "block_commit", "block_commit_prepared", "state_signature", "snapshot", "restore", "prefill_chunked",
     "self_check_workspace_bytes", "self_check", "SELF_CHECK_PERTURB", "tree_verify_ut_noalloc",
@@ -72,6 +73,8 @@ _sig = {
     "gdn_conv_update": ([_D, _P, _P, _P, _P, _P], C.c_int),
     "gdn_decode_step": ([_D, _P, _P, _P, _P, _P, _P], C.c_int),
     "gdn_decode_token": ([_D, _P, _P, _P, _P, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_kda_decode_step": ([_D, _P, _P, _P, _P, _P, _P], C.c_int),
+    "gdn_kda_decode_token": ([_D, _P, _P, _P, _P, _P, _P, _P, _P, _P], C.c_int),
     "gdn_tree_workspace_bytes": ([_D, _I], C.c_size_t),
     "gdn_tree_verify": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
     "gdn_tree_verify_ut": ([_D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P], C.c_int),
@@ -174,6 +177,27 @@ def decode_token(d: Dims, state, tail_in, tail_out, w, x, a, b, o, stream=None) 
                                  _t(w, "conv_w", d.act_torch, Cc * 4), _t(x, "x", d.act_torch, B * Cc),
                                  _t(a, "a", torch.float32, B * Hv), _t(b, "b", torch.float32, B * Hv),
                                  _t(o, "o", torch.float32, B * Hv * dv), _stream(stream)), "gdn_decode_token")
+
+
+def kda_decode_step(d: Dims, state, y, a, b, o, stream=None) -> None:
+    """decode_step with the per-channel forget gate: a is [B][Hv][dk]."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_kda_decode_step(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                    _t(y, "y", torch.float32, B * Cc), _t(a, "a", torch.float32, B * Hv * dk),
+                                    _t(b, "b", torch.float32, B * Hv), _t(o, "o", torch.float32, B * Hv * dv),
+                                    _stream(stream)), "gdn_kda_decode_step")
+
+
+def kda_decode_token(d: Dims, state, tail_in, tail_out, w, x, a, b, o, stream=None) -> None:
+    """decode_token with the per-channel forget gate: a is [B][Hv][dk]."""
+    B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
+    _check(_lib.gdn_kda_decode_token(C.byref(d), _t(state, "state", torch.float32, B * Hv * dv * dk),
+                                     _t(tail_in, "conv_tail_in", d.act_torch, B * Cc * 4),
+                                     _t(tail_out, "conv_tail_out", d.act_torch, B * Cc * 4),
+                                     _t(w, "conv_w", d.act_torch, Cc * 4), _t(x, "x", d.act_torch, B * Cc),
+                                     _t(a, "a", torch.float32, B * Hv * dk), _t(b, "b", torch.float32, B * Hv),
+                                     _t(o, "o", torch.float32, B * Hv * dv), _stream(stream)),
+           "gdn_kda_decode_token")
 
 
 def tree_workspace_bytes(d: Dims, n_nodes: int) -> int:

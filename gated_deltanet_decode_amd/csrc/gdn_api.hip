@@ -151,6 +151,34 @@ gdn_status gdn_decode_token(const gdn_dims* d, float* state, const void* conv_ta
     return launched(gdn::launch_token(g, state, conv_tail_in, conv_tail_out, conv_w, x, a, b, o, as_stream(stream)));
 }
 
+gdn_status gdn_kda_decode_step(const gdn_dims* d, float* state, const float* y, const float* a, const float* b,
+                               float* o, void* stream) {
+    gdn::Geo g;
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK)
+        st = ptrs_ok({state, y, a, b, o});
+    if (st != GDN_OK)
+        return st;
+    return launched(gdn::launch_kda_decode(g, state, y, a, b, o, as_stream(stream)));
+}
+
+gdn_status gdn_kda_decode_token(const gdn_dims* d, float* state, const void* conv_tail_in, void* conv_tail_out,
+                                const void* conv_w, const void* x, const float* a, const float* b, float* o,
+                                void* stream) {
+    gdn::Geo g;
+    gdn_status st = check_dims(d, g);
+    if (st == GDN_OK)
+        st = ptrs_ok({state, conv_tail_in, conv_tail_out, conv_w, x, a, b, o});
+    if (st != GDN_OK)
+        return st;
+    const size_t tail_bytes = static_cast<size_t>(g.B) * g.C * 4 * (g.bf16 ? 2 : 4);
+    const uintptr_t ti = reinterpret_cast<uintptr_t>(conv_tail_in), to = reinterpret_cast<uintptr_t>(conv_tail_out);
+    if (ti < to + tail_bytes && to < ti + tail_bytes)
+        return GDN_ERR_ALIAS;
+    return launched(
+        gdn::launch_kda_token(g, state, conv_tail_in, conv_tail_out, conv_w, x, a, b, o, as_stream(stream)));
+}
+
 gdn_status gdn_tree_tables(int32_t n_nodes, const int32_t* parent, int32_t* depth, int32_t* order,
                            int32_t* tree_status, void* stream) {
     if (n_nodes < 1 || n_nodes > GDN_MAX_TREE_NODES)

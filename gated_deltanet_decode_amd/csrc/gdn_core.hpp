@@ -97,9 +97,11 @@ __device__ __forceinline__ float conv_silu(const float w[4], const float win[4])
 }
 
 // alpha = exp(-softplus(a)) = 1 / (1 + e^a);  beta = sigmoid(b) = 1 / (1 + e^-b).
+__device__ __forceinline__ float forget_gate(float a) { return 1.0f / (1.0f + expf(a)); }
+__device__ __forceinline__ float write_gate(float b) { return 1.0f / (1.0f + expf(-b)); }
 __device__ __forceinline__ void gates(float a, float b, float& alpha, float& beta) {
-    alpha = 1.0f / (1.0f + expf(a));
-    beta = 1.0f / (1.0f + expf(-b));
+    alpha = forget_gate(a);
+    beta = write_gate(b);
 }
 
 // ------------------------------------------------------------ wave reductions
@@ -219,6 +221,61 @@ __device__ __forceinline__ float row_update(float4 (&s)[Row<D>::NV], const float
     for (int j = 0; j < NV; ++j)
         s[j] = axpby4(u, k[j], alpha, s[j]);
     return Scale<D>::value * __builtin_fmaf(u, kq, alpha * pq);
+}
+
+// The per-channel-decay step on one row: the forget gate is a vector over the
+// key channels, applied to the row before the delta correction:
+//   S' = S diag(al);  u = beta (v_i - S'.k);  S <- S' + u k;  o_i = scale (S'.q + u (k.q))
+// ka = al * k and qa = al * q (elementwise, shared by every row of the head)
+// give both dot products of S' from one pass over the old row.
+template <int D>
+__device__ __forceinline__ float row_update_kda(float4 (&s)[Row<D>::NV], const float4 (&k)[Row<D>::NV],
+                                                const float4 (&ka)[Row<D>::NV], const float4 (&qa)[Row<D>::NV],
+                                                const float4 (&al)[Row<D>::NV], float beta, float v, float kq) {
+    constexpr int NV = Row<D>::NV;
+    float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        pk = dot4(s[j], ka[j], pk);
+        pq = dot4(s[j], qa[j], pq);
+    }
+    pk = group_sum<Row<D>::LPR>(pk);
+    pq = group_sum<Row<D>::LPR>(pq);
+    const float u = beta * (v - pk);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        s[j] = make_float4(__builtin_fmaf(u, k[j].x, al[j].x * s[j].x), __builtin_fmaf(u, k[j].y, al[j].y * s[j].y),
+                           __builtin_fmaf(u, k[j].z, al[j].z * s[j].z), __builtin_fmaf(u, k[j].w, al[j].w * s[j].w));
+    return Scale<D>::value * __builtin_fmaf(u, kq, pq);
+}
+
+// Forget gates of this lane's keys from their gate inputs (laid out as k):
+// alpha = 1 / (1 + e^a) with e^a = 2^(a log2 e) and the reciprocal on the
+// hardware (about one ulp each, as in conv_silu), since every lane forms
+// 4 * NV of them on the way to its first row update.  e^a overflowing gives
+// alpha = 0, and underflowing gives alpha = 1, the limits of the gate.
+__device__ __forceinline__ float forget_gate_hw(float a) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * 1.4426950408889634f));
+}
+
+template <int D>
+__device__ __forceinline__ void kda_gates(const float4 (&araw)[Row<D>::NV], float4 (&al)[Row<D>::NV]) {
+#pragma unroll
+    for (int j = 0; j < Row<D>::NV; ++j)
+        al[j] = make_float4(forget_gate_hw(araw[j].x), forget_gate_hw(araw[j].y), forget_gate_hw(araw[j].z),
+                            forget_gate_hw(araw[j].w));
+}
+
+// The gated key and query vectors row_update_kda takes: ka = al * k, qa = al * q.
+template <int D>
+__device__ __forceinline__ void kda_vectors(const float4 (&al)[Row<D>::NV], const float4 (&k)[Row<D>::NV],
+                                            const float4 (&q)[Row<D>::NV], float4 (&ka)[Row<D>::NV],
+                                            float4 (&qa)[Row<D>::NV]) {
+#pragma unroll
+    for (int j = 0; j < Row<D>::NV; ++j) {
+        ka[j] = make_float4(al[j].x * k[j].x, al[j].y * k[j].y, al[j].z * k[j].z, al[j].w * k[j].w);
+        qa[j] = make_float4(al[j].x * q[j].x, al[j].y * q[j].y, al[j].z * q[j].z, al[j].w * q[j].w);
+    }
 }
 
 }  // namespace gdn

@@ -49,7 +49,8 @@ hipError_t launch_conv_update(const Geo& g, const void* x, void* tail, const voi
 // ------------------------------------------------------------ state step
 
 // PASSES row-quads per wave; a workgroup covers 4 * RPW * PASSES rows of one head.
-template <int D, int PASSES>
+// KDA: the forget gate is per key channel, a is [B][Hv][D] (row_update_kda).
+template <int D, int PASSES, bool KDA>
 __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, const float* __restrict__ y,
                                                      const float* __restrict__ a, const float* __restrict__ b,
                                                      float* __restrict__ o, int Hk, int Hv, int C,
@@ -71,6 +72,16 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
     const int wave = threadIdx.x / kWave;
     const int r = lane % LPR;
 
+    // The per-channel gate inputs go before the state loads, so their gates are
+    // computed while the state is in flight.
+    float4 al[NV];
+    if constexpr (KDA) {
+        float4 araw[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            araw[j] = *reinterpret_cast<const float4*>(a + static_cast<size_t>(bh) * D + R::key(j, r));
+        kda_gates<D>(araw, al);
+    }
     float* Sh = S + static_cast<size_t>(bh) * D * D;
     int row[PASSES];
     float4 s[PASSES][NV];
@@ -107,8 +118,11 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
         if (lane == 0)
             kq_s = kq;
     }
-    float alpha, beta;
-    gates(a[bh], b[bh], alpha, beta);
+    float alpha = 0.0f, beta;
+    if constexpr (KDA)
+        beta = write_gate(b[bh]);
+    else
+        gates(a[bh], b[bh], alpha, beta);
     float v[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
@@ -122,10 +136,17 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
         qq[j] = *reinterpret_cast<const float4*>(qs + R::key(j, r));
     }
     const float kq = kq_s;
+    float4 ka[NV], qa[NV];
+    if constexpr (KDA)
+        kda_vectors<D>(al, kk, qq, ka, qa);
     float* oh = o + static_cast<size_t>(bh) * D;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-        const float out = row_update<D>(s[p], kk, qq, alpha, beta, v[p], kq);
+        float out;
+        if constexpr (KDA)
+            out = row_update_kda<D>(s[p], kk, ka, qa, al, beta, v[p], kq);
+        else
+            out = row_update<D>(s[p], kk, qq, alpha, beta, v[p], kq);
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             store_stream(Sh + row[p] * D + R::key(j, r), s[p][j]);
@@ -134,26 +155,37 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ S, cons
     }
 }
 
-template <int D, int PASSES>
+template <int D, int PASSES, bool KDA>
 static hipError_t launch_decode_cfg(const Geo& g, float* S, const float* y, const float* a, const float* b, float* o,
                                     hipStream_t s) {
     constexpr int ROWS_WG = 4 * Row<D>::RPW * PASSES;
     static_assert(D % ROWS_WG == 0, "rows per workgroup must divide the head");
     const int bph = D / ROWS_WG;
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.B) * g.Hv * bph)), block(256);
-    hipLaunchKernelGGL((decode_kernel<D, PASSES>), grid, block, 0, s, S, y, a, b, o, g.Hk, g.Hv, g.C, bph);
+    hipLaunchKernelGGL((decode_kernel<D, PASSES, KDA>), grid, block, 0, s, S, y, a, b, o, g.Hk, g.Hv, g.C, bph);
     return hipGetLastError();
+}
+
+template <bool KDA>
+static hipError_t launch_decode_kind(const Geo& g, float* S, const float* y, const float* a, const float* b,
+                                     float* o, hipStream_t s) {
+    if (g.D == 128) {
+        // Few heads in flight (small batch): one row-quad per wave for the most waves.
+        if (static_cast<int64_t>(g.B) * g.Hv < 512)
+            return launch_decode_cfg<128, 1, KDA>(g, S, y, a, b, o, s);
+        return launch_decode_cfg<128, 2, KDA>(g, S, y, a, b, o, s);
+    }
+    return launch_decode_cfg<32, 1, KDA>(g, S, y, a, b, o, s);
 }
 
 hipError_t launch_decode(const Geo& g, float* S, const float* y, const float* a, const float* b, float* o,
                          hipStream_t s) {
-    if (g.D == 128) {
-        // Few heads in flight (small batch): one row-quad per wave for the most waves.
-        if (static_cast<int64_t>(g.B) * g.Hv < 512)
-            return launch_decode_cfg<128, 1>(g, S, y, a, b, o, s);
-        return launch_decode_cfg<128, 2>(g, S, y, a, b, o, s);
-    }
-    return launch_decode_cfg<32, 1>(g, S, y, a, b, o, s);
+    return launch_decode_kind<false>(g, S, y, a, b, o, s);
+}
+
+hipError_t launch_kda_decode(const Geo& g, float* S, const float* y, const float* a, const float* b, float* o,
+                             hipStream_t s) {
+    return launch_decode_kind<true>(g, S, y, a, b, o, s);
 }
 
 }  // namespace gdn

@@ -17,6 +17,11 @@ hipError_t launch_decode(const Geo& g, float* S, const float* y, const float* a,
                          hipStream_t s);
 hipError_t launch_token(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w, const void* x,
                         const float* a, const float* b, float* o, hipStream_t s);
+// The per-channel-decay step: a is [B][Hv][D] (one forget-gate input per key channel).
+hipError_t launch_kda_decode(const Geo& g, float* S, const float* y, const float* a, const float* b, float* o,
+                             hipStream_t s);
+hipError_t launch_kda_token(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w,
+                            const void* x, const float* a, const float* b, float* o, hipStream_t s);
 hipError_t launch_tree_tables(int n, const int32_t* parent, int32_t* depth, int32_t* order, int32_t* status,
                               hipStream_t s);
 size_t tree_ws_bytes(int B, int n, int Hk, int Hv, int D);

@@ -21,7 +21,8 @@
 
 namespace gdn {
 
-template <int D, int PASSES, typename Act>
+// KDA: the forget gate is per key channel, a is [B][Hv][D] (row_update_kda).
+template <int D, int PASSES, typename Act, bool KDA>
 __global__ __launch_bounds__(256) void token_kernel(float* __restrict__ S, const Act* __restrict__ tail_in,
                                                     Act* __restrict__ tail_out, const Act* __restrict__ w,
                                                     const Act* __restrict__ x, const float* __restrict__ a,
@@ -72,6 +73,17 @@ __global__ __launch_bounds__(256) void token_kernel(float* __restrict__ S, const
         traw[k] = Q::load(ts + static_cast<size_t>(chan[k]) * 4);
         xin[k] = xs[chan[k]];
         wraw[k] = Q::load(w + static_cast<size_t>(chan[k]) * 4);
+    }
+
+    // The per-channel gate inputs go before the state loads, so their gates are
+    // computed while the state is in flight.
+    float4 al[NV];
+    if constexpr (KDA) {
+        float4 araw[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            araw[j] = *reinterpret_cast<const float4*>(a + static_cast<size_t>(bh) * D + R::key(j, r));
+        kda_gates<D>(araw, al);
     }
 
     // then the state rows
@@ -125,8 +137,11 @@ __global__ __launch_bounds__(256) void token_kernel(float* __restrict__ S, const
         if (lane == 0)
             kq_s = kq;
     }
-    float alpha, beta;
-    gates(a[bh], b[bh], alpha, beta);
+    float alpha = 0.0f, beta;
+    if constexpr (KDA)
+        beta = write_gate(b[bh]);
+    else
+        gates(a[bh], b[bh], alpha, beta);
     __syncthreads();
 
     float4 kk[NV], qq[NV];
@@ -136,11 +151,18 @@ __global__ __launch_bounds__(256) void token_kernel(float* __restrict__ S, const
         qq[j] = *reinterpret_cast<const float4*>(qs + R::key(j, r));
     }
     const float kq = kq_s;
+    float4 ka[NV], qa[NV];
+    if constexpr (KDA)
+        kda_vectors<D>(al, kk, qq, ka, qa);
     float* oh = o + static_cast<size_t>(bh) * D;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const float v = ys[2 * D + row[p] - row_base];
-        const float out = row_update<D>(s[p], kk, qq, alpha, beta, v, kq);
+        float out;
+        if constexpr (KDA)
+            out = row_update_kda<D>(s[p], kk, ka, qa, al, beta, v, kq);
+        else
+            out = row_update<D>(s[p], kk, qq, alpha, beta, v, kq);
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             store_stream(Sh + row[p] * D + R::key(j, r), s[p][j]);
@@ -149,36 +171,43 @@ __global__ __launch_bounds__(256) void token_kernel(float* __restrict__ S, const
     }
 }
 
-template <int D, int PASSES, typename Act>
+template <int D, int PASSES, typename Act, bool KDA>
 static hipError_t launch_token_cfg(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w,
                                    const void* x, const float* a, const float* b, float* o, hipStream_t s) {
     constexpr int ROWS_WG = 4 * Row<D>::RPW * PASSES;
     const int bph = D / ROWS_WG;
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.B) * g.Hv * bph)), block(256);
-    hipLaunchKernelGGL((token_kernel<D, PASSES, Act>), grid, block, 0, s, S, static_cast<const Act*>(tail_in),
+    hipLaunchKernelGGL((token_kernel<D, PASSES, Act, KDA>), grid, block, 0, s, S, static_cast<const Act*>(tail_in),
                        static_cast<Act*>(tail_out), static_cast<const Act*>(w), static_cast<const Act*>(x), a, b, o,
                        g.Hk, g.Hv, g.C, bph);
     return hipGetLastError();
 }
 
-template <typename Act>
+template <typename Act, bool KDA>
 static hipError_t launch_token_act(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w,
                                    const void* x, const float* a, const float* b, float* o, hipStream_t s) {
     // Same geometry rule as the state step alone: two row-quads per wave once
     // there are enough (sequence, head) pairs to fill the chip.
     if (g.D == 128) {
         if (static_cast<int64_t>(g.B) * g.Hv < 512)
-            return launch_token_cfg<128, 1, Act>(g, S, tail_in, tail_out, w, x, a, b, o, s);
-        return launch_token_cfg<128, 2, Act>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+            return launch_token_cfg<128, 1, Act, KDA>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+        return launch_token_cfg<128, 2, Act, KDA>(g, S, tail_in, tail_out, w, x, a, b, o, s);
     }
-    return launch_token_cfg<32, 1, Act>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+    return launch_token_cfg<32, 1, Act, KDA>(g, S, tail_in, tail_out, w, x, a, b, o, s);
 }
 
 hipError_t launch_token(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w, const void* x,
                         const float* a, const float* b, float* o, hipStream_t s) {
     if (g.bf16)
-        return launch_token_act<uint16_t>(g, S, tail_in, tail_out, w, x, a, b, o, s);
-    return launch_token_act<float>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+        return launch_token_act<uint16_t, false>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+    return launch_token_act<float, false>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+}
+
+hipError_t launch_kda_token(const Geo& g, float* S, const void* tail_in, void* tail_out, const void* w,
+                            const void* x, const float* a, const float* b, float* o, hipStream_t s) {
+    if (g.bf16)
+        return launch_token_act<uint16_t, true>(g, S, tail_in, tail_out, w, x, a, b, o, s);
+    return launch_token_act<float, true>(g, S, tail_in, tail_out, w, x, a, b, o, s);
 }
 
 }  // namespace gdn

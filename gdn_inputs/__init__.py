@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "LayerShape", "TINY", "QWEN27B_LAYER", "normal_rows", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "random_tree", "random_leaf_path", "tree_depths",
-    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "kda_inputs", "Inputs",
+    "decode_inputs", "tree_inputs", "tree_batch_inputs", "prefill_inputs", "kda_inputs", "channel_gates", "Inputs",
     "GATE_REGIMES",
 ]
 
@@ -272,9 +272,15 @@ def kda_inputs(seed: int, shape: LayerShape, batch: int, steps: int, state_sigma
     from N(0,1) shifted by the regime's mean (its own stream, so a and b keep their
     meaning in every regime)."""
     x, _, b, w, state, tail = _common(seed, shape, batch, steps, state_sigma, tail_random, gates)
+    a = channel_gates(seed, shape, batch, steps, gates)
+    return Inputs(shape, batch, steps, x, a, b, w, state, tail)
+
+
+def channel_gates(seed: int, shape: LayerShape, batch: int, steps: int, gates: str = "normal") -> np.ndarray:
+    """The per-channel gate inputs of kda_inputs alone: [steps][batch][Hv][dk] float32."""
     Hv, dk = shape.num_v_heads, shape.head_k_dim
     a_mean, _ = GATE_REGIMES[gates]
     a = normal_rows(seed, S_A_CHANNEL, steps * batch * Hv, dk).reshape(steps, batch, Hv, dk)
     if a_mean:
         a += np.float32(a_mean)
-    return Inputs(shape, batch, steps, x, a, b, w, state, tail)
+    return a

@@ -135,6 +135,28 @@ gdn_status gdn_decode_token(const gdn_dims* d, float* state, const void* conv_ta
                             void* stream);
 
 /*
+ * gdn_kda_decode_step / gdn_kda_decode_token -- the per-channel-decay variant
+ * of the two calls above (the model-arch page's module list: a Kimi Delta
+ * Attention mixer with a CPU reference and GPU launches; the pages do not
+ * define it).  Everything is as in gdn_decode_step / gdn_decode_token except
+ * the forget gate, which is one value per key channel of each value head and
+ * scales the state's key columns before the delta correction:
+ *   alpha[c] = exp(-softplus(a[c]))
+ *   S <- S diag(alpha) + beta*(v - S diag(alpha) k^) k^T;  o = (S q^) / sqrt(dk)
+ * With every a[c] of a head equal to one value, this is the gated delta rule
+ * with that gate (to rounding; the two kernels order the products differently).
+ *   a  f32 [B][Hv][dk]   per-channel forget-gate inputs (read)
+ *   b  f32 [B][Hv]       write-gate inputs (read)
+ *   all other arguments, layouts and errors as in gdn_decode_step (y from
+ *   gdn_conv_update) and gdn_decode_token (fused conv, out-of-place tail).
+ */
+gdn_status gdn_kda_decode_step(const gdn_dims* d, float* state, const float* y,
+                               const float* a, const float* b, float* o, void* stream);
+gdn_status gdn_kda_decode_token(const gdn_dims* d, float* state, const void* conv_tail_in, void* conv_tail_out,
+                                const void* conv_w, const void* x, const float* a, const float* b, float* o,
+                                void* stream);
+
+/*
  * gdn_tree_verify -- one read-only pass over a draft tree of n_nodes tokens
  * per sequence (decode-loop diagram: a tree of up to 32 nodes verified in one
  * pass; section 8.1: the state must be branched for a tree of guesses; the
