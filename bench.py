@@ -410,11 +410,13 @@ def main():
             tb = tree_bytes(32, shape)
             res["tree_verify_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
                                       "nodes_per_s": 32 / us * 1e6, "bytes": tb, "launch": "hipGraph"}
-            us = graph_time_us(torch, lambda r: gdn.tree_verify_ut(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at,
-                                                                    bt, ot, st, tws), nrep)
-            res["tree_verify_ut_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
-                                         "nodes_per_s": 32 / us * 1e6, "bytes": tb, "launch": "hipGraph",
-                                         "call": "gdn_tree_verify_ut"}
+            # The UT form in one launch (no workspace) and in two (prep into a workspace).
+            for key, wsx in (("tree_verify_ut_n32", None), ("tree_verify_ut_ws_n32", tws)):
+                us = graph_time_us(torch, lambda r: gdn.tree_verify_ut(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at,
+                                                                        bt, ot, st, wsx), nrep)
+                res[key] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
+                            "nodes_per_s": 32 / us * 1e6, "bytes": tb, "launch": "hipGraph",
+                            "call": "gdn_tree_verify_ut", "workspace": wsx is not None}
         if "commit" in rows:
             us = graph_time_us(torch, lambda r: gdn.commit_path(d1, Sp[r % R], Tp[r % R], wt, parent, xt, at, bt,
                                                                  path, None, st), nrep)
@@ -458,12 +460,13 @@ def main():
         res["tree_verify_b64_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
                                       "nodes_per_s": B * 32 / us * 1e6, "bytes": tb, "launch": "hipGraph",
                                       "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
-        us = graph_time_us(torch, lambda r: gdn.tree_verify_ut(dB, S2[r % 2], T2[r % 2], wB, parentB, xB, aB, bB,
-                                                                oB, stB, wsB), 32, reps=2)
-        res["tree_verify_ut_b64_n32"] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
-                                         "nodes_per_s": B * 32 / us * 1e6, "bytes": tb, "launch": "hipGraph",
-                                         "call": "gdn_tree_verify_ut",
-                                         "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
+        for key, wsx in (("tree_verify_ut_b64_n32", None), ("tree_verify_ut_ws_b64_n32", wsB)):
+            us = graph_time_us(torch, lambda r: gdn.tree_verify_ut(dB, S2[r % 2], T2[r % 2], wB, parentB, xB, aB, bB,
+                                                                    oB, stB, wsx), 32, reps=2)
+            res[key] = {"us": us, "GBps": tb / us / 1e3, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
+                        "nodes_per_s": B * 32 / us * 1e6, "bytes": tb, "launch": "hipGraph",
+                        "call": "gdn_tree_verify_ut", "workspace": wsx is not None,
+                        "state_buffers": "2 batches of 64 (ping-pong, 403 MB)"}
         us = graph_time_us(torch, lambda r: gdn.commit_path(dB, S2[r % 2], T2[r % 2], wB, parentB, xB, aB, bB, pathB,
                                                              None, stB), 32, reps=2)
         cbt = commit_bytes(lens, shape)
@@ -499,12 +502,12 @@ def main():
             vb = block_bytes(kb, shape, B)
             res[f"block_verify_b{B}_k{kb}"] = {"us": us, "GBps": vb / us / 1e3, "frac_hbm": vb / us / 1e3 / HBM_PEAK_GBS,
                                                "tokens_per_s": B * kb / us * 1e6, "bytes": vb, "launch": "hipGraph"}
-            us = graph_time_us(torch, lambda r: gdn.block_verify_ut(dB, Sb[r % nbuf], Tb[r % nbuf], wB, xB, aB, bB,
-                                                                     oB, wsB), n, reps=2)
-            res[f"block_verify_ut_b{B}_k{kb}"] = {"us": us, "GBps": vb / us / 1e3,
-                                                  "frac_hbm": vb / us / 1e3 / HBM_PEAK_GBS,
-                                                  "tokens_per_s": B * kb / us * 1e6, "bytes": vb, "launch": "hipGraph",
-                                                  "call": "gdn_block_verify_ut"}
+            for key, wsx in ((f"block_verify_ut_b{B}_k{kb}", None), (f"block_verify_ut_ws_b{B}_k{kb}", wsB)):
+                us = graph_time_us(torch, lambda r: gdn.block_verify_ut(dB, Sb[r % nbuf], Tb[r % nbuf], wB, xB, aB,
+                                                                         bB, oB, wsx), n, reps=2)
+                res[key] = {"us": us, "GBps": vb / us / 1e3, "frac_hbm": vb / us / 1e3 / HBM_PEAK_GBS,
+                            "tokens_per_s": B * kb / us * 1e6, "bytes": vb, "launch": "hipGraph",
+                            "call": "gdn_block_verify_ut", "workspace": wsx is not None}
             if B == 64:
                 acc_np = np.array([(7 * s) % (kb + 1) for s in range(B)], np.int32)
                 acc = torch.from_numpy(acc_np).to(dev)

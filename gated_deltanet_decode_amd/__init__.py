@@ -211,29 +211,29 @@ def tree_verify(d: Dims, state, tail, w, parent, x, a, b, o, status=None, worksp
 
 
 def tree_verify_ut(d: Dims, state, tail, w, parent, x, a, b, o, status=None, workspace=None, stream=None) -> None:
-    """tree_verify in the UT form (one read of each checkpoint, MFMA products): the same
-    arguments; outputs equal decode's to rounding rather than bit for bit."""
-    _tree_verify("gdn_tree_verify_ut", d, state, tail, w, parent, x, a, b, o, status, workspace, stream)
+    """tree_verify in the UT form (one read of each checkpoint, MFMA products); outputs equal
+    decode's to rounding rather than bit for bit.  workspace None: one launch that prepares
+    nothing for commit_path_prepared; with a workspace, as tree_verify."""
+    _tree_verify("gdn_tree_verify_ut", d, state, tail, w, parent, x, a, b, o, status, workspace, stream,
+                 optional=True)
 
 
-def _tree_verify(name, d, state, tail, w, parent, x, a, b, o, status, workspace, stream) -> None:
+def _tree_verify(name, d, state, tail, w, parent, x, a, b, o, status, workspace, stream, optional=False) -> None:
     B = d.batch
     if parent.numel() % B:
         raise ValueError("parent must be [B][n_nodes]")
     n = parent.numel() // B
     Hv, dk, dv, Cc = d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
-    need = tree_workspace_bytes(d, n)
-    if workspace is None or workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("tree_verify needs a contiguous device workspace tensor")
-    ws_bytes = workspace.numel() * workspace.element_size()
-    if ws_bytes < need:
-        raise ValueError(f"workspace of {ws_bytes} bytes, need {need}")
+    if workspace is None and optional:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        ws_ptr, ws_bytes = _blob(workspace, tree_workspace_bytes(d, n), "workspace")
     _check(getattr(_lib, name)(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
                                _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
                                n, _t(parent, "parent", torch.int32, B * n), _t(x, "x", d.act_torch, B * n * Cc),
                                _t(a, "a", torch.float32, B * n * Hv), _t(b, "b", torch.float32, B * n * Hv),
                                _t(o, "o", torch.float32, B * n * Hv * dv), _opt(status, "tree_status", torch.int32, B),
-                               workspace.data_ptr(), ws_bytes, _stream(stream)), name)
+                               ws_ptr, ws_bytes, _stream(stream)), name)
 
 
 def commit_path(d: Dims, state, tail, w, parent, x, a, b, path, o=None, status=None, stream=None) -> None:
@@ -283,11 +283,13 @@ def block_workspace_bytes(d: Dims, k: int) -> int:
     return _lib.gdn_block_workspace_bytes(C.byref(d), k)
 
 
-def _block_common(d, x, workspace):
+def _block_common(d, x, workspace, optional=False):
     B, Cc = d.batch, d.C
     if x.numel() % (B * Cc):
         raise ValueError("x must be [B][k][C]")
     k = x.numel() // (B * Cc)
+    if workspace is None and optional:
+        return k, None, 0
     ptr, nbytes = _blob(workspace, block_workspace_bytes(d, k), "workspace")
     return k, ptr, nbytes
 
@@ -297,14 +299,15 @@ def block_verify(d: Dims, state, tail, w, x, a, b, o, workspace, stream=None) ->
     _block_verify("gdn_block_verify", d, state, tail, w, x, a, b, o, workspace, stream)
 
 
-def block_verify_ut(d: Dims, state, tail, w, x, a, b, o, workspace, stream=None) -> None:
-    """block_verify in the UT form: the same arguments; outputs equal decode's to rounding."""
-    _block_verify("gdn_block_verify_ut", d, state, tail, w, x, a, b, o, workspace, stream)
+def block_verify_ut(d: Dims, state, tail, w, x, a, b, o, workspace=None, stream=None) -> None:
+    """block_verify in the UT form; outputs equal decode's to rounding.  workspace None: one
+    launch that prepares nothing for block_commit_prepared."""
+    _block_verify("gdn_block_verify_ut", d, state, tail, w, x, a, b, o, workspace, stream, optional=True)
 
 
-def _block_verify(name, d, state, tail, w, x, a, b, o, workspace, stream) -> None:
+def _block_verify(name, d, state, tail, w, x, a, b, o, workspace, stream, optional=False) -> None:
     B, Hv, dk, dv, Cc = d.batch, d.num_v_heads, d.head_k_dim, d.head_v_dim, d.C
-    k, ptr, nbytes = _block_common(d, x, workspace)
+    k, ptr, nbytes = _block_common(d, x, workspace, optional)
     _check(getattr(_lib, name)(C.byref(d), _t(state, "state_ckpt", torch.float32, B * Hv * dv * dk),
                                _t(tail, "conv_tail", d.act_torch, B * Cc * 4), _t(w, "conv_w", d.act_torch, Cc * 4),
                                k, _t(x, "x", d.act_torch, B * k * Cc), _t(a, "a", torch.float32, B * k * Hv),

@@ -52,8 +52,10 @@ gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HI
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// ws_optional: the UT-form calls accept a NULL workspace (the one-launch form).
 gdn_status tree_verify_args(const gdn_dims* d, gdn::Geo& g, std::initializer_list<const void*> ptrs, int32_t n_nodes,
-                            const int32_t* tree_status, const void* workspace, size_t workspace_bytes) {
+                            const int32_t* tree_status, const void* workspace, size_t workspace_bytes,
+                            bool ws_optional = false) {
     gdn_status st = check_dims(d, g);
     if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
         st = GDN_ERR_SHAPE;
@@ -65,6 +67,8 @@ gdn_status tree_verify_args(const gdn_dims* d, gdn::Geo& g, std::initializer_lis
         st = GDN_ERR_TREE;
     if (st != GDN_OK)
         return st;
+    if (ws_optional && !workspace)
+        return GDN_OK;
     if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, n_nodes, g.Hk, g.Hv, g.D))
         return GDN_ERR_WORKSPACE;
     return aligned16(workspace) ? GDN_OK : GDN_ERR_ALIGN;
@@ -213,7 +217,7 @@ gdn_status gdn_tree_verify_ut(const gdn_dims* d, const float* state_ckpt, const 
                               float* o, int32_t* tree_status, void* workspace, size_t workspace_bytes, void* stream) {
     gdn::Geo g;
     const gdn_status st = tree_verify_args(d, g, {state_ckpt, conv_tail, conv_w, parent, x, a, b, o}, n_nodes,
-                                           tree_status, workspace, workspace_bytes);
+                                           tree_status, workspace, workspace_bytes, true);
     if (st != GDN_OK)
         return st;
     return launched(gdn::launch_tree_verify_ut(g, state_ckpt, conv_tail, conv_w, n_nodes, parent, x, a, b, o,
@@ -277,7 +281,8 @@ size_t gdn_block_workspace_bytes(const gdn_dims* d, int32_t k) {
 namespace {
 
 gdn_status block_args(const gdn_dims* d, gdn::Geo& g, std::initializer_list<const void*> ptrs, int32_t k,
-                      const void* o, const int32_t* status, const void* workspace, size_t workspace_bytes) {
+                      const void* o, const int32_t* status, const void* workspace, size_t workspace_bytes,
+                      bool ws_optional = false) {
     gdn_status st = check_dims(d, g);
     if (st == GDN_OK && (g.B > GDN_MAX_TREE_BATCH || g.Hv / g.Hk > 64))
         st = GDN_ERR_SHAPE;
@@ -289,6 +294,8 @@ gdn_status block_args(const gdn_dims* d, gdn::Geo& g, std::initializer_list<cons
         st = GDN_ERR_SHAPE;
     if (st != GDN_OK)
         return st;
+    if (ws_optional && !workspace)
+        return GDN_OK;
     if (!workspace || workspace_bytes < gdn::tree_ws_bytes(g.B, k, g.Hk, g.Hv, g.D))
         return GDN_ERR_WORKSPACE;
     return aligned16(workspace) ? GDN_OK : GDN_ERR_ALIGN;
@@ -316,7 +323,7 @@ gdn_status gdn_block_verify_ut(const gdn_dims* d, const float* state_ckpt, const
                                size_t workspace_bytes, void* stream) {
     gdn::Geo g;
     const gdn_status st = block_args(d, g, {state_ckpt, conv_tail, conv_w, x, a, b, o}, k, o, nullptr, workspace,
-                                     workspace_bytes);
+                                     workspace_bytes, true);
     if (st != GDN_OK)
         return st;
     return launched(gdn::launch_tree_verify_ut(g, state_ckpt, conv_tail, conv_w, k, nullptr, x, a, b, o, nullptr,

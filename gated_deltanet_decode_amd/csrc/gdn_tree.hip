@@ -742,18 +742,33 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
 // The arithmetic is reordered against token-by-token decode, so the outputs
 // agree with it to rounding, not bit for bit.
 //
-// One workgroup per (sequence, value head), four waves.  Each wave's share of
-// the checkpoint (D / 4 rows; for D = 32, 16 rows shared by two waves) is
-// loaded right after the q/k rows, in the operand layout of the final
-// product, and stays in flight while the small matrices are built.
-template <int D>
-struct UtSmem {
+// One workgroup per (sequence, value head), four waves, and no other launch:
+// the workgroup convolves the raw inputs of its q/k head's and its value
+// head's channels itself.  Every node's window lies on the node's own path,
+// so the workgroup stages the raw inputs of all its nodes and the four tail
+// entries as rows of one LDS table and convolves each node from the rows of
+// itself and its nearest ancestors.  Each wave's share of the checkpoint
+// (D / 4 rows; for D = 32, 16 rows shared by two waves) is loaded right after
+// the raw inputs, in the operand layout of the final product, and stays in
+// flight through the convolution and the small matrices.
+template <int D, typename Act>
+struct alignas(16) UtSmem {
     static constexpr int P = D + 4;           // bf16 row of D plus 8 bytes: a quarter-wave's reads hit distinct banks
     static constexpr int PS = kMaxNodes + 4;  // 16-byte aligned rows of the 32 x 32 matrices
-    __bf16 kh[kMaxNodes][P], kl[kMaxNodes][P];   // k = kh + kl, each part rounded to bf16
-    __bf16 qh[kMaxNodes][P], ql[kMaxNodes][P];   // q, then e
+    static constexpr int NCH = 3 * D;         // the q | k | v channels the workgroup convolves
+    static constexpr int XR = kMaxNodes + 4;  // staging rows: the nodes' raw inputs, then tail entries 0..3
+    union {
+        struct {                              // raw conv inputs, until every thread holds its outputs
+            Act x[XR][NCH];
+            Act w[NCH][4];
+        };
+        struct {                              // then the split operands
+            __bf16 kh[kMaxNodes][P], kl[kMaxNodes][P];   // k = kh + kl, each part rounded to bf16
+            __bf16 qh[kMaxNodes][P], ql[kMaxNodes][P];   // q, then e
+        };
+    };
     // Each 32 x 32 buffer holds two matrices whose lifetimes are separated by
-    // a barrier, so that three workgroups fit in a CU's LDS.
+    // a barrier, so that three workgroups fit in a CU's LDS (bf16 inputs).
     union {
         float rho[kMaxNodes][PS];   // until A and M are formed
         float t[kMaxNodes][PS];     // (I + A)^-1, after
@@ -766,6 +781,8 @@ struct UtSmem {
     float rg[kMaxNodes][PS];   // R diag(gamma)
     float al[kMaxNodes], be[kMaxNodes], gam[kMaxNodes];
     int32_t par[kMaxNodes];
+    int32_t src[kMaxNodes][4];   // staging rows of each node's conv window, oldest first
+    int32_t ok;
 };
 
 using ut_f4 = __attribute__((ext_vector_type(4))) float;
@@ -794,8 +811,473 @@ __device__ __forceinline__ ut_f4 ut_mma3(ut_bf8 ah, ut_bf8 al, ut_bf8 bh, ut_bf8
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
 }
 
+// Global channel of the workgroup's local channel lc: q of its q/k head, then
+// k, then v of its value head.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tree_ut_kernel(const float* __restrict__ Sc, int n,
+__device__ __forceinline__ int ut_channel(int lc, int g, int h, int Hk) {
+    return lc < D ? g * D + lc : lc < 2 * D ? Hk * D + g * D + (lc - D) : 2 * Hk * D + h * D + (lc - 2 * D);
+}
+
+template <int D, typename Act>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tree_ut_kernel(
+    const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
+    const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
+    const float* __restrict__ b, float* __restrict__ o, int32_t* __restrict__ status, int Hk, int Hv, int C) {
+    static_assert(D == 32 || D == 128, "head dims 32 and 128");
+    using f4 = ut_f4;
+    using bf8 = ut_bf8;
+    using Sm = UtSmem<D, Act>;
+    constexpr int NT = kMaxNodes;                 // nodes padded to two tiles of 16
+    constexpr int RT = D >= 64 ? D / 64 : 1;      // row tiles of 16 per wave in the last product
+    constexpr int NTW = D >= 64 ? 2 : 1;          // node tiles per wave in the last product
+    constexpr int KS = D / 16;                    // 16-wide blocks of the key dim
+    constexpr int ET = D / 32;                    // tiles of e per wave
+    constexpr int NCH = Sm::NCH;
+    constexpr int VPL = 16 / sizeof(Act);         // inputs per 16-byte load
+    constexpr int LPN = NCH / VPL;                // 16-byte loads per node row
+    constexpr int XL = (NT * LPN + 255) / 256;    // per thread
+    constexpr int TL = (NCH + 255) / 256;         // tail and weight quads per thread
+    constexpr int CPS = D / 8;                    // q (and k) channels per thread in the conv
+    __shared__ Sm sm;
+
+    // The index arithmetic is made to depend on every argument, so all the
+    // argument loads issue together (one kernel-argument round trip).
+    asm volatile("" : "+s"(Hv) : "s"(Sc), "s"(tail), "s"(w), "s"(n), "s"(parent), "s"(x), "s"(a), "s"(b), "s"(o),
+                 "s"(status), "s"(Hk), "s"(C));
+    const int id = xcd_packed_id(blockIdx.x, gridDim.x);
+    const int bq = id / Hv, h = id % Hv, g = h / (Hv / Hk);
+    const int m0 = bq * n;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int q = lane >> 4, c = lane & 15;
+    const int rb = D >= 64 ? wave * 16 * RT : 16 * (wave >> 1);   // first checkpoint row of this wave
+    const int u0 = D >= 64 ? 0 : (wave & 1);                      // first node tile of this wave
+
+    // Loads, all unconditional: the raw inputs of every node (padding nodes
+    // read node n - 1 and are zeroed after), the tail and the taps, the parent
+    // row and the gates first; then this wave's checkpoint rows, which stay in
+    // flight through the convolution and the small matrices.
+    using Q = Quad<Act>;
+    f4 xr[XL];
+#pragma unroll
+    for (int e = 0; e < XL; ++e) {
+        const int idx = min(tid + 256 * e, NT * LPN - 1), node = min(idx / LPN, n - 1), f = idx % LPN;
+        const int lc = f * VPL;
+        xr[e] = *reinterpret_cast<const f4*>(x + static_cast<size_t>(m0 + node) * C + ut_channel<D>(lc, g, h, Hk));
+    }
+    typename Q::raw tr[TL], wr[TL];
+#pragma unroll
+    for (int e = 0; e < TL; ++e) {
+        const int lc = min(tid + 256 * e, NCH - 1), gc = ut_channel<D>(lc, g, h, Hk);
+        tr[e] = Q::load(tail + (static_cast<size_t>(bq) * C + gc) * 4);
+        wr[e] = Q::load(w + static_cast<size_t>(gc) * 4);
+    }
+    const int gn = min(lane & (NT - 1), n - 1);
+    const float a_in = a[static_cast<size_t>(m0 + gn) * Hv + h];
+    const float b_in = b[static_cast<size_t>(m0 + gn) * Hv + h];
+    const int32_t pa_in = parent ? parent[m0 + gn] : gn - 1;
+    const float* Sh = Sc + (static_cast<size_t>(bq) * Hv + h) * D * D;
+    f4 sv[RT][KS];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+            sv[t][k] = __builtin_nontemporal_load(
+                reinterpret_cast<const f4*>(Sh + static_cast<size_t>(rb + 16 * t + c) * D + 16 * k + 4 * q));
+
+    // Stage the raw inputs: node rows as loaded, the tail turned into four
+    // rows (entry 0, the oldest, first), the taps as they are.
+#pragma unroll
+    for (int e = 0; e < XL; ++e) {
+        const int idx = tid + 256 * e;
+        if (NT * LPN % 256 == 0 || idx < NT * LPN)
+            *reinterpret_cast<f4*>(&sm.x[idx / LPN][(idx % LPN) * VPL]) = xr[e];
+    }
+#pragma unroll
+    for (int e = 0; e < TL; ++e) {
+        const int lc = tid + 256 * e;
+        if (NCH % 256 == 0 || lc < NCH) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sm.x[NT + j][lc] = Q::elem(tr[e], j);
+            Q::store(&sm.w[lc][0], wr[e]);
+        }
+    }
+    // Wave 0, lane i < n: node i's gates, its depth and nearest ancestors, the
+    // check of the parent row (parent[0] == -1, 0 <= parent[i] < i, depth <=
+    // 8; a block is a chain and always valid), the staging rows of its
+    // window, and rho and gamma: lane i clears row i of rho and walks up from
+    // node i (the gates and parents it reads were written by lanes of the same
+    // wave, whose LDS accesses are processed in order).
+    if (wave == 0) {
+        const bool live = lane < n;
+        int ok = 1, depth = 0, anc[3] = {-1, -1, -1};
+        if (parent == nullptr) {
+            depth = lane + 1;
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                anc[k] = lane - 1 - k;
+        } else {
+            const int p = live ? pa_in : -1;
+            const bool bad = live && (lane == 0 ? p != -1 : (p < 0 || p >= lane));
+            if (__any(bad)) {
+                ok = 0;
+            } else {
+                int cur = live ? lane : -1;
+#pragma unroll
+                for (int st = 0; st <= kMaxDepth; ++st) {
+                    depth += cur >= 0 ? 1 : 0;
+                    const int up = __shfl(p, cur >= 0 ? cur : 0, kWave);
+                    if (st < 3)
+                        anc[st] = cur >= 0 ? up : -1;
+                    cur = cur >= 0 ? up : -1;
+                }
+                ok = __any(live && cur >= 0) ? 0 : 1;
+            }
+        }
+        if (lane < NT) {
+            int src[4] = {0, 0, 0, 0};
+            if (ok && live) {
+                src[3] = lane;
+#pragma unroll
+                for (int k = 1; k <= 3; ++k)
+                    src[3 - k] = k <= depth - 1 ? anc[k - 1] : NT + 3 + depth - k;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                sm.src[lane][k] = src[k];
+            float al_v, be_v;
+            gates(a_in, b_in, al_v, be_v);
+            sm.al[lane] = live ? al_v : 1.0f;
+            sm.be[lane] = live ? be_v : 0.0f;
+            sm.par[lane] = live && ok ? pa_in : -1;
+#pragma unroll
+            for (int l = 0; l < NT; l += 4)
+                *reinterpret_cast<f4*>(&sm.rho[lane][l]) = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            float prod = 1.0f;
+            if (parent == nullptr) {
+                if (lane >= n)
+                    sm.rho[lane][lane] = 1.0f;
+                for (int l = live ? lane : -1; l >= 0; --l) {
+                    sm.rho[lane][l] = prod;
+                    prod *= sm.al[l];
+                }
+            } else {
+                int cur = lane;
+                for (int st = 0; st < NT && cur >= 0 && cur < NT; ++st) {
+                    sm.rho[lane][cur] = prod;
+                    prod *= sm.al[cur];
+                    cur = sm.par[cur];
+                }
+            }
+            sm.gam[lane] = prod;
+        }
+        if (lane == 0)
+            sm.ok = ok;
+    }
+    __syncthreads();
+    if (!sm.ok) {   // malformed tree: reported, nothing written
+        if (status && h == 0 && tid == 0)
+            status[bq] = 5;
+        return;
+    }
+    if (status && h == 0 && tid == 0)
+        status[bq] = 0;
+
+    // The conv.  q and k: thread (node tid / 8, part tid % 8) convolves CPS
+    // channels of each, and the eight threads of a node reduce its norms.  v:
+    // every lane convolves the values of the final product's B operand it
+    // holds: slot e of lane (q, c) is node 4 q + e, or 16 + 4 q + e - 4, at
+    // rows rb + 16 t + c.
+    float qn[CPS], kn[CPS];
+    {
+        const int node = tid >> 3, part = tid & 7;
+        int srow[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            srow[k] = sm.src[node][k];
+        float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+        for (int j4 = 0; j4 < CPS; j4 += 4) {
+            const int l0 = part * CPS + j4;
+            float xq[4][4], xk[4][4];   // [tap][channel]
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                Q::to_float(Q::load(&sm.x[srow[k]][l0]), xq[k]);
+                Q::to_float(Q::load(&sm.x[srow[k]][D + l0]), xk[k]);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float wf[4], win[4];
+                Q::to_float(Q::load(&sm.w[l0 + jj][0]), wf);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    win[k] = xq[k][jj];
+                const float yq = node < n ? conv_silu(wf, win) : 0.0f;
+                Q::to_float(Q::load(&sm.w[D + l0 + jj][0]), wf);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    win[k] = xk[k][jj];
+                const float yk = node < n ? conv_silu(wf, win) : 0.0f;
+                qn[j4 + jj] = yq;
+                kn[j4 + jj] = yk;
+                sq = __builtin_fmaf(yq, yq, sq);
+                sk = __builtin_fmaf(yk, yk, sk);
+            }
+        }
+        sq = group_sum<8>(sq);
+        sk = group_sum<8>(sk);
+        const float rq = __builtin_amdgcn_rsqf(sq + kEps), rk = __builtin_amdgcn_rsqf(sk + kEps);
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) {
+            qn[j] *= rq;
+            kn[j] *= rk;
+        }
+    }
+    float vv[RT][8];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int lc = 2 * D + rb + 16 * t + c;
+        float wf[4];
+        Q::to_float(Q::load(&sm.w[lc][0]), wf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int node = e < 4 ? 4 * q + e : 12 + 4 * q + e;
+            float win[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                win[k] = widen(sm.x[sm.src[node][k]][lc]);
+            vv[t][e] = node < n ? conv_silu(wf, win) : 0.0f;
+        }
+    }
+    __syncthreads();   // the staged inputs are dead: the split operands take their place
+    {
+        const int node = tid >> 3, part = tid & 7;
+#pragma unroll
+        for (int j0 = 0; j0 < CPS; j0 += 4) {
+            ut_bf4 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ut_split_at(qn[j0 + j], hi, lo, j);
+            *reinterpret_cast<ut_bf4*>(&sm.qh[node][part * CPS + j0]) = hi;
+            *reinterpret_cast<ut_bf4*>(&sm.ql[node][part * CPS + j0]) = lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ut_split_at(kn[j0 + j], hi, lo, j);
+            *reinterpret_cast<ut_bf4*>(&sm.kh[node][part * CPS + j0]) = hi;
+            *reinterpret_cast<ut_bf4*>(&sm.kl[node][part * CPS + j0]) = lo;
+        }
+    }
+    __syncthreads();
+
+    // Every wave takes one 16x16 tile (I, J) of K K^T and of Q K^T, and forms
+    // A and M on it from the gates on the ancestor paths (rho is 0 off them).
+    // Tile (0, 1) lies above the diagonal, where neither has an entry.
+    {
+        const int I = wave >> 1, J = wave & 1;
+        f4 gk0 = {0.0f, 0.0f, 0.0f, 0.0f}, gk1 = gk0, gq0 = gk0, gq1 = gk0;
+        if (!(I == 0 && J == 1)) {
+#pragma unroll
+            for (int m = 0; m < KS / 2; ++m) {
+                const int c0 = 32 * m + 4 * q, c1 = c0 + 16;
+                const bf8 akh = ut_cat(&sm.kh[16 * I + c][c0], &sm.kh[16 * I + c][c1]);
+                const bf8 akl = ut_cat(&sm.kl[16 * I + c][c0], &sm.kl[16 * I + c][c1]);
+                const bf8 aqh = ut_cat(&sm.qh[16 * I + c][c0], &sm.qh[16 * I + c][c1]);
+                const bf8 aql = ut_cat(&sm.ql[16 * I + c][c0], &sm.ql[16 * I + c][c1]);
+                const bf8 bkh = ut_cat(&sm.kh[16 * J + c][c0], &sm.kh[16 * J + c][c1]);
+                const bf8 bkl = ut_cat(&sm.kl[16 * J + c][c0], &sm.kl[16 * J + c][c1]);
+                gk0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akh, bkh, gk0, 0, 0, 0);
+                gq0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqh, bkh, gq0, 0, 0, 0);
+                gk1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akh, bkl, gk1, 0, 0, 0);
+                gq1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqh, bkl, gq1, 0, 0, 0);
+                gk1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akl, bkh, gk1, 0, 0, 0);
+                gq1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aql, bkh, gq1, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * I + 4 * q + v, l = 16 * J + c;
+            const float r = sm.rho[i][l];
+            sm.ga[i][l] = l == i ? 0.0f : sm.be[i] * r * (gk0[v] + gk1[v]);
+            sm.gm[i][l] = r * (gq0[v] + gq1[v]);
+        }
+    }
+    __syncthreads();
+
+    // (I + A)^-1: the two diagonal 16x16 blocks by substitution (wave 0, lane =
+    // (block, column)); the block above the diagonal is 0.
+    if (wave == 0 && lane < NT) {
+        const int b0 = 16 * (lane >> 4), j = lane & 15;
+        float X[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float arow[16];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f4 a4 = *reinterpret_cast<const f4*>(&sm.ga[b0 + i][b0 + 4 * p]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    arow[4 * p + e] = a4[e];
+            }
+            float s = i == j ? 1.0f : 0.0f;
+#pragma unroll
+            for (int k = 0; k < i; ++k)
+                s = __builtin_fmaf(-arow[k], X[k], s);
+            X[i] = s;
+            sm.t[b0 + i][b0 + j] = s;
+        }
+    } else if (wave == 1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            sm.t[4 * q + v][16 + c] = 0.0f;
+    }
+    __syncthreads();
+    // the block below it: T_10 = -T_11 (A_10 T_00)
+    if (wave == 0) {
+        f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ga[16 + c][4 * q + s], sm.t[4 * q + s][c], z, 0, 0, 0);
+        f4 tt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            tt = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.t[16 + c][16 + 4 * q + s], z[s], tt, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            sm.t[16 + 4 * q + v][c] = -tt[v];
+    }
+    __syncthreads();
+
+    // R = M (I + A)^-1 diag(beta) and R diag(gamma), one 16x16 tile per wave.
+    {
+        const int I = wave >> 1, J = wave & 1;
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!(I == 0 && J == 1)) {
+#pragma unroll
+            for (int K = 0; K < 2; ++K)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.gm[16 * I + c][16 * K + 4 * q + s],
+                                                               sm.t[16 * K + 4 * q + s][16 * J + c], acc, 0, 0, 0);
+        }
+        const float bc = sm.be[16 * J + c], gc = sm.gam[16 * J + c];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float rv = acc[v] * bc;
+            sm.r[16 * I + 4 * q + v][16 * J + c] = rv;
+            sm.rg[16 * I + 4 * q + v][16 * J + c] = rv * gc;
+        }
+    }
+    __syncthreads();
+
+    // e = gamma q - (R diag(gamma)) K, written over q; and the accumulators of
+    // the last product start at R V.  Both on split bf16 MFMA with the 32
+    // nodes as k: slot e of lane (q, c) is node 4 q + e, or 16 + 4 q + e - 4.
+    auto row_split = [&](const float (*M)[Sm::PS], int row, bf8& hi, bf8& lo) {
+        const f4 x0 = *reinterpret_cast<const f4*>(&M[row][4 * q]);
+        const f4 x1 = *reinterpret_cast<const f4*>(&M[row][16 + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ut_split_at(x0[e], hi, lo, e);
+            ut_split_at(x1[e], hi, lo, 4 + e);
+        }
+    };
+#pragma unroll
+    for (int e = 0; e < ET; ++e) {
+        const int tau = wave * ET + e, U = tau & 1, Ct = tau >> 1, col = 16 * Ct + c;
+        bf8 ah, al;
+        row_split(sm.rg, 16 * U + c, ah, al);
+        bf8 bh, bl;   // k of the slot nodes, one column: 2-byte reads down the rows
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int l = e < 4 ? 4 * q + e : 12 + 4 * q + e;
+            bh[e] = sm.kh[l][col];
+            bl[e] = sm.kl[l][col];
+        }
+        const f4 z = ut_mma3(ah, al, bh, bl, f4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * U + 4 * q + v;
+            const float qv = static_cast<float>(sm.qh[i][col]) + static_cast<float>(sm.ql[i][col]);
+            ut_split(sm.gam[i] * qv - z[v], sm.qh[i][col], sm.ql[i][col]);
+        }
+    }
+    f4 acc[RT][NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+        bf8 ah, al;
+        row_split(sm.r, 16 * (u0 + u) + c, ah, al);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            bf8 vh, vl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ut_split_at(vv[t][e], vh, vl, e);
+            acc[t][u] = ut_mma3(ah, al, vh, vl, f4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+    }
+    __syncthreads();
+
+    // o = s (E S_c^T + R V) over this wave's rows, E and the checkpoint rows
+    // split alike.  Lane (q, c) holds, for k-step m, the columns 32 m + 4 q +
+    // 0..3 and 32 m + 16 + 4 q + 0..3 of its row, in both operands.
+#pragma unroll
+    for (int m = 0; m < KS / 2; ++m) {
+        bf8 shi[RT], slo[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ut_split_at(sv[t][2 * m + e / 4][e % 4], shi[t], slo[t], e);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            const int row = 16 * (u0 + u) + c, c0 = 32 * m + 4 * q;
+            const bf8 ah = ut_cat(&sm.qh[row][c0], &sm.qh[row][c0 + 16]);
+            const bf8 al = ut_cat(&sm.ql[row][c0], &sm.ql[row][c0 + 16]);
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                acc[t][u] = ut_mma3(ah, al, shi[t], slo[t], acc[t][u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NTW; ++u)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int node = 16 * (u0 + u) + 4 * q + v;
+                if (node < n)
+                    o[(static_cast<size_t>(m0 + node) * Hv + h) * D + rb + 16 * t + c] = Scale<D>::value * acc[t][u][v];
+            }
+}
+
+// The two-launch form of the same verify: the prep launch convolves and
+// normalises every node's operands into the workspace (where a prepared
+// commit can read them), spread over many workgroups, and the UT workgroup
+// reads them from there.
+template <int D>
+struct UtWsSmem {
+    static constexpr int P = D + 4;           // bf16 row of D plus 8 bytes: a quarter-wave's reads hit distinct banks
+    static constexpr int PS = kMaxNodes + 4;  // 16-byte aligned rows of the 32 x 32 matrices
+    __bf16 kh[kMaxNodes][P], kl[kMaxNodes][P];   // k = kh + kl, each part rounded to bf16
+    __bf16 qh[kMaxNodes][P], ql[kMaxNodes][P];   // q, then e
+    // Each 32 x 32 buffer holds two matrices whose lifetimes are separated by
+    // a barrier, so that three workgroups fit in a CU's LDS.
+    union {
+        float rho[kMaxNodes][PS];   // until A and M are formed
+        float t[kMaxNodes][PS];     // (I + A)^-1, after
+    };
+    union {
+        float ga[kMaxNodes][PS];    // A, until (I + A)^-1 is complete
+        float r[kMaxNodes][PS];     // R, after
+    };
+    float gm[kMaxNodes][PS];   // M
+    float rg[kMaxNodes][PS];   // R diag(gamma)
+    float al[kMaxNodes], be[kMaxNodes], gam[kMaxNodes];
+    int32_t par[kMaxNodes];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tree_ut_ws_kernel(const float* __restrict__ Sc, int n,
                                                       const int32_t* __restrict__ parent, TreeWs ws,
                                                       float* __restrict__ o, int Hk, int Hv) {
     static_assert(D == 32 || D == 128, "head dims 32 and 128");
@@ -806,7 +1288,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     constexpr int NTW = D >= 64 ? 2 : 1;          // node tiles per wave in the last product
     constexpr int KS = D / 16;                    // 16-wide blocks of the key dim
     constexpr int ET = D / 32;                    // tiles of e per wave
-    __shared__ UtSmem<D> sm;
+    __shared__ UtWsSmem<D> sm;
 
     // The index arithmetic is made to depend on every argument, so all the
     // argument loads issue together (one kernel-argument round trip).
@@ -1005,7 +1487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     // e = gamma q - (R diag(gamma)) K, written over q; and the accumulators of
     // the last product start at R V.  Both on split bf16 MFMA with the 32
     // nodes as k: slot e of lane (q, c) is node 4 q + e, or 16 + 4 q + e - 4.
-    auto row_split = [&](const float (*M)[UtSmem<D>::PS], int row, bf8& hi, bf8& lo) {
+    auto row_split = [&](const float (*M)[UtWsSmem<D>::PS], int row, bf8& hi, bf8& lo) {
         const f4 x0 = *reinterpret_cast<const f4*>(&M[row][4 * q]);
         const f4 x1 = *reinterpret_cast<const f4*>(&M[row][16 + 4 * q]);
 #pragma unroll
@@ -1085,10 +1567,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
             }
 }
 
-// The UT-form verify of a tree, or of a block when parent is null.
+// The UT-form verify of a tree, or of a block when parent is null.  With no
+// workspace, the one launch; with one, the prep launch fills it (for a
+// prepared commit to read) and the UT kernel reads its operands from it.
+// Measured on the 27B-class layer, one launch against two: 16.0 us against
+// 15.3 at one tree, 23.7 against 31.0 at 8, 104 against 120 at 64.
 hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail, const void* w, int n,
                                  const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                                  int32_t* status, void* ws, hipStream_t s) {
+    if (ws == nullptr)
+        return dispatch(g, [&](auto dtag, auto atag) {
+            constexpr int D = decltype(dtag)::value;
+            using Act = decltype(atag);
+            hipLaunchKernelGGL((tree_ut_kernel<D, Act>), dim3(static_cast<unsigned>(g.B * g.Hv)), dim3(256), 0, s,
+                               S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                               static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C);
+        });
     const TreeWs W = tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D);
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
@@ -1099,7 +1593,7 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
         return e;
     return dispatch(g, [&](auto dtag, auto) {
         constexpr int D = decltype(dtag)::value;
-        hipLaunchKernelGGL((tree_ut_kernel<D>), dim3(static_cast<unsigned>(g.B * g.Hv)), dim3(256), 0, s, S, n,
+        hipLaunchKernelGGL((tree_ut_ws_kernel<D>), dim3(static_cast<unsigned>(g.B * g.Hv)), dim3(256), 0, s, S, n,
                            parent, W, o, g.Hk, g.Hv);
     });
 }

@@ -74,12 +74,13 @@ def test_decode_chained_steps(gates):
 
 
 @pytest.mark.parametrize("gates", REGIMES)
-@pytest.mark.parametrize("ut", [False, True], ids=["walk", "ut"])
+@pytest.mark.parametrize("ut", [False, True, "one_launch"], ids=["walk", "ut", "ut_one_launch"])
 def test_tree_verify_and_commit(gates, ut):
     """Three 32-node trees of the 27B-class layer: every node's o (per node, normwise)
-    against the oracle's path replay, in the exact-walk and the UT form; the commit of
-    each accepted path against the oracle and, bit for bit, against the walk's path
-    rows and a token-by-token replay."""
+    against the oracle's path replay, in the exact-walk and the UT form (with a
+    workspace, and in one launch without); the commit of each accepted path against
+    the oracle and, bit for bit, against the walk's path rows and a token-by-token
+    replay (after the one-launch form, which prepares nothing, gdn_commit_path)."""
     import gated_deltanet_decode_amd as gdn
     from tests.gpu_util import act_to_host, i32_to_dev
     from tests.test_gpu_tree_batch import batch_case, decode_path, one_case, row_len
@@ -90,14 +91,18 @@ def test_tree_verify_and_commit(gates, ut):
     o = torch.full((B, n, 48, 128), float("nan"), device="cuda")
     st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(gdn.tree_workspace_bytes(d, n), dtype=torch.uint8, device="cuda")
+    one = ut == "one_launch"
     (gdn.tree_verify_ut if ut else gdn.tree_verify)(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"],
-                                                    c["b"], o, st, ws)
+                                                    c["b"], o, st, None if one else ws)
     path = inp.extra["path"]
     S, tail = c["S"].clone(), c["tail"].clone()
     L = path.shape[1]
     oc = torch.full((B, L, 48, 128), float("nan"), device="cuda")
     cst = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-    gdn.commit_path_prepared(d, S, tail, c["parent"], c["x"], i32_to_dev(path), ws, oc, cst)
+    if one:
+        gdn.commit_path(d, S, tail, c["w"], c["parent"], c["x"], c["a"], c["b"], i32_to_dev(path), oc, cst)
+    else:
+        gdn.commit_path_prepared(d, S, tail, c["parent"], c["x"], i32_to_dev(path), ws, oc, cst)
     torch.cuda.synchronize()
     assert (st.cpu().numpy() == 0).all() and (cst.cpu().numpy() == 0).all()
     og = o.cpu().numpy()
@@ -121,14 +126,16 @@ def test_tree_verify_and_commit(gates, ut):
         assert _same_bits(oc[s, :Ls], o_d)
         if not ut:
             assert _same_bits(o[s, path[s, Ls - 1]], o_d[-1]), f"sequence {s}: walk row != decode row"
-    print(f"[gate regimes] tree {'ut' if ut else 'walk'} {gates}: worst normwise error {worst:.3e}")
+    print(f"[gate regimes] tree {'ut one launch' if one else 'ut' if ut else 'walk'} {gates}: "
+          f"worst normwise error {worst:.3e}")
 
 
 @pytest.mark.parametrize("gates", REGIMES)
 def test_block_verify_and_commit(gates):
-    """32-token blocks at batch 2: the walk and the UT form against the oracle's chained
-    decode (per position, normwise), the walk bit for bit against decode, and a commit
-    of 21 tokens bit for bit against decode."""
+    """32-token blocks at batch 2: the walk and the UT form (with a workspace, and in
+    one launch without) against the oracle's chained decode (per position, normwise),
+    the walk bit for bit against decode, and a commit of 21 tokens bit for bit against
+    decode."""
     import gated_deltanet_decode_amd as gdn
     from tests.test_gpu_block import commit, decode, dev, verify
     B, k = 2, 32
@@ -139,13 +146,15 @@ def test_block_verify_and_commit(gates):
     o_ut = torch.full_like(o_walk, float("nan"))
     ws = torch.empty(gdn.block_workspace_bytes(d, k), dtype=torch.uint8, device="cuda")
     gdn.block_verify_ut(d, c["S"], c["T"], c["w"], c["x"], c["a"], c["b"], o_ut, ws)
+    o_one = torch.full_like(o_walk, float("nan"))
+    gdn.block_verify_ut(d, c["S"], c["T"], c["w"], c["x"], c["a"], c["b"], o_one)
     torch.cuda.synchronize()
     outs, states, tails = decode(c, k)
     worst = 0.0
     for s in range(B):
         o_r, _, _ = oracle.run(inp.shape, inp.state[s], inp.tail[s], inp.w, inp.x[:, s], inp.a[:, s], inp.b[:, s])
         for t in range(k):
-            for og in (o_walk, o_ut):
+            for og in (o_walk, o_ut, o_one):
                 err = normwise(og[s, t].cpu().numpy(), o_r[t])
                 worst = max(worst, err)
                 assert err < TOL, f"sequence {s} position {t}: error {err:.3e}"

@@ -1,4 +1,5 @@
-"""GPU tree and block verify in the UT form (gdn_tree_verify_ut, gdn_block_verify_ut).
+"""GPU tree and block verify in the UT form (gdn_tree_verify_ut, gdn_block_verify_ut),
+in both of its forms: one launch (no workspace) and two (prep into a workspace).
 
 The UT form reorders the arithmetic, so it is held to the oracle's per-node
 path replay within 1e-4 normwise (per node: over that node's heads and rows),
@@ -24,14 +25,19 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
 
-def verify(c, B, n, ut=True):
+FORMS = ["one_launch", "workspace"]
+
+
+def verify(c, B, n, ut=True, form="one_launch"):
+    """form: the UT form's one launch (no workspace) or its two (prep into a workspace)."""
     import gated_deltanet_decode_amd as gdn
     d = c["d"]
     o = torch.full((B, n, d.num_v_heads, d.head_v_dim), float("nan"), device="cuda")
     st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(gdn.tree_workspace_bytes(d, n), dtype=torch.uint8, device="cuda")
     f = gdn.tree_verify_ut if ut else gdn.tree_verify
-    f(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"], c["b"], o, st, ws)
+    f(d, c["S"], c["tail"], c["w"], c["parent"], c["x"], c["a"], c["b"], o, st,
+      None if ut and form == "one_launch" else ws)
     torch.cuda.synchronize()
     return o, st.cpu().numpy()
 
@@ -54,11 +60,12 @@ def oracle_tree(inp, s, parent=None):
                                             (TINY, 3, 9, 205), (QWEN27B_LAYER, 6, 32, 206), (TINY, 70, 23, 207)],
                          ids=["27b_B1", "27b_B3", "tiny_B4", "tiny_n17", "27b_n1", "tiny_n9", "27b_B6",
                               "tiny_B70"])
-def test_ut_verify_matches_oracle(shape, B, n, seed):
+@pytest.mark.parametrize("form", FORMS)
+def test_ut_verify_matches_oracle(shape, B, n, seed, form):
     inp = gi.tree_batch_inputs(seed, shape, B, n)
     c = batch_case(inp)
     S0, T0 = c["S"].clone(), c["tail"].clone()
-    o, st = verify(c, B, n)
+    o, st = verify(c, B, n, form=form)
     assert (st == 0).all()
     assert torch.equal(c["S"], S0) and torch.equal(c["tail"], T0), "verify wrote the checkpoint"
     og = o.cpu().numpy()
@@ -67,24 +74,26 @@ def test_ut_verify_matches_oracle(shape, B, n, seed):
 
 
 @pytest.mark.parametrize("shape", [QWEN27B_LAYER, TINY], ids=["27b", "tiny"])
-def test_ut_verify_matches_the_exact_walk(shape):
+@pytest.mark.parametrize("form", FORMS)
+def test_ut_verify_matches_the_exact_walk(shape, form):
     B, n = 4, 32
     inp = gi.tree_batch_inputs(210, shape, B, n)
     c = batch_case(inp)
-    o_ut, _ = verify(c, B, n)
+    o_ut, _ = verify(c, B, n, form=form)
     o_w, _ = verify(c, B, n, ut=False)
     for s in range(B):
         per_node(o_ut[s].cpu().numpy(), o_w[s].cpu().numpy().astype(np.float64), f"sequence {s}")
 
 
 @pytest.mark.parametrize("B", [3, 6], ids=["B3", "B6"])
-def test_malformed_tree_in_one_sequence(B):
+@pytest.mark.parametrize("form", FORMS)
+def test_malformed_tree_in_one_sequence(B, form):
     n = 32
     inp = gi.tree_batch_inputs(211, QWEN27B_LAYER, B, n)
     parent = inp.extra["parent"].copy()
     parent[1, 7] = 9                       # a parent after its child
     c = batch_case(inp, parent)
-    o, st = verify(c, B, n)
+    o, st = verify(c, B, n, form=form)
     assert list(st) == [0, 5] + [0] * (B - 2)
     assert torch.isnan(o[1]).all(), "a malformed tree's outputs were written"
     og = o.cpu().numpy()
@@ -95,7 +104,8 @@ def test_malformed_tree_in_one_sequence(B):
 @pytest.mark.parametrize("shape,B,k", [(QWEN27B_LAYER, 2, 32), (TINY, 3, 32), (QWEN27B_LAYER, 2, 1),
                                        (TINY, 2, 13), (QWEN27B_LAYER, 6, 32)],
                          ids=["27b_k32", "tiny_k32", "27b_k1", "tiny_k13", "27b_B6_k32"])
-def test_ut_block_verify_matches_oracle(shape, B, k):
+@pytest.mark.parametrize("form", FORMS)
+def test_ut_block_verify_matches_oracle(shape, B, k, form):
     import gated_deltanet_decode_amd as gdn
     from tests.gpu_util import act_to_dev, dims_of, f32_to_dev
     inp = gi.decode_inputs(220 + k, shape, B, k, state_sigma=0.1, tail_random=True)
@@ -104,7 +114,7 @@ def test_ut_block_verify_matches_oracle(shape, B, k):
     o = torch.full((B, k, shape.num_v_heads, shape.head_v_dim), float("nan"), device="cuda")
     ws = torch.empty(gdn.block_workspace_bytes(d, k), dtype=torch.uint8, device="cuda")
     gdn.block_verify_ut(d, S, T, act_to_dev(inp.w), act_to_dev(seq_major(inp.x)), f32_to_dev(seq_major(inp.a)),
-                        f32_to_dev(seq_major(inp.b)), o, ws)
+                        f32_to_dev(seq_major(inp.b)), o, None if form == "one_launch" else ws)
     torch.cuda.synchronize()
     og = o.cpu().numpy()
     for s in range(B):
@@ -112,13 +122,14 @@ def test_ut_block_verify_matches_oracle(shape, B, k):
         per_node(og[s], o_r, f"sequence {s}")
 
 
-def test_batch64_full_size_sampled():
-    """The 27B-class layer, 64 trees of 32 nodes (the launch the bench times): four
-    sequences against the oracle; all 64 against the exact walk."""
+@pytest.mark.parametrize("form", FORMS)
+def test_batch64_full_size_sampled(form):
+    """The 27B-class layer, 64 trees of 32 nodes (the one-launch form is the launch the
+    bench times): four sequences against the oracle; all 64 against the exact walk."""
     B, n = 64, 32
     inp = gi.tree_batch_inputs(230, QWEN27B_LAYER, B, n)
     c = batch_case(inp)
-    o, st = verify(c, B, n)
+    o, st = verify(c, B, n, form=form)
     assert (st == 0).all()
     og = o.cpu().numpy()
     for s in (0, 21, 42, 63):

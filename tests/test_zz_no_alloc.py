@@ -45,9 +45,11 @@ def _both(inp):
     return o, st, o_ref, st_ref
 
 
-def test_two_calls_in_a_row_second_smaller():
-    big = gi.tree_batch_inputs(400, QWEN27B_LAYER, 8, 32)          # 10.7 MB of operands
-    small = gi.tree_batch_inputs(401, QWEN27B_LAYER, 3, 17)        # the second call, smaller
+@pytest.mark.parametrize("big_batch,small_shape,small_batch", [(8, QWEN27B_LAYER, 3), (1, TINY, 3)],
+                         ids=["27b_eight_trees_then_three", "27b_one_tree_then_three_tiny"])
+def test_two_calls_in_a_row_second_smaller(big_batch, small_shape, small_batch):
+    big = gi.tree_batch_inputs(400, QWEN27B_LAYER, big_batch, 32)
+    small = gi.tree_batch_inputs(401, small_shape, small_batch, 17)   # the second call, smaller
     for inp in (big, small):
         o, st, o_ref, st_ref = _both(inp)
         assert (st.cpu().numpy() == 0).all() and (st_ref.cpu().numpy() == 0).all()
