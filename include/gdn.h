@@ -201,10 +201,19 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
  * "earlier in the chunk").  No node's state is built: each sequence's
  * checkpoint enters once, as one product with 32 derived query vectors per
  * value head, and the small per-head matrices run on fp32 MFMA.  The same
- * arguments, workspace, status and error behaviour as gdn_tree_verify; the
- * outputs agree with token-by-token decode to rounding (within 1e-4 normwise
- * of the sequential definition), not bit for bit.  A commit of the accepted
- * path (gdn_commit_path) is exact either way: it replays the path.
+ * arguments, status and error behaviour as gdn_tree_verify, except that the
+ * workspace is optional:
+ *   workspace NULL   one launch: each (sequence, value head) workgroup
+ *                    convolves, normalises and gates its own nodes' operands;
+ *                    nothing is prepared for gdn_commit_path_prepared (commit
+ *                    with gdn_commit_path).  The faster form from two trees on.
+ *   workspace given  (>= gdn_tree_workspace_bytes) two launches: the nodes'
+ *                    operands are prepared in the workspace, as by
+ *                    gdn_tree_verify, and gdn_commit_path_prepared may follow.
+ * The outputs agree with token-by-token decode to rounding (within 1e-4
+ * normwise of the sequential definition), not bit for bit, and the two forms
+ * round differently.  A commit of the accepted path is exact either way: it
+ * replays the path.
  */
 gdn_status gdn_tree_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
                               const void* conv_w, int32_t n_nodes, const int32_t* parent,
@@ -313,7 +322,8 @@ gdn_status gdn_block_verify(const gdn_dims* d, const float* state_ckpt, const vo
 /*
  * gdn_block_verify_ut -- gdn_block_verify in the UT form (a block is the chain
  * tree; see gdn_tree_verify_ut): the same arguments and errors, outputs equal
- * to decode's to rounding.
+ * to decode's to rounding.  As there, workspace may be NULL (one launch, nothing
+ * prepared for gdn_block_commit_prepared).
  */
 gdn_status gdn_block_verify_ut(const gdn_dims* d, const float* state_ckpt, const void* conv_tail,
                                const void* conv_w, int32_t k, const void* x, const float* a, const float* b,
@@ -432,7 +442,9 @@ gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void*
  * library-held device array of GDN_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU,
  * held from the library's first use on that GPU until the process ends.  The
  * caller still passes inputs and outputs; arguments, outputs, statuses and
- * errors are gdn_tree_verify_ut's, and the outputs are bit-identical to it.
+ * errors are gdn_tree_verify_ut's with a workspace (the two-launch form), and
+ * the outputs are bit-identical to it.  (gdn_tree_verify_ut with no workspace
+ * allocates nothing either; this call gives the two-launch form's bits.)
  *   GDN_ERR_WORKSPACE  gdn_tree_workspace_bytes(d, n_nodes) exceeds the array
  *                      (at 16 q/k and 48 value heads of 128 and 32 nodes: more
  *                      than 12 sequences)
