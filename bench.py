@@ -211,6 +211,10 @@ def main():
 
     # ---------------------------------------------------------------- inputs
     t0 = time.time()
+
+    def note(what):
+        """Progress on stderr, so a long run shows it is alive (the JSON line is stdout's only line)."""
+        print(f"[bench] {what} at {time.time() - t0:.0f} s", file=sys.stderr, flush=True)
     steps_total = K + W
     inp = gi.decode_inputs(1, shape, 1, steps_total, state_sigma=0.1, tail_random=True)
     pool = gi.decode_inputs(101, shape, R, 1, state_sigma=0.1, tail_random=True)  # R independent states
@@ -269,6 +273,7 @@ def main():
     # is evicted by a 1 GiB device copy, and one replay is timed: every state
     # the timed steps touch is read from HBM.
     graph_ms = None
+    note("graph")
     if "graph" in rows:
         ms = cold_graph_ms(torch, lambda t: step(W + t, t % R), K, evict)
         graph_ms = ms
@@ -287,6 +292,7 @@ def main():
                                             "graph_steps": 2 * R}
 
     # ---------------------------------------------------------------- the state-step kernel alone
+    note("kernel")
     if "kernel" in rows:
         yk = torch.empty(R, 1, C, device=dev)
         for r in range(R):
@@ -299,6 +305,7 @@ def main():
         del yk
 
     # ---------------------------------------------------------------- hot: one state buffer
+    note("hot")
     if "hot" in rows:
         S1 = S_pool[0].clone()
         th = (tails[cnt[0] % 2][0].clone(), tails[cnt[0] % 2][0].clone())
@@ -314,6 +321,7 @@ def main():
     # The same cold graph as decode_b1_cold_graph_all_states (2R steps over the R
     # states, Infinity Cache evicted before the timed replay), through
     # gdn_kda_decode_token with one gate input per (value head, key channel).
+    note("kda")
     if "kda" in rows:
         ak = f32(gi.channel_gates(5, shape, 1, 2 * R)[:, 0])
         kb = kda_token_bytes(1, shape)
@@ -332,6 +340,7 @@ def main():
         del ak
 
     # ---------------------------------------------------------------- batch 64, ping-pong over two batches
+    note("b64")
     if "b64" in rows:
         B = 64
         steps64 = 256
@@ -390,6 +399,7 @@ def main():
         del S64, T64, tails64, x64, a64, b64, y64, o64
 
     # ---------------------------------------------------------------- tree verify + commit
+    note("tree")
     if "tree" in rows or "commit" in rows:
         tin = gi.tree_inputs(3, shape, n_nodes=32, max_depth=8)
         pool = gi.decode_inputs(103, shape, R, 1, state_sigma=0.1, tail_random=True)
@@ -438,6 +448,7 @@ def main():
     # ---------------------------------------------------------------- batched tree verify + commit
     # 64 sequences, one 32-node tree each, accepted paths of mixed lengths;
     # two batches of checkpoints (403 MB) alternate so states come from HBM.
+    note("tree64")
     if "tree64" in rows:
         B = 64
         tbi = gi.tree_batch_inputs(5, shape, B, n_nodes=32, max_depth=8)
@@ -483,6 +494,7 @@ def main():
 
     # ---------------------------------------------------------------- block verify + commit, 16 tokens
     # Batch 1 rotates over the R cold states; batch 64 alternates two batches.
+    note("block")
     if "block" in rows:
         kb = 16
         for B, nbuf in ((1, R), (64, 2)):
@@ -530,6 +542,7 @@ def main():
     # ---------------------------------------------------------------- snapshot / restore, 64 sequences
     # Save all 64 sequences of one batch into a blob and restore them into the
     # other batch; the two batches and the blob (1.2 GB) exceed the cache.
+    note("snapshot")
     if "snapshot" in rows:
         B = 64
         pool = gi.decode_inputs(106, shape, 2 * B, 1, state_sigma=0.1, tail_random=True)
@@ -554,6 +567,7 @@ def main():
         del S2, T2, blobs
 
     # ---------------------------------------------------------------- chunked prefill
+    note("prefill")
     if "prefill" in rows:
         try:
             T = 32768
@@ -595,6 +609,7 @@ def main():
     # may use, its heads split by q/k head group over threads (each head keeps
     # its own token order, so the results are the same numbers).
     cpu = None
+    note("cpu")
     if "cpu" in rows:
         import oracle
         oracle.build(force=False)
