@@ -1746,9 +1746,14 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
 
 // ------------------------------------------------------------ commit
 
+// PREPARED: the operands come from the verify's workspace, so no workgroup
+// reads the tail, and the kernel also rewrites it (tail_out, the same buffer):
+// each channel by one thread, after the path is validated.  Otherwise the
+// conv reads the tail here and commit_tail_kernel rewrites it afterwards.
 template <int D, typename Act, bool PREPARED>
 __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S, const Act* __restrict__ tail,
-                                                           const Act* __restrict__ w, int n,
+                                                           Act* __restrict__ tail_out, const Act* __restrict__ w,
+                                                           int n,
                                                            const int32_t* __restrict__ parent,
                                                            const Act* __restrict__ x, const float* __restrict__ a,
                                                            const float* __restrict__ b, int L,
@@ -1762,8 +1767,8 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
 
     // The index arithmetic is made to depend on every argument, so all the
     // argument loads issue together (one kernel-argument round trip).
-    asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(tail), "s"(w), "s"(n), "s"(parent), "s"(x), "s"(a), "s"(b),
-                 "s"(L), "s"(path), "s"(o), "s"(status), "s"(Hk), "s"(Hv), "s"(C));
+    asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(tail), "s"(tail_out), "s"(w), "s"(n), "s"(parent), "s"(x),
+                 "s"(a), "s"(b), "s"(L), "s"(path), "s"(o), "s"(status), "s"(Hk), "s"(Hv), "s"(C));
     // Workgroups of one (sequence, q/k head) share their token inputs; they
     // are kept on one XCD.
     const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
@@ -1783,6 +1788,7 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     a += static_cast<size_t>(bq) * n * Hv;
     b += static_cast<size_t>(bq) * n * Hv;
     tail += static_cast<size_t>(bq) * C * 4;
+    tail_out += PREPARED ? static_cast<size_t>(bq) * C * 4 : 0;
 
     float* Sh = S + (static_cast<size_t>(bq) * Hv + h) * D * D;
     float4 s[NV];
@@ -1833,6 +1839,18 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
         // k.q): every token's loads in flight at once, then into LDS.
         constexpr int U = D / 2 + ROWS / 4 + 1;              // 16-byte units per token
         constexpr int NL = (kMaxDepth * U + 255) / 256;      // units per thread
+        // This thread's tail channel (the sequence's workgroups share them out):
+        // its old entries and the path tokens' inputs, loaded with the operands.
+        const int per = (C + blocks_per_head * Hv - 1) / (blocks_per_head * Hv);
+        const int tc = (wid % (blocks_per_head * Hv)) * per + static_cast<int>(threadIdx.x);
+        const bool tail_writer = static_cast<int>(threadIdx.x) < per && tc < C;
+        const int tcc = tail_writer ? tc : 0;
+        using Q = Quad<Act>;
+        const typename Q::raw told = Q::load(tail_out + static_cast<size_t>(tcc) * 4);
+        Act xin[kMaxDepth];
+#pragma unroll
+        for (int j = 0; j < kMaxDepth; ++j)
+            xin[j] = x[static_cast<size_t>(sm.node[j]) * C + tcc];
         float4 un[NL];
 #pragma unroll
         for (int e = 0; e < NL; ++e) {
@@ -1861,6 +1879,14 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
             }
         }
         __syncthreads();
+        if (sm.ok && len > 0 && tail_writer) {
+            typename Q::raw t = told;
+#pragma unroll
+            for (int j = 0; j < kMaxDepth; ++j)
+                if (j < len)
+                    t = Q::push(t, xin[j]);
+            Q::store(tail_out + static_cast<size_t>(tc) * 4, t);
+        }
     }
     if (!sm.ok || len == 0)
         return;
@@ -1936,15 +1962,16 @@ hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int 
         const int bph = D / (4 * Row<D>::RPW);
         if (ws == nullptr)
             hipLaunchKernelGGL((commit_state_kernel<D, Act, false>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)),
-                               dim3(256), 0, s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                               static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph, TreeWs{});
+                               dim3(256), 0, s, S, static_cast<const Act*>(tail), nullptr, static_cast<const Act*>(w), n,
+                               parent, static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph,
+                               TreeWs{});
         else
             hipLaunchKernelGGL((commit_state_kernel<D, Act, true>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)),
-                               dim3(256), 0, s, S, static_cast<const Act*>(tail), nullptr, n, parent,
+                               dim3(256), 0, s, S, nullptr, static_cast<Act*>(tail), nullptr, n, parent,
                                static_cast<const Act*>(x), nullptr, nullptr, L, path, o, status, g.Hk, g.Hv, g.C, bph,
                                tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D));
     });
-    if (e != hipSuccess)
+    if (e != hipSuccess || ws != nullptr)   // the prepared form rewrote the tail itself
         return e;
     const dim3 grid(static_cast<unsigned>((g.C + 255) / 256), static_cast<unsigned>(g.B)), block(256);
     if (g.bf16)
