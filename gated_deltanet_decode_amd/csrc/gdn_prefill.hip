@@ -14,21 +14,21 @@
 // overflows however strong the decay.
 //
 // Work split for MI355X, per segment of at most 2,048 tokens, every chunk
-// product on 32x32x16 fp16 MFMAs (fp32 accumulation):
+// product on fp16 MFMAs (fp32 accumulation):
 //   conv  (parallel over 32-token blocks x q/k heads): conv + SiLU of the
 //         q/k head's channels and of its value heads' channels, q/k L2 norm;
 //         writes fp16 q^, k^, k^ transposed and v transposed, as fragments.
 //   tri   (parallel over value heads x chunks): gates and G, K K^T and K Q^T,
 //         A, the blocked inverse T in fp32 (16x16 diagonal blocks by
 //         substitution, off-diagonal blocks by fp32 MFMA block products), then
-//         U~ = T (beta V) and W~^T = (beta e^G K)^T T^T.  P, U~, W~ and the
-//         decay-scaled k^T of the scan are written straight from registers.
+//         U~ = T (beta V) and W~^T = (beta e^G K)^T T^T.  P, U~ and W~ are
+//         written straight from registers, with e^G and e^{G_n - G}.
 //   scan  (sequential over chunks; one workgroup per (sequence, value head,
 //         32-row slice of the state)): Z = W~ S0^T, U = U~ - Z,
-//         O = s (e^G (.) Q S0^T + P U), S <- e^{G_n} S + U^T (e^{G_n - G} K).
+//         O = s (e^G (.) Q S0^T + P U), S <- e^{G_n} S + (e^{G_n - G} (.) U)^T K.
 //         The state is held transposed in accumulator tiles, so the
 //         recurrence passes from one product to the next in registers.
-// The workspace holds one segment (about 139 MB at the 27B-class shape),
+// The workspace holds one segment (about 114 MB at the 27B-class shape),
 // whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
 #include <utility>
@@ -62,18 +62,18 @@ constexpr float kScale = Scale<D>::value;
 //   vt    fp16 [B][Hv][NC][fragments of 128 dims x 64 tokens]   v transposed
 //   ut    fp16 [B][Hv][NC][accumulators of 64 tokens x 128 dims] U~ = T (beta V)
 //   wt    fp16 [B][Hv][NC][fragments of 64 tokens x 128 keys]   W~ = T (beta e^G K)
-//   kd    fp16 [B][Hv][NC][fragments of 128 keys x 64 tokens]   (e^{G_last - G} k^)^T
 //   P     fp16 [B][Hv][NC][fragments of 64 x 64 tokens]
 //   eg    f32  [B][Hv][SP]                     e^{G_t}
+//   ed    f32  [B][Hv][SP]                     e^{G_last - G_t} of the token's chunk
 struct Ws {
-    _Float16 *q, *k, *kt, *vt, *ut, *wt, *kd, *P;
-    float* eg;
+    _Float16 *q, *k, *kt, *vt, *ut, *wt, *P;
+    float *eg, *ed;
 };
 
 inline size_t seg_pitch(int T) { return static_cast<size_t>(T >= SEG ? SEG : (T + CH - 1) / CH * CH); }
 
 inline size_t ws_bytes(int B, int Hk, int Hv, size_t SP) {
-    const size_t per_tok = 3ull * Hk * D * 2 + 4ull * Hv * D * 2 + Hv * CH * 2ull + Hv * 4ull;
+    const size_t per_tok = 3ull * Hk * D * 2 + 3ull * Hv * D * 2 + Hv * CH * 2ull + 2ull * Hv * 4;
     return static_cast<size_t>(B) * SP * per_tok + 256 * 10;
 }
 
@@ -91,9 +91,9 @@ inline Ws carve(void* base, int B, int Hk, int Hv, size_t SP) {
     w.vt = take16(nv);
     w.ut = take16(nv);
     w.wt = take16(nv);
-    w.kd = take16(nv);
     w.P = take16(nm);
     w.eg = take32(ng);
+    w.ed = take32(ng);
     return w;
 }
 
@@ -135,7 +135,7 @@ __device__ __forceinline__ h8 ldfrag(const _Float16* m, int tile, int lane) { re
 __device__ __forceinline__ h8 ldfrag_once(const _Float16* m, int tile, int lane) {
     return __builtin_nontemporal_load(reinterpret_cast<const h8*>(m + tile * 512 + lane * 8));
 }
-constexpr int kChunkQK = CH * D;   // fp16 elements of one chunk of q, k, k^T, v^T, U~, W~, kd
+constexpr int kChunkQK = CH * D;   // fp16 elements of one chunk of q, k, k^T, v^T, U~, W~
 constexpr int kChunkP = CH * CH;   // fp16 elements of one chunk of P
 
 // Prefill stores q^, k^ and v as fp16 (relative step 2^-11), so its conv and
@@ -317,7 +317,6 @@ struct alignas(16) TriSmem {
     float beta[CH];
     float bv[CH];    // beta_t            (scales V in U~)
     float bk[CH];    // beta_t e^{G_t}    (scales K in W~)
-    float ed[CH];    // e^{G_last - G_t}  (scales K in the scan's update operand)
 };
 
 __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, const float* __restrict__ bg, Ws ws,
@@ -383,12 +382,13 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
         }
         const float l2 = la * kLog2e;             // G in log2 units
         const float eg = __builtin_amdgcn_exp2f(l2);
-        sm.ed[lane] = __builtin_amdgcn_exp2f(__shfl(l2, kWave - 1, kWave) - l2);
+        const float ed = __builtin_amdgcn_exp2f(__shfl(l2, kWave - 1, kWave) - l2);
         sm.G[lane] = l2;
         sm.beta[lane] = be;
         sm.bv[lane] = be;
         sm.bk[lane] = be * eg;
         ws.eg[hs + lane] = eg;
+        ws.ed[hs + lane] = ed;
     }
     f16v kk = zero16(), kq = zero16();
 #pragma unroll
@@ -508,22 +508,16 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
                 tf[tt][s][4 + e] = static_cast<_Float16>(up[e]);
             }
         }
-    // beta V (column tile w) and beta e^G K (key tile w) with the token as k;
-    // e^{G_last - G} K (key tile w) is the scan's state-update operand
+    // beta V (column tile w) and beta e^G K (key tile w) with the token as k
     h8 vs[4], ks[4];
-    _Float16* kdo = ws.kd + hc;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        h8 kd;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int tp = 16 * s + kperm(hi, e);
-            const float kv = static_cast<float>(kf[s][e]);
             vs[s][e] = static_cast<_Float16>(static_cast<float>(vf[s][e]) * sm.bv[tp]);
-            ks[s][e] = static_cast<_Float16>(kv * sm.bk[tp]);
-            kd[e] = static_cast<_Float16>(kv * sm.ed[tp]);
+            ks[s][e] = static_cast<_Float16>(static_cast<float>(kf[s][e]) * sm.bk[tp]);
         }
-        *reinterpret_cast<h8*>(kdo + ((wave * 4 + s) * 64 + lane) * 8) = kd;
     }
     _Float16* uto = ws.ut + hc;
     _Float16* wto = ws.wt + hc;
@@ -559,33 +553,44 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 
 // ------------------------------------------------------------ scan
 
-// One workgroup per (sequence, value head, 32-row slice of the state), four
+// One workgroup per (sequence, value head, 32-row slice of the state), six
 // waves with one barrier per chunk:
-//   state  (wave 0) holds S^T of the slice (keys x rows) in four 32 x 32
-//          accumulator tiles across chunks.  Their fp16 copies are directly
-//          the B fragments of Z = W~ S0^T; Z's accumulators give U = U~ - Z,
-//          whose fp16 copies are directly the B fragments of the update
-//          S^T <- e^{G_n} S^T + (e^{G_n - G} K)^T U: no LDS round trip and no
-//          barrier inside the recurrence.  It hands S0^T and U, as B
-//          fragments, to the output waves through LDS (two buffers).
-//   output (waves 1, 2; token tile 32 (w - 1)) compute Y = Q S0^T and P U one
-//          chunk behind and store o = s (e^G Y + P U); Q and P stream through
-//          a register ring.
-//   loader (wave 3) copies W~, (e^{G_n - G} K)^T, this slice's U~ and e^G of
-//          chunk k + 2 into a three-stage LDS ring by direct global-to-LDS loads,
-//          and waits for chunk k + 1 before the barrier that ends step k.
+//   state  (waves 0, 1: rows 16 w .. 16 w + 15 of the slice) hold S^T of their
+//          rows (keys x rows) in eight 16 x 16 accumulator tiles across chunks
+//          and run the recurrence on 16x16x32 fp16 MFMAs:
+//            Z = W~ S0^T - U~        (the accumulators start at -U~: Z = -U)
+//            S^T <- e^{G_n} S^T + K^T (e^{G_n - G} (.) U)
+//          The fp16 copies of S^T's accumulators are directly the B fragments
+//          of Z, and Z's accumulators, negated and scaled per token, directly
+//          the B fragments of the update: no LDS round trip and no barrier
+//          inside the recurrence.  Each wave hands S0^T and U of its rows to
+//          the output waves through LDS (two buffers).
+//   output (waves 2, 3: token tile 32 (w - 2)) compute Y = Q S0^T and P U one
+//          chunk behind on 32x32x16 MFMAs and store o = s (e^G Y + P U); Q and
+//          P stream through a register ring.
+//   copies (waves 4, 5) copy W~, the q/k head's k^T, this slice's U~, e^G and
+//          e^{G_n - G} of chunk k + 2 into a three-stage LDS ring by direct
+//          global-to-LDS loads, and wait for chunk k + 1 before the barrier
+//          that ends step k.  Two waves share the copies so that two chunks'
+//          worth stays within each wave's outstanding vector loads.
+// Splitting the rows over two waves halves the matrix and vector work on the
+// recurrence's dependent chain; each state wave still reads the whole chunk's
+// W~ and k^T (32 KB) from LDS.
 // Workgroups of one (sequence, q/k head) share an XCD and its L2.
 constexpr int kStages = 3;
-constexpr int kOutRing = 3;
-constexpr int kDmaPerChunk = 16 + 16 + 4 + 1;   // W~, kd, U~ (two 2 KB tiles), e^G
+constexpr int kOutRing = 2;
+constexpr int kScanThreads = 6 * kWave;
+constexpr int kDmaW = 16 + 2;   // wave 4, per chunk: W~ (16 KB), e^G, e^{G_n - G}
+constexpr int kDmaK = 16 + 4;   // wave 5, per chunk: k^T (16 KB), U~ (two 2 KB tiles)
 
 struct alignas(16) ScanSmem {
     h8 wt[kStages][16][64];     // W~ fragments (token tile, key step)
-    h8 kd[kStages][16][64];     // (e^{G_n - G} K)^T fragments (key tile, token step)
+    h8 kt[kStages][16][64];     // k^T fragments of the q/k head (key tile, token step)
     h8 ut[kStages][2][64][2];   // U~ of the slice: token tile, lane, 32 bytes
     float eg[kStages][CH];
-    h8 xs[2][8][64];            // S0^T as B fragments (key step)
-    h8 xu[2][4][64];            // U as B fragments (token step)
+    float ed[kStages][CH];
+    h8 xs[2][8][64];            // S0^T as 32x32x16 B fragments (key step)
+    h8 xu[2][4][64];            // U as 32x32x16 B fragments (token step)
 };
 
 template <int N>
@@ -594,13 +599,48 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// 16x16x32 fp16 MFMA.  Lane (q, r) = (lane / 16, lane % 16).  A fragment: row r,
+// eight k values; B fragment: column r, the same eight k; accumulator i of lane
+// (q, c) is row 4 q + i, column c.
+__device__ __forceinline__ f4 mma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+// Row m of the recurrence's 16-row tile t (keys: t = 0..7; tokens: t = 0..3)
+// is index rho(t, m) of the chunk.  The eight indices that a lane of quarter q
+// contributes to k-step s (rows 4 q .. 4 q + 3 of tiles 2 s and 2 s + 1) are
+// then 16 (2 s + q / 2) + kperm(q % 2, e), e = 0..7: exactly the 16-byte unit
+// (k-step 2 s + q / 2, lane half q % 2) of the 32x32x16 fragment storage.  So
+// every operand of the recurrence is one 16-byte LDS read per lane from the
+// storage the other kernels write, accumulators pass from one product to the
+// next in registers, and S0^T and U reach the output waves unit for unit in
+// their 32x32x16 B layout.
+__host__ __device__ constexpr int rho(int t, int m) {
+    return 32 * (t >> 1) + 16 * (m >> 3) + 8 * (t & 1) + 4 * ((m >> 2) & 1) + (m & 3);
+}
+constexpr bool rho_is_a_permutation() {
+    bool seen[D] = {};
+    for (int t = 0; t < D / 16; ++t)
+        for (int m = 0; m < 16; ++m) {
+            const int r = rho(t, m);
+            if (r < 0 || r >= D || seen[r])
+                return false;
+            seen[r] = true;
+        }
+    for (int s = 0; s < D / 32; ++s)
+        for (int q = 0; q < 4; ++q)
+            for (int e = 0; e < 8; ++e)
+                if (rho(2 * s + (e >> 2), 4 * q + (e & 3)) != 16 * (2 * s + (q >> 1)) + kperm(q & 1, e))
+                    return false;
+    return true;
+}
+static_assert(rho_is_a_permutation(), "the recurrence's row order must tile the chunk's 32x32x16 fragment units");
+
 struct OutOps {
     h8 qf[8], pf[4];
     f4 eg[4];
 };
 
-__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws, int T,
-                                                   int seg0, int SP, int nch, int B, int Hk, int Hv) {
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ S, float* __restrict__ o, Ws ws,
+                                                            int T, int seg0, int SP, int nch, int B, int Hk, int Hv) {
     __shared__ ScanSmem sm;
     const int G = Hv / Hk;
     // workgroups of one (sequence, q/k head) share an XCD: blockIdx % 8 picks the XCD
@@ -619,130 +659,145 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
     const size_t kbase = (static_cast<size_t>(bq) * Hk + g) * NC;   // chunks of q/k head g
     const int len = min(SEG, T - seg0);
 
-    if (wave == 3) {
-        // ---- loader
+    if (wave >= 4) {
+        // ---- copies: wave 4 W~, e^G and e^{G_n - G}; wave 5 k^T and U~ (each
+        // wave's copies of two chunks fit its 63 outstanding vector loads)
         auto issue = [&](int cl) {
             const int st = cl % kStages;
-            const char* wsrc = reinterpret_cast<const char*>(ws.wt + (vbase + cl) * kChunkQK) + lane * 16;
-            const char* ksrc = reinterpret_cast<const char*>(ws.kd + (vbase + cl) * kChunkQK) + lane * 16;
-            const char* usrc = reinterpret_cast<const char*>(ws.ut + (vbase + cl) * kChunkQK) + lane * 16;
+            if (wave == 4) {
+                const char* wsrc = reinterpret_cast<const char*>(ws.wt + (vbase + cl) * kChunkQK) + lane * 16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                __builtin_amdgcn_global_load_lds(wsrc + i * 1024, &sm.wt[st][i][0], 16, 0, 0);
+                for (int i = 0; i < 16; ++i)
+                    __builtin_amdgcn_global_load_lds(wsrc + i * 1024, &sm.wt[st][i][0], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(ws.eg + hbase + cl * CH + lane, &sm.eg[st][0], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(ws.ed + hbase + cl * CH + lane, &sm.ed[st][0], 4, 0, 0);
+            } else {
+                const char* ksrc = reinterpret_cast<const char*>(ws.kt + (kbase + cl) * kChunkQK) + lane * 16;
+                const char* usrc = reinterpret_cast<const char*>(ws.ut + (vbase + cl) * kChunkQK) + lane * 16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                __builtin_amdgcn_global_load_lds(ksrc + i * 1024, &sm.kd[st][i][0], 16, 0, 0);
+                for (int i = 0; i < 16; ++i)
+                    __builtin_amdgcn_global_load_lds(ksrc + i * 1024, &sm.kt[st][i][0], 16, 0, 0);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)   // accumulator tile (tt, slc) of U~: 2 KB
-                    __builtin_amdgcn_global_load_lds(usrc + (tt * (D / 32) + slc) * 2048 + q * 1024,
-                                                     &sm.ut[st][tt][0][0] + q * 64, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(ws.eg + hbase + cl * CH + lane, &sm.eg[st][0], 4, 0, 0);
+                    for (int h2 = 0; h2 < 2; ++h2)   // accumulator tile (tt, slc) of U~: 2 KB
+                        __builtin_amdgcn_global_load_lds(usrc + (tt * (D / 32) + slc) * 2048 + h2 * 1024,
+                                                         &sm.ut[st][tt][0][0] + h2 * 64, 16, 0, 0);
+            }
+        };
+        // wait until only the copies of the chunk just issued may be in flight
+        auto wait_one_behind = [&](bool issued) {
+            if (!issued)
+                wait_vmem<0>();
+            else if (wave == 4)
+                wait_vmem<kDmaW>();
+            else
+                wait_vmem<kDmaK>();
         };
         issue(0);
-        if (nch > 1) {
+        if (nch > 1)
             issue(1);
-            wait_vmem<kDmaPerChunk>();
-        } else {
-            wait_vmem<0>();
-        }
+        wait_one_behind(nch > 1);
         __builtin_amdgcn_s_barrier();
         for (int k = 0; k < nch; ++k) {
-            if (k + 2 < nch) {
+            if (k + 2 < nch)
                 issue(k + 2);
-                wait_vmem<kDmaPerChunk>();
-            } else {
-                wait_vmem<0>();
-            }
+            wait_one_behind(k + 2 < nch);
             __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_s_barrier();
-    } else if (wave == 0) {
-        // ---- state
-        float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0 + c32) * D;   // row row0 + c32
-        f16v st[4];   // st[kt][v]: key 32 kt + 8 (v / 4) + 4 hi + v % 4, row row0 + c32
+    } else if (wave < 2) {
+        // ---- state: rows row0 + 16 wave + c
+        const int q = lane >> 4, c = lane & 15, qs = q >> 1;
+        float* Sh = S + ((static_cast<size_t>(bq) * Hv + h) * D + row0 + 16 * wave + c) * D;
+        f4 st[8];   // st[t][i]: key rho(t, 4 q + i)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f4 v = *reinterpret_cast<const f4*>(Sh + 32 * kt + 8 * j + 4 * hi);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    st[kt][4 * j + r] = v[r];
-            }
+        for (int t = 0; t < 8; ++t)
+            st[t] = *reinterpret_cast<const f4*>(Sh + rho(t, 4 * q));
+        // LDS lane positions: an A fragment row rho(t, c) sits at lane (q % 2) * 32
+        // + rho(t, c) % 32 of its 1 KB run (which depends on t only through t % 2);
+        // this wave's B units for the output waves at (q % 2) * 32 + 16 wave + c.
+        const int la0 = (q & 1) * 32 + (rho(0, c) & 31), la1 = (q & 1) * 32 + (rho(1, c) & 31);
+        const int xl = (q & 1) * 32 + 16 * wave + c;
         __syncthreads();
         for (int k = 0; k < nch; ++k) {
             const int stg = k % kStages, par = k & 1;
-            // the chunk's operands, all requested before the first product
-            h8 wf[16], kf[16];
+            h8 wf[4][4];   // W~: token tile T, key step s
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                wf[i] = sm.wt[stg][i][lane];
-            const h8 ua[2][2] = {{sm.ut[stg][0][lane][0], sm.ut[stg][0][lane][1]},
-                                 {sm.ut[stg][1][lane][0], sm.ut[stg][1][lane][1]}};
+            for (int T4 = 0; T4 < 4; ++T4)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    wf[T4][s] = sm.wt[stg][(T4 >> 1) * 8 + 2 * s + qs][(T4 & 1) ? la1 : la0];
+            // token rho(T, 4 q + i) of U~'s accumulator tile T / 2 is value 8 (q / 2) + 4 (T % 2) + i of lane xl
+            const h8 u0 = sm.ut[stg][0][xl][qs], u1 = sm.ut[stg][1][xl][qs];
             const float eglast = sm.eg[stg][CH - 1];
-            __builtin_amdgcn_sched_barrier(0);
-            h8 bs[8];
+            f4 edv[2][2];  // e^{G_n - G} of the tokens of update step s2, slots 4 j .. 4 j + 3
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    edv[s2][j] = *reinterpret_cast<const f4*>(&sm.ed[stg][16 * (2 * s2 + qs) + 8 * j + 4 * (q & 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+            h8 bs[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    bs[s][e] = static_cast<_Float16>(st[s >> 1][8 * (s & 1) + e]);
-            f16v z0 = zero16(), z1 = zero16();
+                    bs[s][e] = static_cast<_Float16>(st[2 * s + (e >> 2)][e & 3]);
+            f4 z[4];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                z0 = mma32(wf[s], bs[s], z0);
-                z1 = mma32(wf[8 + s], bs[s], z1);
-            }
-            // (e^{G_n - G} K)^T is read while Z is in the matrix pipe
+            for (int T4 = 0; T4 < 4; ++T4)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                kf[i] = sm.kd[stg][i][lane];
+                for (int i = 0; i < 4; ++i)
+                    z[T4][i] = -static_cast<float>((T4 >> 1 ? u1 : u0)[4 * (T4 & 1) + i]);
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-                st[kt] *= eglast;
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int T4 = 0; T4 < 4; ++T4)
+                    z[T4] = mma16(wf[T4][s], bs[s], z[T4]);
+            // k^T is read while Z is in the matrix pipe
+            h8 kf[8][2];   // key tile t, token step s2
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    kf[t][s2] = sm.kt[stg][(t >> 1) * 4 + 2 * s2 + qs][(t & 1) ? la1 : la0];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                st[t] *= eglast;
             // S0^T for the output waves, off the recurrence's path
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
-                sm.xs[par][s][lane] = bs[s];
-            // U = U~ - Z (accumulator order: token 32 tt + 8 (v / 4) + 4 hi + v % 4, row c32);
-            // token step s of U is accumulator values 8 (s & 1) .. + 7 of tile s / 2
-            h8 bu[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int tt = s >> 1, j = s & 1;
-                const f16v& z = tt ? z1 : z0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bu[s][e] = static_cast<_Float16>(static_cast<float>(ua[tt][j][e]) - z[8 * j + e]);
-            }
-#pragma unroll
             for (int s = 0; s < 4; ++s)
+                sm.xs[par][2 * s + qs][xl] = bs[s];
+            // U = -Z; token step s2 of U is tiles 2 s2 and 2 s2 + 1
+            h8 bu[2], bd[2];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-                    st[kt] = mma32(kf[kt * 4 + s], bu[s], st[kt]);
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sm.xu[par][s][lane] = bu[s];
+                for (int e = 0; e < 8; ++e) {
+                    const float u = -z[2 * s2 + (e >> 2)][e & 3];
+                    bu[s2][e] = static_cast<_Float16>(u);
+                    bd[s2][e] = static_cast<_Float16>(u * edv[s2][e >> 2][e & 3]);
+                }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    st[t] = mma16(kf[t][s2], bd[s2], st[t]);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                sm.xu[par][2 * s2 + qs][xl] = bu[s2];
             __syncthreads();
         }
         __syncthreads();
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f4 v;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[r] = st[kt][4 * j + r];
-                *reinterpret_cast<f4*>(Sh + 32 * kt + 8 * j + 4 * hi) = v;
-            }
+        for (int t = 0; t < 8; ++t)
+            *reinterpret_cast<f4*>(Sh + rho(t, 4 * q)) = st[t];
     } else {
         // ---- output, token tile tt
-        const int tt = wave - 1;
-        const size_t ostride = static_cast<size_t>(Hv) * D;
-        float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0 + c32;
+        const int tt = wave - 2;
+        const uint32_t ostride = static_cast<uint32_t>(Hv) * D;   // a segment's o (2,048 rows) spans < 4 G floats
+        float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
         auto load = [&](OutOps& op, int cl) {
             const _Float16* qc = ws.q + (kbase + cl) * kChunkQK;
             const _Float16* pc = ws.P + (vbase + cl) * kChunkP;
@@ -773,7 +828,6 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 xu[s] = sm.xu[par][s][lane];
-            __builtin_amdgcn_sched_barrier(0);
             f16v y = zero16(), pu = zero16();
 #pragma unroll
             for (int s = 0; s < 8; ++s)
@@ -782,14 +836,16 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
             for (int s = 0; s < 4; ++s)
                 pu = mma32(op.pf[s], xu[s], pu);
             const int n = min(CH, len - cl * CH);
+            // the chunk's first row (uniform) and a 32-bit offset per lane and value
             float* orow = obase + static_cast<size_t>(cl) * CH * ostride;
+            const uint32_t lrow = static_cast<uint32_t>(32 * tt + 4 * hi) * ostride + c32;
             if (n == CH) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         __builtin_nontemporal_store(kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]),
-                                                    orow + static_cast<size_t>(32 * tt + 8 * j + 4 * hi + r) * ostride);
+                                                    orow + (lrow + static_cast<uint32_t>(8 * j + r) * ostride));
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -798,24 +854,23 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ S, float*
                         const int t = 32 * tt + 8 * j + 4 * hi + r;
                         if (t < n)
                             __builtin_nontemporal_store(kScale * __builtin_fmaf(op.eg[j][r], y[4 * j + r], pu[4 * j + r]),
-                                                        orow + static_cast<size_t>(t) * ostride);
+                                                        orow + (lrow + static_cast<uint32_t>(8 * j + r) * ostride));
                     }
             }
             load(ring[P], min(cl + kOutRing, nch - 1));
             __syncthreads();
         };
+        static_assert(kOutRing == 2, "the ring is walked in pairs");
         int cl0 = 0;
         for (; cl0 + kOutRing <= nch; cl0 += kOutRing) {
             step(std::integral_constant<int, 0>{}, cl0);
             step(std::integral_constant<int, 1>{}, cl0 + 1);
-            step(std::integral_constant<int, 2>{}, cl0 + 2);
         }
         if (cl0 < nch)
             step(std::integral_constant<int, 0>{}, cl0);
-        if (cl0 + 1 < nch)
-            step(std::integral_constant<int, 1>{}, cl0 + 1);
     }
 }
+
 
 // New tail = the last four raw inputs of (old tail ++ the prompt).
 template <typename Act>
@@ -873,8 +928,8 @@ hipError_t launch_prefill(const Geo& g, float* S, void* tail, const void* w, int
                            seg0, SP, nch, g.Hk, g.Hv);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), dim3(256), 0, s, S, o, W, T,
-                           seg0, SP, nch, g.B, g.Hk, g.Hv);
+        hipLaunchKernelGGL(pf::scan_kernel, dim3(static_cast<unsigned>(scan_grid)), dim3(pf::kScanThreads), 0, s, S,
+                           o, W, T, seg0, SP, nch, g.B, g.Hk, g.Hv);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
