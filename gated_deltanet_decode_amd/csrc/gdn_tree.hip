@@ -20,16 +20,16 @@
 //                       through a register ring several nodes ahead.
 // A block (the "Architecture" page's parts list: delta-rule kernels for one
 // token, a block and a tree) is the chain 0 -> 1 -> ... -> k-1: the same two
-// launches with no parent array, no tables to check and no saved levels;
-// committing a block prefix is the same walk writing the rows back, plus a
-// launch that appends the committed inputs to the conv tail.
+// launches with no parent array, no tables to check and no saved levels.
+// Committing a block prefix streams each state once, replaying the prefix's
+// prepared operands from LDS, and rewrites the conv tail in the same launch.
 //
 // Commit of a tree path replays the accepted path from the checkpoint with
 // the same per-token arithmetic as decode (gdn_core.hpp), so the committed
-// state is bit-identical to token-by-token decode of the path; the tail is
-// rewritten by a second, stream-ordered launch after every workgroup of the
-// first has read it.  Its per-token operands are computed per workgroup into
-// LDS.
+// state is bit-identical to token-by-token decode of the path.  Its per-token
+// operands are computed per workgroup into LDS, or read from the verify's
+// workspace; in the first form the tail is rewritten by a second,
+// stream-ordered launch after every workgroup of the first has read it.
 #include "gdn_core.hpp"
 #include "gdn_launch.hpp"
 #include "gdn_tree.hpp"
@@ -455,7 +455,6 @@ struct VerifyCtx {
     using R = Row<D>;
     static constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW, ROWS = 4 * RPW;
     int h, grp, bq, lane, r, row, m0, n, Hk, Hv, ord_l, dep_l, ok;
-    bool first;   // the workgroup of head 0, rows 0.. of its sequence
     const float* Sh;
     float* oh;   // o of this lane's row at node 0 of the sequence
     TreeWs ws;
@@ -468,7 +467,6 @@ struct VerifyCtx {
         const int blk = wid % blocks_per_head;
         h = (wid / blocks_per_head) % Hv;
         bq = wid / (blocks_per_head * Hv);
-        first = wid % (blocks_per_head * Hv) == 0;
         grp = h / (Hv / Hk);
         lane = threadIdx.x & (kWave - 1);
         r = lane % LPR;
@@ -534,25 +532,23 @@ struct WalkWide {
 
 // What a walk does.  Tree: verify a draft tree (saved levels, reloads).
 // Chain: verify a block, the chain 0 -> 1 -> ... -> n-1 (every node continues
-// from the previous one: no saved levels, no LDS).  ChainCommit: advance each
-// sequence's state in place by the first accepted[seq] nodes of its block.
-enum class WalkKind { Tree, Chain, ChainCommit };
+// from the previous one: no saved levels, no LDS).
+enum class WalkKind { Tree, Chain };
 
 struct NoSmem {};
 
 template <int D, typename Walk, WalkKind KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves))) void tree_verify_kernel(
-    const float* __restrict__ Sc, int n, TreeWs ws, float* __restrict__ o, int Hk, int Hv, int blocks_per_head,
-    const int32_t* __restrict__ accepted, int32_t* __restrict__ status) {
+    const float* __restrict__ Sc, int n, TreeWs ws, float* __restrict__ o, int Hk, int Hv, int blocks_per_head) {
     using R = Row<D>;
     constexpr int NV = R::NV, RING = Walk::ring, LEVELS = Walk::levels;
-    constexpr bool TREE = KIND == WalkKind::Tree, COMMIT = KIND == WalkKind::ChainCommit;
+    constexpr bool TREE = KIND == WalkKind::Tree;
     using Smem = std::conditional_t<TREE, VerifySmem<D, LEVELS>, NoSmem>;
     __shared__ Smem sm;
     // The index arithmetic is made to depend on every argument, so all the
     // argument loads issue together (one kernel-argument round trip).
     asm volatile("" : "+s"(blocks_per_head) : "s"(Sc), "s"(n), "s"(ws.qk), "s"(ws.v), "s"(ws.abk), "s"(ws.tab), "s"(o),
-                 "s"(Hk), "s"(Hv), "s"(accepted), "s"(status));
+                 "s"(Hk), "s"(Hv));
     const VerifyCtx<D> c(Sc, n, ws, o, Hk, Hv, blocks_per_head);
     const int tid = threadIdx.x;
     float4 base[NV];
@@ -561,15 +557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         base[j] = load_stream(c.Sh + c.row * D + R::key(j, c.r));
     if (!c.ok)   // nothing is written for a malformed tree
         return;
-    int len = n;   // walk steps
-    if constexpr (COMMIT) {
-        len = accepted[c.bq];
-        const bool valid = len >= 0 && len <= n;
-        if (status && c.first && c.lane == 0 && threadIdx.x == 0)
-            status[c.bq] = valid ? 0 : 10;   // GDN_ERR_INDEX
-        if (!valid || len == 0)
-            return;
-    }
+    const int len = n;   // walk steps
 
     // Node operands stream through a ring of RING register slots, unrolled so
     // that each slot keeps its registers: a slot is refilled with the node
@@ -592,7 +580,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         save_base = base - kLevelBytes;
         parent_base = base - 2 * kLevelBytes;
     }
-    const bool want_o = !COMMIT || o != nullptr;
     int dprev = 0;
     // One walk step per node, expanded at compile time (at most kMaxNodes),
     // so that ring slots are static registers and every wait on a slot counts
@@ -631,8 +618,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
             }
         }
         const float out = node_update<D>(s, ring[p]);
-        if (want_o)
-            c.store_o(it, out);
+        c.store_o(it, out);
         if constexpr (TREE) {
             if (d <= LEVELS) {
 #pragma unroll
@@ -650,12 +636,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Walk::waves
         return true;
     };
     walk_all(step, std::make_integer_sequence<int, kMaxNodes>{});
-    if constexpr (COMMIT) {
-        float* Sw = const_cast<float*>(c.Sh);
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            store_stream(Sw + c.row * D + R::key(j, c.r), s[j]);
-    }
 }
 
 // Runs f(D, Act) for the geometry's head width and activation type.
@@ -710,10 +690,10 @@ hipError_t launch_tree_verify(const Geo& g, const float* S, const void* tail, co
         // More workgroups than two per CU: the form for several trees per CU.
         if (grid > 2u * 256u)
             hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::Tree>), dim3(grid), dim3(256), 0, s, S, n,
-                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
+                               W, o, g.Hk, g.Hv, bph);
         else
             hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep, WalkKind::Tree>), dim3(grid), dim3(256), 0, s, S, n,
-                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
+                               W, o, g.Hk, g.Hv, bph);
     });
 }
 
@@ -1681,24 +1661,140 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
 
 // ------------------------------------------------------------ blocks
 
-// The tail after a block commit holds the last four raw inputs of (old tail ++
-// the block's first len tokens); a sequence with an invalid or zero len keeps
-// its tail.  Runs after the prep launch, the only reader of the old tail.
-template <typename Act>
-__global__ __launch_bounds__(256) void block_tail_kernel(Act* __restrict__ tail, const Act* __restrict__ x, int k,
-                                                         const int32_t* __restrict__ accepted, int C) {
-    const int bq = blockIdx.y;
+// Block commit from the prepared operands of the block's positions (the prep
+// launch's workspace): each sequence's state advances by its first len =
+// accepted[seq] positions with decode's per-token arithmetic, so the result is
+// the bits of one decode step per position.  The work split is the path
+// commit's: one workgroup per (sequence, value head, ROWS rows), the state
+// rows streamed once; the positions' q|k, v and gates are staged in LDS with
+// one 16-byte load per unit, all in flight together.  The kernel also
+// rewrites the conv tail (the last four raw inputs of old tail ++ the first
+// len positions): nothing in it reads the old tail, so the sequence's
+// workgroups share its C channels out, one thread per channel.  A sequence
+// whose len is out of range keeps its state and tail and gets status
+// GDN_ERR_INDEX.
+template <int D, int ROWS>
+struct alignas(16) BlockSmem {
+    float qk[kMaxNodes][2 * D];   // q^|k^ of each position
+    float v[kMaxNodes][ROWS];     // v of the workgroup's rows
+    float kq[kMaxNodes], alpha[kMaxNodes], beta[kMaxNodes];
+};
+
+template <int D, typename Act>
+__global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S, Act* __restrict__ tail, int k,
+                                                           const Act* __restrict__ x,
+                                                           const int32_t* __restrict__ accepted,
+                                                           float* __restrict__ o, int32_t* __restrict__ status,
+                                                           int Hk, int Hv, int C, int blocks_per_head, TreeWs ws) {
+    using R = Row<D>;
+    constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
+    constexpr int ROWS = 4 * RPW;
+    __shared__ BlockSmem<D, ROWS> sm;
+    asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(tail), "s"(k), "s"(x), "s"(accepted), "s"(o), "s"(status),
+                 "s"(Hk), "s"(Hv), "s"(C));
+    const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
+    const int blk = wid % blocks_per_head;
+    const int h = (wid / blocks_per_head) % Hv;
+    const int bq = wid / (blocks_per_head * Hv);
+    const int grp = h / (Hv / Hk);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r = lane % LPR;
+    const int row0 = blk * ROWS;
+    const int lrow = wave * RPW + lane / LPR;
+    const int row = row0 + lrow;
+    float* Sh = S + (static_cast<size_t>(bq) * Hv + h) * D * D;
+    float4 s[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        s[j] = load_stream(Sh + row * D + R::key(j, r));
     const int len = accepted[bq];
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (len <= 0 || len > k || c >= C)
+    const bool valid = len >= 0 && len <= k;
+    if (status && wid % (blocks_per_head * Hv) == 0 && threadIdx.x == 0)
+        status[bq] = valid ? 0 : 10;   // GDN_ERR_INDEX
+    if (!valid || len == 0)
         return;
+
+    // This thread's tail channel (the sequence's workgroups share the C
+    // channels out: at most 96 per workgroup for the supported head widths)
+    // and its last four inputs, loaded with the operands.
+    const int per = (C + blocks_per_head * Hv - 1) / (blocks_per_head * Hv);
+    const int tc = (wid % (blocks_per_head * Hv)) * per + static_cast<int>(threadIdx.x);
+    const bool tail_writer = static_cast<int>(threadIdx.x) < per && tc < C;
+    const int tcc = tail_writer ? tc : 0;
     using Q = Quad<Act>;
-    Act* tc = tail + (static_cast<size_t>(bq) * C + c) * 4;
-    typename Q::raw t = Q::load(tc);
-    const Act* xb = x + static_cast<size_t>(bq) * k * C + c;
-    for (int j = len > 4 ? len - 4 : 0; j < len; ++j)
-        t = Q::push(t, xb[static_cast<size_t>(j) * C]);
-    Q::store(tc, t);
+    Act* tp = tail + (static_cast<size_t>(bq) * C + tcc) * 4;
+    const typename Q::raw told = Q::load(tp);
+    Act xin[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int j = len - 4 + e;
+        xin[e] = x[(static_cast<size_t>(bq) * k + (j < 0 ? 0 : j)) * C + tcc];
+    }
+
+    // The positions' operands: q|k of the q/k head, v of this workgroup's
+    // rows, (alpha, beta, k.q) of the value head; one 16-byte unit per load.
+    constexpr int U = D / 2 + ROWS / 4 + 1;             // units per position
+    constexpr int NL = (kMaxNodes * U + 255) / 256;     // units per thread
+    float4 un[NL];
+#pragma unroll
+    for (int e = 0; e < NL; ++e) {
+        const int idx = min(static_cast<int>(threadIdx.x) + 256 * e, len * U - 1), i = idx / U, f = idx % U;
+        const size_t m = static_cast<size_t>(bq) * k + i;
+        const float* src = f < D / 2 ? ws.qk + (m * Hk + grp) * 2 * D + 4 * f
+                           : f < D / 2 + ROWS / 4 ? ws.v + (m * Hv + h) * D + row0 + 4 * (f - D / 2)
+                                                  : ws.abk + (m * Hv + h) * 4;
+        un[e] = *reinterpret_cast<const float4*>(src);
+    }
+#pragma unroll
+    for (int e = 0; e < NL; ++e) {
+        const int idx = threadIdx.x + 256 * e, i = idx / U, f = idx % U;
+        if (idx < len * U) {
+            if (f < D / 2) {
+                *reinterpret_cast<float4*>(&sm.qk[i][4 * f]) = un[e];
+            } else if (f < D / 2 + ROWS / 4) {
+                *reinterpret_cast<float4*>(&sm.v[i][4 * (f - D / 2)]) = un[e];
+            } else {
+                sm.alpha[i] = un[e].x;
+                sm.beta[i] = un[e].y;
+                sm.kq[i] = un[e].z;
+            }
+        }
+    }
+    __syncthreads();
+    if (tail_writer) {
+        typename Q::raw t = told;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (len - 4 + e >= 0)
+                t = Q::push(t, xin[e]);
+        Q::store(tp, t);
+    }
+
+    float* ob = o ? o + static_cast<size_t>(bq) * k * Hv * D : nullptr;
+    TokOps<D> cur, nxt;
+    auto load_tok = [&](TokOps<D>& t, int i) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            t.k[j] = *reinterpret_cast<const float4*>(&sm.qk[i][D + R::key(j, r)]);
+            t.q[j] = *reinterpret_cast<const float4*>(&sm.qk[i][R::key(j, r)]);
+        }
+        t.v = sm.v[i][lrow];
+        t.alpha = sm.alpha[i];
+        t.beta = sm.beta[i];
+        t.kq = sm.kq[i];
+    };
+    load_tok(cur, 0);
+    for (int i = 0; i < len; ++i) {
+        load_tok(nxt, i + 1 < len ? i + 1 : i);
+        const float out = row_update<D>(s, cur.k, cur.q, cur.alpha, cur.beta, cur.v, cur.kq);
+        if (ob && r == 0)
+            ob[(static_cast<size_t>(i) * Hv + h) * D + row] = out;
+        cur = nxt;
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        store_stream(Sh + row * D + R::key(j, r), s[j]);
 }
 
 // prepared: the workspace already holds the block's operands (from the
@@ -1714,34 +1810,21 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
     });
     if (e != hipSuccess)
         return e;
-    e = dispatch(g, [&](auto dtag, auto) {
+    return dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
+        using Act = decltype(atag);
         const int bph = D / (4 * Row<D>::RPW);
         const unsigned grid = static_cast<unsigned>(g.B * g.Hv * bph);
-        const bool wide = grid > 2u * 256u;
-        if (commit && wide)
-            hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::ChainCommit>), dim3(grid), dim3(256), 0, s,
-                               S, k, W, o, g.Hk, g.Hv, bph, accepted, status);
-        else if (commit)
-            hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep, WalkKind::ChainCommit>), dim3(grid), dim3(256), 0, s,
-                               S, k, W, o, g.Hk, g.Hv, bph, accepted, status);
-        else if (wide)
+        if (commit)
+            hipLaunchKernelGGL((block_commit_kernel<D, Act>), dim3(grid), dim3(256), 0, s, S, static_cast<Act*>(tail), k,
+                               static_cast<const Act*>(x), accepted, o, status, g.Hk, g.Hv, g.C, bph, W);
+        else if (grid > 2u * 256u)
             hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::Chain>), dim3(grid), dim3(256), 0, s, S, k,
-                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
+                               W, o, g.Hk, g.Hv, bph);
         else
             hipLaunchKernelGGL((tree_verify_kernel<D, WalkDeep, WalkKind::Chain>), dim3(grid), dim3(256), 0, s, S, k,
-                               W, o, g.Hk, g.Hv, bph, nullptr, nullptr);
+                               W, o, g.Hk, g.Hv, bph);
     });
-    if (e != hipSuccess || !commit)
-        return e;
-    const dim3 grid(static_cast<unsigned>((g.C + 255) / 256), static_cast<unsigned>(g.B)), block(256);
-    if (g.bf16)
-        hipLaunchKernelGGL(block_tail_kernel<uint16_t>, grid, block, 0, s, static_cast<uint16_t*>(tail),
-                           static_cast<const uint16_t*>(x), k, accepted, g.C);
-    else
-        hipLaunchKernelGGL(block_tail_kernel<float>, grid, block, 0, s, static_cast<float*>(tail),
-                           static_cast<const float*>(x), k, accepted, g.C);
-    return hipGetLastError();
 }
 
 // ------------------------------------------------------------ commit
