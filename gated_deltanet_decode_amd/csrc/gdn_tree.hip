@@ -1661,6 +1661,15 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
 
 // ------------------------------------------------------------ blocks
 
+// Kernels that rewrite the conv tail themselves give each of a sequence's
+// B*Hv*bph workgroups ceil(C / (Hv*bph)) channels, one per thread.  With
+// C = 2*Hk*D + Hv*D <= 3*Hv*D that is at most 3*D/bph (96 for both supported
+// head widths); the launchers refuse a geometry where it would exceed 256.
+static bool tail_share_fits(const Geo& g) {
+    const int bph = g.D == 128 ? 128 / (4 * Row<128>::RPW) : 32 / (4 * Row<32>::RPW);   // row blocks per head
+    return (g.C + g.Hv * bph - 1) / (g.Hv * bph) <= 256;
+}
+
 // Block commit from the prepared operands of the block's positions (the prep
 // launch's workspace): each sequence's state advances by its first len =
 // accepted[seq] positions with decode's per-token arithmetic, so the result is
@@ -1802,6 +1811,8 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
 hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const void* w, int k, const void* x,
                         const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
                         bool prepared, hipStream_t s) {
+    if (commit && !tail_share_fits(g))
+        return hipErrorInvalidValue;
     const TreeWs W = tree_ws_carve(ws, g.B, k, g.Hk, g.Hv, g.D);
     hipError_t e = prepared ? hipSuccess : dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
@@ -2039,6 +2050,8 @@ __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
                          int32_t* status, void* ws, hipStream_t s) {
+    if (ws != nullptr && !tail_share_fits(g))
+        return hipErrorInvalidValue;
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
