@@ -271,11 +271,11 @@ static TreeWs tree_ws_carve(void* base, int B, int n, int Hk, int Hv, int D) {
 // checked, so a malformed parent array stays in bounds (the verify kernel
 // reports it and writes nothing).
 template <int D, typename Act, int NPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
-                                                        int n, const int32_t* __restrict__ parent,
-                                                        const Act* __restrict__ x, const float* __restrict__ a,
-                                                        const float* __restrict__ b, TreeWs ws,
-                                                        int32_t* __restrict__ status, int B, int Hk, int Hv, int C) {
+__device__ __forceinline__ void tree_prep_body(int bid, const Act* __restrict__ tail, const Act* __restrict__ w,
+                                               int n, const int32_t* __restrict__ parent,
+                                               const Act* __restrict__ x, const float* __restrict__ a,
+                                               const float* __restrict__ b, TreeWs ws,
+                                               int32_t* __restrict__ status, int B, int Hk, int Hv, int C) {
     static_assert(NPW >= 1 && NPW <= 4, "one wave normalises each node of the workgroup");
     // The index arithmetic is made to depend on every argument, so all the
     // argument loads issue together (one kernel-argument round trip).
@@ -284,8 +284,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
     __shared__ float yqk[NPW][2 * D];
     __shared__ int32_t anc_s[NPW][4];
     __shared__ int32_t depth_s[kMaxNodes], order_s[kMaxNodes];
-    if (static_cast<int>(blockIdx.x) < B) {
-        const int bq = blockIdx.x;
+    if (bid < B) {
+        const int bq = bid;
         if (parent == nullptr) {
             int32_t* tab = ws.tab + static_cast<size_t>(bq) * (2 * n + 1);
             const int t = threadIdx.x;
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
         }
         return;
     }
-    const int wg = blockIdx.x - B;
+    const int wg = bid - B;
     const int nq = (n + NPW - 1) / NPW;   // node groups per (sequence, q/k head)
     const int i0 = (wg % nq) * NPW;       // the workgroup's first node
     const int g = (wg / nq) % Hk;
@@ -421,6 +421,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
         if (lane < G)
             ws.abk[(static_cast<size_t>(m0 + i) * Hv + G * g + lane) * 4 + 2] = kq;
     }
+}
+
+// Workgroup bid < B builds sequence bid's tables; the rest prepare node operands.
+template <int D, typename Act, int NPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tree_prep_kernel(const Act* __restrict__ tail, const Act* __restrict__ w,
+                                                        int n, const int32_t* __restrict__ parent,
+                                                        const Act* __restrict__ x, const float* __restrict__ a,
+                                                        const float* __restrict__ b, TreeWs ws,
+                                                        int32_t* __restrict__ status, int B, int Hk, int Hv, int C) {
+    tree_prep_body<D, Act, NPW>(blockIdx.x, tail, w, n, parent, x, a, b, ws, status, B, Hk, Hv, C);
 }
 
 
@@ -814,7 +824,7 @@ __device__ __forceinline__ int ut_channel(int lc, int g, int h, int Hk) {
 // budget of 168 (three per CU) spills.  Measured on the 27B-class layer: 93.9
 // against 97.6 us for 64 trees with the widening conv at three per CU.
 template <int D, typename Act>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void tree_ut_kernel(
+__device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
     const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
     const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
     const float* __restrict__ b, float* __restrict__ o, int32_t* __restrict__ status, int Hk, int Hv, int C) {
@@ -839,7 +849,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     // argument loads issue together (one kernel-argument round trip).
     asm volatile("" : "+s"(Hv) : "s"(Sc), "s"(tail), "s"(w), "s"(n), "s"(parent), "s"(x), "s"(a), "s"(b), "s"(o),
                  "s"(status), "s"(Hk), "s"(C));
-    const int id = xcd_packed_id(blockIdx.x, gridDim.x);
+    const int id = xcd_packed_id(bid, nblocks);
     const int bq = id / Hv, h = id % Hv, g = h / (Hv / Hk);
     const int m0 = bq * n;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -1311,6 +1321,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
             }
 }
 
+template <int D, typename Act>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void tree_ut_kernel(
+    const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
+    const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
+    const float* __restrict__ b, float* __restrict__ o, int32_t* __restrict__ status, int Hk, int Hv, int C) {
+    tree_ut_body<D, Act>(blockIdx.x, gridDim.x, Sc, tail, w, n, parent, x, a, b, o, status, Hk, Hv, C);
+}
+
+// The one-launch UT verify and the prep of a workspace for a prepared commit,
+// in one grid: workgroups [0, ut_blocks) verify (their ids packed by XCD as
+// in tree_ut_kernel), the rest are tree_prep_kernel's workgroups.  The two
+// parts share nothing but the inputs, so at small batches (where neither
+// fills the chip) they run side by side instead of one after the other.
+// The tree's status is written by the verify part only.
+template <int D, typename Act>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void tree_ut_prep_kernel(
+    const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
+    const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
+    const float* __restrict__ b, float* __restrict__ o, int32_t* __restrict__ status, TreeWs ws, int B, int Hk,
+    int Hv, int C, int ut_blocks) {
+    if (static_cast<int>(blockIdx.x) < ut_blocks)
+        tree_ut_body<D, Act>(blockIdx.x, ut_blocks, Sc, tail, w, n, parent, x, a, b, o, status, Hk, Hv, C);
+    else
+        tree_prep_body<D, Act, 1>(blockIdx.x - ut_blocks, tail, w, n, parent, x, a, b, ws, nullptr, B, Hk, Hv, C);
+}
+
 // The two-launch form of the same verify: the prep launch convolves and
 // normalises every node's operands into the workspace (where a prepared
 // commit can read them), spread over many workgroups, and the UT workgroup
@@ -1629,10 +1665,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 }
 
 // The UT-form verify of a tree, or of a block when parent is null.  With no
-// workspace, the one launch; with one, the prep launch fills it (for a
-// prepared commit to read) and the UT kernel reads its operands from it.
-// Measured on the 27B-class layer, one launch against two: 16.0 us against
-// 15.3 at one tree, 23.7 against 31.0 at 8, 104 against 120 at 64.
+// workspace, the one launch; with one, the workspace is filled for a prepared
+// commit to read: at small batches by prep workgroups in the same launch as
+// the one-launch verify, otherwise by the prep launch, after which the UT
+// kernel reads its operands from it.  Measured on the 27B-class layer, the
+// one-launch form against prep + workspace UT kernel: 16.0 us against 15.3 at
+// one tree, 23.7 against 31.0 at 8, 104 against 120 at 64 (before the
+// dot-product conv).
+// Up to this batch the UT verify with a workspace runs as one launch (the
+// one-launch verify beside the prep of the workspace); above it, the prep
+// launch and the UT kernel that reads the prepared operands.  Measured on the
+// 27B-class layer (32-node trees, graphs of 64 calls), one launch against two:
+// 13.3 / 16.4 us at batch 1, 13.9 / 18.2 at 2, 20.5 / 22.1 at 4, 40.3 / 31.2
+// at 8 (the prep part's many small workgroups then queue behind the verify's).
+constexpr int kUtPrepMaxBatch = 4;
+
 hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail, const void* w, int n,
                                  const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                                  int32_t* status, void* ws, hipStream_t s) {
@@ -1645,6 +1692,16 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
                                static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C);
         });
     const TreeWs W = tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D);
+    if (g.B <= kUtPrepMaxBatch)
+        return dispatch(g, [&](auto dtag, auto atag) {
+            constexpr int D = decltype(dtag)::value;
+            using Act = decltype(atag);
+            const int ut_blocks = g.B * g.Hv, prep_blocks = g.B + g.B * g.Hk * n;
+            hipLaunchKernelGGL((tree_ut_prep_kernel<D, Act>), dim3(static_cast<unsigned>(ut_blocks + prep_blocks)),
+                               dim3(256), 0, s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n,
+                               parent, static_cast<const Act*>(x), a, b, o, status, W, g.B, g.Hk, g.Hv, g.C,
+                               ut_blocks);
+        });
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);

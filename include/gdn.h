@@ -206,12 +206,16 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
  *   workspace NULL   one launch: each (sequence, value head) workgroup
  *                    convolves, normalises and gates its own nodes' operands;
  *                    nothing is prepared for gdn_commit_path_prepared (commit
- *                    with gdn_commit_path).  The faster form from two trees on.
- *   workspace given  (>= gdn_tree_workspace_bytes) two launches: the nodes'
- *                    operands are prepared in the workspace, as by
- *                    gdn_tree_verify, and gdn_commit_path_prepared may follow.
+ *                    with gdn_commit_path).
+ *   workspace given  (>= gdn_tree_workspace_bytes) the nodes' operands are
+ *                    also prepared in the workspace, as by gdn_tree_verify,
+ *                    and gdn_commit_path_prepared may follow.  Up to 4
+ *                    sequences this is still one launch (the verify of the
+ *                    first form beside the preparation, whose outputs it
+ *                    shares); above, two launches, the second reading the
+ *                    prepared operands.
  * The outputs agree with token-by-token decode to rounding (within 1e-4
- * normwise of the sequential definition), not bit for bit, and the two forms
+ * normwise of the sequential definition), not bit for bit, and the forms may
  * round differently.  A commit of the accepted path is exact either way: it
  * replays the path.
  */
