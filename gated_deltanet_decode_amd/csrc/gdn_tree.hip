@@ -820,9 +820,9 @@ __device__ __forceinline__ int ut_channel(int lc, int g, int h, int Hk) {
 }
 
 // Two workgroups per CU: the checkpoint rows in flight (64 registers), the
-// conv operands and the split products need about 200 registers, and a
-// budget of 168 (three per CU) spills.  Measured on the 27B-class layer: 93.9
-// against 97.6 us for 64 trees with the widening conv at three per CU.
+// conv operands and the split products need about 194 registers, and a
+// budget of 168 (three per CU) spills.  Measured on the 27B-class layer, 64
+// trees: 88.8 us at two per CU against 113.7 at three (31 registers spilled).
 template <int D, typename Act>
 __device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
     const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
