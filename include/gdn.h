@@ -446,9 +446,10 @@ gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void*
  * library-held device array of GDN_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU,
  * held from the library's first use on that GPU until the process ends.  The
  * caller still passes inputs and outputs; arguments, outputs, statuses and
- * errors are gdn_tree_verify_ut's with a workspace (the two-launch form), and
- * the outputs are bit-identical to it.  (gdn_tree_verify_ut with no workspace
- * allocates nothing either; this call gives the two-launch form's bits.)
+ * errors are gdn_tree_verify_ut's with a workspace, and the outputs are
+ * bit-identical to it (above 4 sequences its two-launch form, whose verify
+ * reads the prepared operands back).  gdn_tree_verify_ut with no workspace
+ * allocates nothing either.
  *   GDN_ERR_WORKSPACE  gdn_tree_workspace_bytes(d, n_nodes) exceeds the array
  *                      (at 16 q/k and 48 value heads of 128 and 32 nodes: more
  *                      than 12 sequences)
