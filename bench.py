@@ -379,6 +379,20 @@ def main():
         res["decode_b64"]["kernel_us"] = us
         res["decode_b64"]["kernel_GBps"] = db / us / 1e3
         res["decode_b64"]["kernel_frac_hbm"] = db / us / 1e3 / HBM_PEAK_GBS
+        # the same steps in place on one batch of 64 states (201 MB, which fits the 256 MB Infinity Cache)
+        cnt_ip = [0]
+
+        def step64_in_place(t):
+            i = cnt_ip[0] % 2
+            gdn.decode_token(d64, S64[0], tails64[i][0], tails64[1 - i][0], w64, x64[t], a64[t], b64[t], o64)
+            cnt_ip[0] += 1
+
+        us = graph_time_us(torch, lambda t: step64_in_place(16 + t), steps64, reps=2)
+        res["decode_b64_in_place"] = {"ms_per_step": us / 1e3, "GBps": tb / us / 1e3,
+                                      "tokens_per_s": B / us * 1e6, "frac_hbm": tb / us / 1e3 / HBM_PEAK_GBS,
+                                      "launch": "hipGraph", "call": "gdn_decode_token",
+                                      "state_buffers": "1 batch of 64 in place (201 MB: may be served from the "
+                                                       "Infinity Cache rather than HBM)"}
         if "kda" in rows:
             ak64 = f32(gi.channel_gates(6, shape, B, steps64 + 16))
 
