@@ -23,7 +23,7 @@ __all__ = [
     "tree_tables", "block_verify", "block_verify_ut", "block_commit", "block_commit_prepared", "state_signature", "snapshot", "restore", "prefill_chunked",
     "self_check_workspace_bytes", "self_check", "SELF_CHECK_PERTURB", "tree_verify_ut_noalloc",
     "NOALLOC_SCRATCH_BYTES",
-    "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "F32", "BF16",
+    "LIB_PATH", "MAX_TREE_NODES", "MAX_TREE_DEPTH", "PREFILL_CHUNK", "PREFILL_SEGMENT", "F32", "BF16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 MAX_TREE_NODES = 32
 MAX_TREE_DEPTH = 8
 PREFILL_CHUNK = 64
+PREFILL_SEGMENT = 4096   # tokens per group of prefill launches; the workspace stops growing here
 F32, BF16 = 0, 1
 SELF_CHECK_PERTURB = 1
 NOALLOC_SCRATCH_BYTES = 16 << 20

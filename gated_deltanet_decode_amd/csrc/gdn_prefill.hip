@@ -13,7 +13,7 @@
 // Only differences G_i - G_j with i >= j are exponentiated, so nothing
 // overflows however strong the decay.
 //
-// Work split for MI355X, per segment of at most 2,048 tokens, every chunk
+// Work split for MI355X, per segment of at most 4,096 tokens, every chunk
 // product on fp16 MFMAs (fp32 accumulation):
 //   conv  (parallel over 32-token blocks x q/k heads): conv + SiLU of the
 //         q/k head's channels and of its value heads' channels, q/k L2 norm;
@@ -28,7 +28,7 @@
 //         O = s (e^G (.) Q S0^T + P U), S <- e^{G_n} S + (e^{G_n - G} (.) U)^T K.
 //         The state is held transposed in accumulator tiles, so the
 //         recurrence passes from one product to the next in registers.
-// The workspace holds one segment (about 114 MB at the 27B-class shape),
+// The workspace holds one segment (about 228 MB at the 27B-class shape),
 // whatever the prompt length, small enough to live in the Infinity Cache.
 #include <algorithm>
 #include <utility>
@@ -45,7 +45,12 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;       // head width handled by the prefill kernels
 constexpr int CH = 64;       // chunk length
-constexpr int SEG = 2048;    // tokens per segment
+// Tokens per segment: the workspace of one segment (about 228 MB at the
+// 27B-class shape) still fits the 256 MB Infinity Cache between its writes
+// (conv, tri) and its reads (tri, scan).  Measured on that layer at T = 32,768:
+// 1,226-1,278 us at 4,096 against 1,363 at 2,048, 1,570 at 1,024 and 1,586 at
+// 8,192 (whose workspace no longer fits).
+constexpr int SEG = 4096;
 constexpr int TB = 16;       // tokens per conv sub-block (one k-step of a chunk)
 constexpr int DS = 32;       // state rows per scan workgroup
 constexpr int NS = D / DS;   // scan workgroups per value head
@@ -799,7 +804,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ 
     } else {
         // ---- output, token tile tt
         const int tt = wave - 2;
-        const uint32_t ostride = static_cast<uint32_t>(Hv) * D;   // a segment's o (2,048 rows) spans < 4 G floats
+        const uint32_t ostride = static_cast<uint32_t>(Hv) * D;   // a chunk's o (64 rows) spans < 4 G floats
         float* obase = o + ((static_cast<size_t>(bq) * T + seg0) * Hv + h) * D + row0;
         auto load = [&](OutOps& op, int cl) {
             const _Float16* qc = ws.q + (kbase + cl) * kChunkQK;

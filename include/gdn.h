@@ -290,7 +290,7 @@ gdn_status gdn_tree_tables(int32_t n_nodes, const int32_t* parent, int32_t* dept
  *   conv_tail act [B][C][4]        in/out
  *   x act [B][T][C];  a, b f32 [B][T][Hv];  o f32 [B][T][Hv][dv] (written)
  *   workspace device bytes >= gdn_prefill_workspace_bytes(d, T), 256-byte
- *             aligned; its size depends on T only up to 2,048 tokens.
+ *             aligned; its size depends on T only up to 4,096 tokens.
  * This call needs head_k_dim == head_v_dim == 128 and num_v_heads / num_k_heads
  * <= 8 (GDN_ERR_SHAPE otherwise).  Outputs and state are within rounding of
  * the token-by-token calls: operands of the chunk products are fp16, sums and

@@ -50,6 +50,21 @@ def mk(**kw):
     return Dims(**d)
 
 
+def test_prefill_workspace_stops_growing_at_one_segment(lib):
+    """The binding's PREFILL_SEGMENT is the library's: the prefill workspace holds
+    one segment, so it grows with T (in 64-token chunks) up to it and no further."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_gdn_consts", os.path.join(ROOT, "gated_deltanet_decode_amd",
+                                                                               "__init__.py"))
+    src = open(spec.origin).read()
+    seg = int(re.search(r"^PREFILL_SEGMENT = (\d+)", src, re.M).group(1))
+    lib.gdn_prefill_workspace_bytes.restype = C.c_size_t
+    lib.gdn_prefill_workspace_bytes.argtypes = [C.POINTER(Dims), C.c_int32]
+    d = mk()
+    ws = lambda T: lib.gdn_prefill_workspace_bytes(C.byref(d), T)
+    assert ws(64) < ws(seg - 64) < ws(seg) == ws(seg + 64) == ws(8 * seg)
+
+
 def test_tree_workspace_is_bounded(lib):
     lib.gdn_tree_workspace_bytes.restype = C.c_size_t
     d = mk()

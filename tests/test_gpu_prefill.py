@@ -88,8 +88,9 @@ def test_batched_prompts():
 
 
 def test_crosses_segment_boundary():
-    """2,048-token segments: a prompt of 2,200 tokens spans two launches pairs."""
-    inp = gi.prefill_inputs(6, SMALL, 2200, state_sigma=0.1, tail_random=True)
+    """A prompt a little longer than one segment spans two groups of launches."""
+    import gated_deltanet_decode_amd as gdn
+    inp = gi.prefill_inputs(6, SMALL, gdn.PREFILL_SEGMENT + 152, state_sigma=0.1, tail_random=True)
     o, S, tail = gpu_prefill(inp)
     check_against_oracle(inp, o, S, tail)
 
@@ -122,12 +123,13 @@ def test_27b_layer_32768_tokens():
     assert np.array_equal(oracle.f64(tg), t_r)
 
 
-@pytest.mark.parametrize("split", [64, 128, 2048])
+@pytest.mark.parametrize("split", [64, 128, 2048, 4096])
 def test_split_at_chunk_boundary_is_bitwise(split):
-    inp = gi.prefill_inputs(7, SMALL, 2200, state_sigma=0.1, tail_random=True)
+    T = 4400   # past one segment, so that the unsplit call crosses a segment boundary too
+    inp = gi.prefill_inputs(7, SMALL, T, state_sigma=0.1, tail_random=True)
     o1, S1, t1 = gpu_prefill(inp)
     oa, Sa, ta = gpu_prefill(inp, T=split)
-    ob, Sb, tb = gpu_prefill(inp, T=2200 - split, S=Sa, tail=ta, x_off=split)
+    ob, Sb, tb = gpu_prefill(inp, T=T - split, S=Sa, tail=ta, x_off=split)
     assert torch.equal(S1.view(torch.int32), Sb.view(torch.int32))
     assert torch.equal(t1, tb)
     assert torch.equal(o1[:, :split].view(torch.int32), oa.view(torch.int32))
@@ -186,10 +188,11 @@ def test_refusals():
 
 
 def test_three_segments_pipelined():
-    """6,244 tokens = three full 2,048-token segments and a ragged fourth, the
+    """Three full segments and a ragged fourth (100 tokens), the
     workspace reused by each.  Checked against the oracle on all heads, and bit
     for bit against a second run."""
-    inp = gi.prefill_inputs(10, SMALL, 3 * 2048 + 100, state_sigma=0.1, tail_random=True)
+    import gated_deltanet_decode_amd as gdn
+    inp = gi.prefill_inputs(10, SMALL, 3 * gdn.PREFILL_SEGMENT + 100, state_sigma=0.1, tail_random=True)
     o, S, tail = gpu_prefill(inp)
     check_against_oracle(inp, o, S, tail)
     o2, S2, tail2 = gpu_prefill(inp)
@@ -206,7 +209,7 @@ def test_pipelined_call_keeps_caller_stream_order_and_graph_capture():
     for bit each time."""
     import gated_deltanet_decode_amd as gdn
     from tests.gpu_util import act_to_dev, dims_of, f32_to_dev
-    T = 2 * 2048 + 64
+    T = 2 * gdn.PREFILL_SEGMENT + 64
     inp = gi.prefill_inputs(11, SMALL, T, state_sigma=0.1, tail_random=True)
     ref_o, ref_S, ref_tail = gpu_prefill(inp)
     d = dims_of(SMALL, 1)
@@ -247,7 +250,7 @@ def test_pipelined_call_keeps_caller_stream_order_and_graph_capture():
         assert torch.equal(tail, ref_tail)
 
 
-@pytest.mark.parametrize("T", [150, 2100])
+@pytest.mark.parametrize("T", [150, 4200])
 def test_f32_activations(T):
     """fp32 activations (the float channel-pair loads of conv, the fp32 tail),
     from a random state and tail, within one segment and across two."""
