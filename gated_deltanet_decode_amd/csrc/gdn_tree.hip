@@ -1672,9 +1672,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 // one-launch form against prep + workspace UT kernel: 16.0 us against 15.3 at
 // one tree, 23.7 against 31.0 at 8, 104 against 120 at 64 (before the
 // dot-product conv).
-// Up to this batch the UT verify with a workspace runs as one launch (the
-// one-launch verify beside the prep of the workspace); above it, the prep
-// launch and the UT kernel that reads the prepared operands.  Measured on the
+// Up to this batch (bf16 activations) the UT verify with a workspace runs as
+// one launch (the one-launch verify beside the prep of the workspace); above
+// it, the prep launch and the UT kernel that reads the prepared operands.  Measured on the
 // 27B-class layer (32-node trees, graphs of 64 calls), one launch against two:
 // 13.3 / 16.4 us at batch 1, 13.9 / 18.2 at 2, 20.5 / 22.1 at 4, 40.3 / 31.2
 // at 8 (the prep part's many small workgroups then queue behind the verify's).
@@ -1692,15 +1692,19 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
                                static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C);
         });
     const TreeWs W = tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D);
-    if (g.B <= kUtPrepMaxBatch)
+    // bf16 activations only: with fp32 ones the verify's staging alone takes
+    // half a CU's LDS, and the prep's share would leave one workgroup per CU.
+    if (g.B <= kUtPrepMaxBatch && g.bf16)
         return dispatch(g, [&](auto dtag, auto atag) {
             constexpr int D = decltype(dtag)::value;
             using Act = decltype(atag);
-            const int ut_blocks = g.B * g.Hv, prep_blocks = g.B + g.B * g.Hk * n;
-            hipLaunchKernelGGL((tree_ut_prep_kernel<D, Act>), dim3(static_cast<unsigned>(ut_blocks + prep_blocks)),
-                               dim3(256), 0, s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n,
-                               parent, static_cast<const Act*>(x), a, b, o, status, W, g.B, g.Hk, g.Hv, g.C,
-                               ut_blocks);
+            if constexpr (sizeof(Act) == 2) {
+                const int ut_blocks = g.B * g.Hv, prep_blocks = g.B + g.B * g.Hk * n;
+                hipLaunchKernelGGL((tree_ut_prep_kernel<D, Act>),
+                                   dim3(static_cast<unsigned>(ut_blocks + prep_blocks)), dim3(256), 0, s, S,
+                                   static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                                   static_cast<const Act*>(x), a, b, o, status, W, g.B, g.Hk, g.Hv, g.C, ut_blocks);
+            }
         });
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
@@ -1739,14 +1743,16 @@ static bool tail_share_fits(const Geo& g) {
 // workgroups share its C channels out, one thread per channel.  A sequence
 // whose len is out of range keeps its state and tail and gets status
 // GDN_ERR_INDEX.
-template <int D, int ROWS>
+// MAXL (8, 16 or 32) bounds the block length, and so the LDS a workgroup
+// holds: a shorter bound lets more workgroups share a CU.
+template <int D, int ROWS, int MAXL>
 struct alignas(16) BlockSmem {
-    float qk[kMaxNodes][2 * D];   // q^|k^ of each position
-    float v[kMaxNodes][ROWS];     // v of the workgroup's rows
-    float kq[kMaxNodes], alpha[kMaxNodes], beta[kMaxNodes];
+    float qk[MAXL][2 * D];   // q^|k^ of each position
+    float v[MAXL][ROWS];     // v of the workgroup's rows
+    float kq[MAXL], alpha[MAXL], beta[MAXL];
 };
 
-template <int D, typename Act>
+template <int D, typename Act, int MAXL>
 __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S, Act* __restrict__ tail, int k,
                                                            const Act* __restrict__ x,
                                                            const int32_t* __restrict__ accepted,
@@ -1755,7 +1761,7 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
     constexpr int ROWS = 4 * RPW;
-    __shared__ BlockSmem<D, ROWS> sm;
+    __shared__ BlockSmem<D, ROWS, MAXL> sm;
     asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(tail), "s"(k), "s"(x), "s"(accepted), "s"(o), "s"(status),
                  "s"(Hk), "s"(Hv), "s"(C));
     const int wid = xcd_packed_id(blockIdx.x, gridDim.x);
@@ -1801,7 +1807,7 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
     // The positions' operands: q|k of the q/k head, v of this workgroup's
     // rows, (alpha, beta, k.q) of the value head; one 16-byte unit per load.
     constexpr int U = D / 2 + ROWS / 4 + 1;             // units per position
-    constexpr int NL = (kMaxNodes * U + 255) / 256;     // units per thread
+    constexpr int NL = (MAXL * U + 255) / 256;          // units per thread
     float4 un[NL];
 #pragma unroll
     for (int e = 0; e < NL; ++e) {
@@ -1883,9 +1889,18 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
         using Act = decltype(atag);
         const int bph = D / (4 * Row<D>::RPW);
         const unsigned grid = static_cast<unsigned>(g.B * g.Hv * bph);
-        if (commit)
-            hipLaunchKernelGGL((block_commit_kernel<D, Act>), dim3(grid), dim3(256), 0, s, S, static_cast<Act*>(tail), k,
-                               static_cast<const Act*>(x), accepted, o, status, g.Hk, g.Hv, g.C, bph, W);
+        if (commit && k <= 8)
+            hipLaunchKernelGGL((block_commit_kernel<D, Act, 8>), dim3(grid), dim3(256), 0, s, S,
+                               static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
+                               g.Hv, g.C, bph, W);
+        else if (commit && k <= 16)
+            hipLaunchKernelGGL((block_commit_kernel<D, Act, 16>), dim3(grid), dim3(256), 0, s, S,
+                               static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
+                               g.Hv, g.C, bph, W);
+        else if (commit)
+            hipLaunchKernelGGL((block_commit_kernel<D, Act, kMaxNodes>), dim3(grid), dim3(256), 0, s, S,
+                               static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
+                               g.Hv, g.C, bph, W);
         else if (grid > 2u * 256u)
             hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::Chain>), dim3(grid), dim3(256), 0, s, S, k,
                                W, o, g.Hk, g.Hv, bph);

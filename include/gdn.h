@@ -210,7 +210,7 @@ gdn_status gdn_tree_verify(const gdn_dims* d, const float* state_ckpt, const voi
  *   workspace given  (>= gdn_tree_workspace_bytes) the nodes' operands are
  *                    also prepared in the workspace, as by gdn_tree_verify,
  *                    and gdn_commit_path_prepared may follow.  Up to 4
- *                    sequences this is still one launch (the verify of the
+ *                    sequences (bf16 activations) this is still one launch (the verify of the
  *                    first form beside the preparation, whose outputs it
  *                    shares); above, two launches, the second reading the
  *                    prepared operands.
@@ -447,8 +447,8 @@ gdn_status gdn_self_check(const gdn_dims* d, uint32_t seed, int32_t flags, void*
  * held from the library's first use on that GPU until the process ends.  The
  * caller still passes inputs and outputs; arguments, outputs, statuses and
  * errors are gdn_tree_verify_ut's with a workspace, and the outputs are
- * bit-identical to it (above 4 sequences its two-launch form, whose verify
- * reads the prepared operands back).  gdn_tree_verify_ut with no workspace
+ * bit-identical to it (above 4 sequences or with fp32 activations its
+ * two-launch form, whose verify reads the prepared operands back).  gdn_tree_verify_ut with no workspace
  * allocates nothing either.
  *   GDN_ERR_WORKSPACE  gdn_tree_workspace_bytes(d, n_nodes) exceeds the array
  *                      (at 16 q/k and 48 value heads of 128 and 32 nodes: more
