@@ -1725,11 +1725,23 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
 // Kernels that rewrite the conv tail themselves give each of a sequence's
 // B*Hv*bph workgroups ceil(C / (Hv*bph)) channels, one per thread.  With
 // C = 2*Hk*D + Hv*D <= 3*Hv*D that is at most 3*D/bph (96 for both supported
-// head widths); the launchers refuse a geometry where it would exceed 256.
-static bool tail_share_fits(const Geo& g) {
-    const int bph = g.D == 128 ? 128 / (4 * Row<128>::RPW) : 32 / (4 * Row<32>::RPW);   // row blocks per head
+// head widths at their fewest row blocks per head); the launchers refuse a
+// geometry where it would exceed 256.
+static bool tail_share_fits(const Geo& g, int bph) {
     return (g.C + g.Hv * bph - 1) / (g.Hv * bph) <= 256;
 }
+static int row_blocks_per_head(const Geo& g) {   // one pass of 4 row groups per workgroup
+    return g.D == 128 ? 128 / (4 * Row<128>::RPW) : 32 / (4 * Row<32>::RPW);
+}
+
+// From this many (sequence, value head) pairs on, a commit (of a path or of
+// a block) gives each wave two row groups.  Measured on the 27B-class layer
+// (graphs of 64 calls; prepared / replaying), paths in 32-node trees:
+// 82.1 / 105.4 us against 92.5 / 138.3 at 64 sequences, 13.1 / 22.8 against
+// 16.4 / 29.4 at 8, 9.8 / 16.7 against 10.0 / 19.3 at 4, the same to within
+// 2% at 1 and 2; 16-token blocks, 502 tokens accepted over 64 sequences:
+// 94.1 / 113.7 against 118.9 / 133.0.
+constexpr int64_t kCommitTwoPassMin = 192;
 
 // Block commit from the prepared operands of the block's positions (the prep
 // launch's workspace): each sequence's state advances by its first len =
@@ -1752,7 +1764,7 @@ struct alignas(16) BlockSmem {
     float kq[MAXL], alpha[MAXL], beta[MAXL];
 };
 
-template <int D, typename Act, int MAXL>
+template <int D, typename Act, int MAXL, int PASSES>
 __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S, Act* __restrict__ tail, int k,
                                                            const Act* __restrict__ x,
                                                            const int32_t* __restrict__ accepted,
@@ -1760,7 +1772,9 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
                                                            int Hk, int Hv, int C, int blocks_per_head, TreeWs ws) {
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
-    constexpr int ROWS = 4 * RPW;
+    constexpr int ROWS_PASS = 4 * RPW;
+    constexpr int ROWS = ROWS_PASS * PASSES;   // PASSES row groups per wave, as in commit_state_kernel
+    static_assert(ROWS <= D, "a workgroup's rows lie in one head");
     __shared__ BlockSmem<D, ROWS, MAXL> sm;
     asm volatile("" : "+s"(blocks_per_head) : "s"(S), "s"(tail), "s"(k), "s"(x), "s"(accepted), "s"(o), "s"(status),
                  "s"(Hk), "s"(Hv), "s"(C));
@@ -1773,13 +1787,17 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
     const int wave = threadIdx.x / kWave;
     const int r = lane % LPR;
     const int row0 = blk * ROWS;
-    const int lrow = wave * RPW + lane / LPR;
-    const int row = row0 + lrow;
-    float* Sh = S + (static_cast<size_t>(bq) * Hv + h) * D * D;
-    float4 s[NV];
+    int lrow[PASSES];   // the lane's row in each pass, within the workgroup's rows
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        s[j] = load_stream(Sh + row * D + R::key(j, r));
+    for (int p = 0; p < PASSES; ++p)
+        lrow[p] = p * ROWS_PASS + wave * RPW + lane / LPR;
+    float* Sh = S + (static_cast<size_t>(bq) * Hv + h) * D * D;
+    float4 s[PASSES][NV];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            s[p][j] = load_stream(Sh + (row0 + lrow[p]) * D + R::key(j, r));
     const int len = accepted[bq];
     const bool valid = len >= 0 && len <= k;
     if (status && wid % (blocks_per_head * Hv) == 0 && threadIdx.x == 0)
@@ -1844,29 +1862,42 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
     }
 
     float* ob = o ? o + static_cast<size_t>(bq) * k * Hv * D : nullptr;
-    TokOps<D> cur, nxt;
-    auto load_tok = [&](TokOps<D>& t, int i) {
+    TokOps<D> cur, nxt;   // v of pass 0 in .v, of the others in cv / nv
+    float cv[PASSES], nv[PASSES];
+    auto load_tok = [&](TokOps<D>& t, float (&vp)[PASSES], int i) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             t.k[j] = *reinterpret_cast<const float4*>(&sm.qk[i][D + R::key(j, r)]);
             t.q[j] = *reinterpret_cast<const float4*>(&sm.qk[i][R::key(j, r)]);
         }
-        t.v = sm.v[i][lrow];
+        t.v = sm.v[i][lrow[0]];
+#pragma unroll
+        for (int p = 1; p < PASSES; ++p)
+            vp[p] = sm.v[i][lrow[p]];
         t.alpha = sm.alpha[i];
         t.beta = sm.beta[i];
         t.kq = sm.kq[i];
     };
-    load_tok(cur, 0);
+    load_tok(cur, cv, 0);
     for (int i = 0; i < len; ++i) {
-        load_tok(nxt, i + 1 < len ? i + 1 : i);
-        const float out = row_update<D>(s, cur.k, cur.q, cur.alpha, cur.beta, cur.v, cur.kq);
-        if (ob && r == 0)
-            ob[(static_cast<size_t>(i) * Hv + h) * D + row] = out;
+        load_tok(nxt, nv, i + 1 < len ? i + 1 : i);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const float out =
+                row_update<D>(s[p], cur.k, cur.q, cur.alpha, cur.beta, p == 0 ? cur.v : cv[p], cur.kq);
+            if (ob && r == 0)
+                ob[(static_cast<size_t>(i) * Hv + h) * D + row0 + lrow[p]] = out;
+        }
         cur = nxt;
+#pragma unroll
+        for (int p = 1; p < PASSES; ++p)
+            cv[p] = nv[p];
     }
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        store_stream(Sh + row * D + R::key(j, r), s[j]);
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            store_stream(Sh + (row0 + lrow[p]) * D + R::key(j, r), s[p][j]);
 }
 
 // prepared: the workspace already holds the block's operands (from the
@@ -1874,7 +1905,9 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
 hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const void* w, int k, const void* x,
                         const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
                         bool prepared, hipStream_t s) {
-    if (commit && !tail_share_fits(g))
+    const bool two = commit && g.D == 128 && static_cast<int64_t>(g.B) * g.Hv >= kCommitTwoPassMin;
+    const int cbph = row_blocks_per_head(g) / (two ? 2 : 1);   // row blocks per head of the commit
+    if (commit && !tail_share_fits(g, cbph))
         return hipErrorInvalidValue;
     const TreeWs W = tree_ws_carve(ws, g.B, k, g.Hk, g.Hv, g.D);
     hipError_t e = prepared ? hipSuccess : dispatch(g, [&](auto dtag, auto atag) {
@@ -1889,19 +1922,31 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
         using Act = decltype(atag);
         const int bph = D / (4 * Row<D>::RPW);
         const unsigned grid = static_cast<unsigned>(g.B * g.Hv * bph);
-        if (commit && k <= 8)
-            hipLaunchKernelGGL((block_commit_kernel<D, Act, 8>), dim3(grid), dim3(256), 0, s, S,
-                               static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
-                               g.Hv, g.C, bph, W);
-        else if (commit && k <= 16)
-            hipLaunchKernelGGL((block_commit_kernel<D, Act, 16>), dim3(grid), dim3(256), 0, s, S,
-                               static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
-                               g.Hv, g.C, bph, W);
-        else if (commit)
-            hipLaunchKernelGGL((block_commit_kernel<D, Act, kMaxNodes>), dim3(grid), dim3(256), 0, s, S,
-                               static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
-                               g.Hv, g.C, bph, W);
-        else if (grid > 2u * 256u)
+        auto commit_go = [&](auto ptag) {
+            constexpr int PASSES = decltype(ptag)::value;
+            const dim3 cgrid(static_cast<unsigned>(g.B * g.Hv * cbph));
+            if (k <= 8)
+                hipLaunchKernelGGL((block_commit_kernel<D, Act, 8, PASSES>), cgrid, dim3(256), 0, s, S,
+                                   static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
+                                   g.Hv, g.C, cbph, W);
+            else if (k <= 16)
+                hipLaunchKernelGGL((block_commit_kernel<D, Act, 16, PASSES>), cgrid, dim3(256), 0, s, S,
+                                   static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
+                                   g.Hv, g.C, cbph, W);
+            else
+                hipLaunchKernelGGL((block_commit_kernel<D, Act, kMaxNodes, PASSES>), cgrid, dim3(256), 0, s, S,
+                                   static_cast<Act*>(tail), k, static_cast<const Act*>(x), accepted, o, status, g.Hk,
+                                   g.Hv, g.C, cbph, W);
+        };
+        if (commit) {
+            if constexpr (D == 128) {
+                if (two) {
+                    commit_go(std::integral_constant<int, 2>{});
+                    return;
+                }
+            }
+            commit_go(std::integral_constant<int, 1>{});
+        } else if (grid > 2u * 256u)
             hipLaunchKernelGGL((tree_verify_kernel<D, WalkWide, WalkKind::Chain>), dim3(grid), dim3(256), 0, s, S, k,
                                W, o, g.Hk, g.Hv, bph);
         else
@@ -1916,7 +1961,10 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
 // reads the tail, and the kernel also rewrites it (tail_out, the same buffer):
 // each channel by one thread, after the path is validated.  Otherwise the
 // conv reads the tail here and commit_tail_kernel rewrites it afterwards.
-template <int D, typename Act, bool PREPARED>
+// PASSES: row groups per wave (a workgroup covers 4 * RPW * PASSES rows).  Two
+// halve the per-row share of the path's operand loads and the validation, and
+// give each token's replay two independent row updates.
+template <int D, typename Act, bool PREPARED, int PASSES>
 __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S, const Act* __restrict__ tail,
                                                            Act* __restrict__ tail_out, const Act* __restrict__ w,
                                                            int n,
@@ -1928,7 +1976,9 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
                                                            int blocks_per_head, TreeWs ws) {
     using R = Row<D>;
     constexpr int NV = R::NV, LPR = R::LPR, RPW = R::RPW;
-    constexpr int ROWS = 4 * RPW;
+    constexpr int ROWS_PASS = 4 * RPW;
+    constexpr int ROWS = ROWS_PASS * PASSES;
+    static_assert(ROWS <= D, "a workgroup's rows lie in one head");
     __shared__ NodeSmem<D, ROWS, kMaxDepth, Act> sm;
 
     // The index arithmetic is made to depend on every argument, so all the
@@ -1946,8 +1996,10 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     const int wave = threadIdx.x / kWave;
     const int r = lane % LPR;
     const int row0 = blk * ROWS;
-    const int lrow = wave * RPW + lane / LPR;
-    const int row = row0 + lrow;
+    int lrow[PASSES];   // the lane's row in each pass, within the workgroup's rows
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        lrow[p] = p * ROWS_PASS + wave * RPW + lane / LPR;
     parent += static_cast<size_t>(bq) * n;
     path += static_cast<size_t>(bq) * L;
     x += static_cast<size_t>(bq) * n * C;
@@ -1957,10 +2009,12 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
     tail_out += PREPARED ? static_cast<size_t>(bq) * C * 4 : 0;
 
     float* Sh = S + (static_cast<size_t>(bq) * Hv + h) * D * D;
-    float4 s[NV];
+    float4 s[PASSES][NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        s[j] = load_stream(Sh + row * D + R::key(j, r));
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            s[p][j] = load_stream(Sh + (row0 + lrow[p]) * D + R::key(j, r));
 
     // Token i of the commit is path position i; its ancestors are the
     // positions before it.  The row's length is the index of its first -1.
@@ -2058,18 +2112,35 @@ __global__ __launch_bounds__(256) void commit_state_kernel(float* __restrict__ S
         return;
 
     float* ob = o ? o + static_cast<size_t>(bq) * L * Hv * D : nullptr;
-    TokOps<D> cur, nxt;
-    tok_load(cur, sm, 0, r, lrow);
+    TokOps<D> cur, nxt;   // v of pass 0 in .v, of the others in cv / nv
+    float cv[PASSES], nv[PASSES];
+    tok_load(cur, sm, 0, r, lrow[0]);
+#pragma unroll
+    for (int p = 1; p < PASSES; ++p)
+        cv[p] = sm.v[0][lrow[p]];
     for (int i = 0; i < len; ++i) {
-        tok_load(nxt, sm, i + 1 < len ? i + 1 : i, r, lrow);
-        const float out = row_update<D>(s, cur.k, cur.q, cur.alpha, cur.beta, cur.v, cur.kq);
-        if (ob && r == 0)
-            ob[(static_cast<size_t>(i) * Hv + h) * D + row] = out;
+        const int i1 = i + 1 < len ? i + 1 : i;
+        tok_load(nxt, sm, i1, r, lrow[0]);
+#pragma unroll
+        for (int p = 1; p < PASSES; ++p)
+            nv[p] = sm.v[i1][lrow[p]];
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const float out =
+                row_update<D>(s[p], cur.k, cur.q, cur.alpha, cur.beta, p == 0 ? cur.v : cv[p], cur.kq);
+            if (ob && r == 0)
+                ob[(static_cast<size_t>(i) * Hv + h) * D + row0 + lrow[p]] = out;
+        }
         cur = nxt;
+#pragma unroll
+        for (int p = 1; p < PASSES; ++p)
+            cv[p] = nv[p];
     }
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        store_stream(Sh + row * D + R::key(j, r), s[j]);
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            store_stream(Sh + (row0 + lrow[p]) * D + R::key(j, r), s[p][j]);
 }
 
 // The tail after a commit holds the last four raw inputs of (old tail ++ path).
@@ -2122,22 +2193,35 @@ __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
                          int32_t* status, void* ws, hipStream_t s) {
-    if (ws != nullptr && !tail_share_fits(g))
+    // Two passes per wave (half as many workgroups) once the batch fills the chip.
+    const bool two = g.D == 128 && static_cast<int64_t>(g.B) * g.Hv >= kCommitTwoPassMin;
+    const int bph = row_blocks_per_head(g) / (two ? 2 : 1);
+    if (ws != nullptr && !tail_share_fits(g, bph))
         return hipErrorInvalidValue;
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
         constexpr int D = decltype(dtag)::value;
         using Act = decltype(atag);
-        const int bph = D / (4 * Row<D>::RPW);
-        if (ws == nullptr)
-            hipLaunchKernelGGL((commit_state_kernel<D, Act, false>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)),
-                               dim3(256), 0, s, S, static_cast<const Act*>(tail), nullptr, static_cast<const Act*>(w), n,
-                               parent, static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph,
-                               TreeWs{});
-        else
-            hipLaunchKernelGGL((commit_state_kernel<D, Act, true>), dim3(static_cast<unsigned>(g.B * g.Hv * bph)),
-                               dim3(256), 0, s, S, nullptr, static_cast<Act*>(tail), nullptr, n, parent,
-                               static_cast<const Act*>(x), nullptr, nullptr, L, path, o, status, g.Hk, g.Hv, g.C, bph,
-                               tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D));
+        auto go = [&](auto ptag) {
+            constexpr int PASSES = decltype(ptag)::value;
+            const dim3 grid(static_cast<unsigned>(g.B * g.Hv * bph));
+            if (ws == nullptr)
+                hipLaunchKernelGGL((commit_state_kernel<D, Act, false, PASSES>), grid, dim3(256), 0, s, S,
+                                   static_cast<const Act*>(tail), nullptr, static_cast<const Act*>(w), n, parent,
+                                   static_cast<const Act*>(x), a, b, L, path, o, status, g.Hk, g.Hv, g.C, bph,
+                                   TreeWs{});
+            else
+                hipLaunchKernelGGL((commit_state_kernel<D, Act, true, PASSES>), grid, dim3(256), 0, s, S, nullptr,
+                                   static_cast<Act*>(tail), nullptr, n, parent, static_cast<const Act*>(x), nullptr,
+                                   nullptr, L, path, o, status, g.Hk, g.Hv, g.C, bph,
+                                   tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D));
+        };
+        if constexpr (D == 128) {
+            if (two) {
+                go(std::integral_constant<int, 2>{});
+                return;
+            }
+        }
+        go(std::integral_constant<int, 1>{});
     });
     if (e != hipSuccess || ws != nullptr)   // the prepared form rewrote the tail itself
         return e;
