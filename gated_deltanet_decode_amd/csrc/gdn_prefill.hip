@@ -576,20 +576,21 @@ __global__ __launch_bounds__(256) void tri_kernel(const float* __restrict__ a, c
 //   output (waves 2, 3: token tile 32 (w - 2)) compute Y = Q S0^T and P U one
 //          chunk behind on 32x32x16 MFMAs and store o = s (e^G Y + P U); Q and
 //          P stream through a register ring.
-//   copies (waves 4, 5) copy W~, the q/k head's k^T, this slice's U~, e^G and
-//          e^{G_n - G} of chunk k + 2 into a three-stage LDS ring by direct
-//          global-to-LDS loads, and wait for chunk k + 1 before the barrier
-//          that ends step k.  Two waves share the copies so that two chunks'
-//          worth stays within each wave's outstanding vector loads.
+//   copies (waves 4, 5) copy the q/k head's k^T, this slice's U~, e^G and
+//          e^{G_n - G} of chunk k + 2 and W~ of chunk k + 3 into a three-stage
+//          LDS ring by direct global-to-LDS loads, and wait for the previous
+//          group before the barrier that ends step k.  Two waves share the
+//          copies so that two groups' worth stays within each wave's
+//          outstanding vector loads.
 // Splitting the rows over two waves halves the matrix and vector work on the
 // recurrence's dependent chain; each state wave still reads the whole chunk's
-// W~ and k^T (32 KB) from LDS.
+// W~ and k^T (32 KB) from LDS, k^T one read behind each product of Z and the
+// next chunk's W~ one read behind each product of the update (hence W~ one
+// chunk ahead in the ring).
 // Workgroups of one (sequence, q/k head) share an XCD and its L2.
 constexpr int kStages = 3;
 constexpr int kOutRing = 2;
 constexpr int kScanThreads = 6 * kWave;
-constexpr int kDmaW = 16 + 2;   // wave 4, per chunk: W~ (16 KB), e^G, e^{G_n - G}
-constexpr int kDmaK = 16 + 4;   // wave 5, per chunk: k^T (16 KB), U~ (two 2 KB tiles)
 
 struct alignas(16) ScanSmem {
     h8 wt[kStages][16][64];     // W~ fragments (token tile, key step)
@@ -600,6 +601,10 @@ struct alignas(16) ScanSmem {
     h8 xs[2][8][64];            // S0^T as 32x32x16 B fragments (key step)
     h8 xu[2][4][64];            // U as 32x32x16 B fragments (token step)
 };
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -668,20 +673,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ 
     const int len = min(SEG, T - seg0);
 
     if (wave >= 4) {
-        // ---- copies: wave 4 W~, e^G and e^{G_n - G}; wave 5 k^T and U~ (each
-        // wave's copies of two chunks fit its 63 outstanding vector loads)
-        auto issue = [&](int cl) {
-            const int st = cl % kStages;
+        // ---- copies, in groups: group j (j = -1 .. nch - 1) is W~ of chunk j + 1
+        // with e^G and e^{G_n - G} of chunk j (wave 4) and k^T and U~ of chunk j
+        // (wave 5), in ring slot (j + 3) % 3.  The state waves read group j's
+        // k^T during step j's Z and its W~ during step j's update, so W~ runs one
+        // chunk ahead of the rest.  Each wave's copies of two groups fit its 63
+        // outstanding vector loads.
+        auto count = [&](int j) {   // copies this wave issues for group j
+            return wave == 4 ? (j + 1 < nch ? 16 : 0) + (j >= 0 ? 2 : 0) : (j >= 0 ? 20 : 0);
+        };
+        auto issue = [&](int j) {
+            const int st = (j + kStages) % kStages;
             if (wave == 4) {
-                const char* wsrc = reinterpret_cast<const char*>(ws.wt + (vbase + cl) * kChunkQK) + lane * 16;
+                if (j + 1 < nch) {
+                    const char* wsrc = reinterpret_cast<const char*>(ws.wt + (vbase + j + 1) * kChunkQK) + lane * 16;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    __builtin_amdgcn_global_load_lds(wsrc + i * 1024, &sm.wt[st][i][0], 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(ws.eg + hbase + cl * CH + lane, &sm.eg[st][0], 4, 0, 0);
-                __builtin_amdgcn_global_load_lds(ws.ed + hbase + cl * CH + lane, &sm.ed[st][0], 4, 0, 0);
-            } else {
-                const char* ksrc = reinterpret_cast<const char*>(ws.kt + (kbase + cl) * kChunkQK) + lane * 16;
-                const char* usrc = reinterpret_cast<const char*>(ws.ut + (vbase + cl) * kChunkQK) + lane * 16;
+                    for (int i = 0; i < 16; ++i)
+                        __builtin_amdgcn_global_load_lds(wsrc + i * 1024, &sm.wt[st][i][0], 16, 0, 0);
+                }
+                if (j >= 0) {
+                    __builtin_amdgcn_global_load_lds(ws.eg + hbase + j * CH + lane, &sm.eg[st][0], 4, 0, 0);
+                    __builtin_amdgcn_global_load_lds(ws.ed + hbase + j * CH + lane, &sm.ed[st][0], 4, 0, 0);
+                }
+            } else if (j >= 0) {
+                const char* ksrc = reinterpret_cast<const char*>(ws.kt + (kbase + j) * kChunkQK) + lane * 16;
+                const char* usrc = reinterpret_cast<const char*>(ws.ut + (vbase + j) * kChunkQK) + lane * 16;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     __builtin_amdgcn_global_load_lds(ksrc + i * 1024, &sm.kt[st][i][0], 16, 0, 0);
@@ -693,24 +709,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ 
                                                          &sm.ut[st][tt][0][0] + h2 * 64, 16, 0, 0);
             }
         };
-        // wait until only the copies of the chunk just issued may be in flight
-        auto wait_one_behind = [&](bool issued) {
-            if (!issued)
-                wait_vmem<0>();
-            else if (wave == 4)
-                wait_vmem<kDmaW>();
-            else
-                wait_vmem<kDmaK>();
+        // wait until at most n of this wave's copies are in flight
+        auto wait_pending = [&](int n) {
+            switch (n) {
+            case 2: wait_vmem<2>(); break;
+            case 18: wait_vmem<18>(); break;
+            case 20: wait_vmem<20>(); break;
+            default: wait_vmem<0>(); break;
+            }
         };
+        issue(-1);
         issue(0);
         if (nch > 1)
             issue(1);
-        wait_one_behind(nch > 1);
+        wait_pending(nch > 1 ? count(1) : 0);
         __builtin_amdgcn_s_barrier();
         for (int k = 0; k < nch; ++k) {
             if (k + 2 < nch)
                 issue(k + 2);
-            wait_one_behind(k + 2 < nch);
+            wait_pending(k + 2 < nch ? count(k + 2) : 0);
             __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_s_barrier();
@@ -727,15 +744,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ 
         // this wave's B units for the output waves at (q % 2) * 32 + 16 wave + c.
         const int la0 = (q & 1) * 32 + (rho(0, c) & 31), la1 = (q & 1) * 32 + (rho(1, c) & 31);
         const int xl = (q & 1) * 32 + 16 * wave + c;
-        __syncthreads();
-        for (int k = 0; k < nch; ++k) {
-            const int stg = k % kStages, par = k & 1;
-            h8 wf[4][4];   // W~: token tile T, key step s
+        h8 wf[4][4];   // W~ of the current chunk: token tile T, key step s
+        auto read_wt = [&](int slot) {
 #pragma unroll
             for (int T4 = 0; T4 < 4; ++T4)
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    wf[T4][s] = sm.wt[stg][(T4 >> 1) * 8 + 2 * s + qs][(T4 & 1) ? la1 : la0];
+                    wf[T4][s] = sm.wt[slot][(T4 >> 1) * 8 + 2 * s + qs][(T4 & 1) ? la1 : la0];
+        };
+        __syncthreads();
+        read_wt(kStages - 1);   // W~ of chunk 0 (copy group -1)
+        for (int k = 0; k < nch; ++k) {
+            const int stg = k % kStages, par = k & 1;
             // token rho(T, 4 q + i) of U~'s accumulator tile T / 2 is value 8 (q / 2) + 4 (T % 2) + i of lane xl
             const h8 u0 = sm.ut[stg][0][xl][qs], u1 = sm.ut[stg][1][xl][qs];
             const float eglast = sm.eg[stg][CH - 1];
@@ -777,6 +797,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ 
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 sm.xs[par][2 * s + qs][xl] = bs[s];
+            // each k^T read issues behind one of Z's products
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // U = -Z; token step s2 of U is tiles 2 s2 and 2 s2 + 1
             h8 bu[2], bd[2];
 #pragma unroll
@@ -792,9 +819,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(float* __restrict__ 
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
                     st[t] = mma16(kf[t][s2], bd[s2], st[t]);
+            // the next chunk's W~ (copy group k) is read while the update is in the
+            // matrix pipe, one read behind each product (after the last chunk the
+            // slot holds no W~ and the values read go unused)
+            read_wt(stg);
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 sm.xu[par][2 * s2 + qs][xl] = bu[s2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
             __syncthreads();
         }
         __syncthreads();
