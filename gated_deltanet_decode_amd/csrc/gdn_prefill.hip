@@ -199,14 +199,17 @@ __global__ __launch_bounds__(640) void conv_kernel(const Act* __restrict__ x, co
     __shared__ __align__(16) float ys[TB][2 * D];    // q~ | k~ of a sub-block, fp32
     __shared__ __align__(16) _Float16 qkh[2][TB][D]; // q^, k^ of a sub-block, fp16
     // The workgroups of one chunk write the two halves of the same q^ / k^
-    // fragments; they share an XCD (blockIdx % 8 picks it).
+    // fragments; they share an XCD (blockIdx % 8 picks it).  The q/k head
+    // varies fastest, so the workgroups resident together read whole token
+    // rows of x rather than one head's pieces of many rows (a segment's conv
+    // 40.3 -> 38.0 us against chunk-fastest order).
     constexpr int BPC = CH / (SUB * TB);             // workgroups per chunk
     const int xcd = blockIdx.x % 8, r8 = blockIdx.x / 8;
-    const int chunk_id = (r8 / BPC) * 8 + xcd;       // (sequence, q/k head, chunk of the segment)
+    const int chunk_id = (r8 / BPC) * 8 + xcd;       // (sequence, chunk of the segment, q/k head)
     if (chunk_id >= B * Hk * nch)
         return;
-    const int cl = chunk_id % nch;
-    const int g = (chunk_id / nch) % Hk;
+    const int g = chunk_id % Hk;
+    const int cl = (chunk_id / Hk) % nch;
     const int bq = chunk_id / (nch * Hk);
     const int cb = (r8 % BPC) * SUB * TB;            // chunk offset of the workgroup's first token
     const int t0 = seg0 + cl * CH + cb;              // its prompt index
