@@ -823,7 +823,11 @@ __device__ __forceinline__ int ut_channel(int lc, int g, int h, int Hk) {
 // conv operands and the split products need about 194 registers, and a
 // budget of 168 (three per CU) spills.  Measured on the 27B-class layer, 64
 // trees: 88.8 us at two per CU against 113.7 at three (31 registers spilled).
-template <int D, typename Act>
+// With SPLIT = 2 each wave holds half as many checkpoint rows (133 registers).
+// SPLIT = 2 (small batches, D = 128): two workgroups per (sequence, value
+// head), each with half the rows: its share of the checkpoint, of the value
+// convolution and of the last product; both build the small matrices.
+template <int D, typename Act, int SPLIT = 1>
 __device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
     const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
     const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
@@ -833,7 +837,8 @@ __device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
     using bf8 = ut_bf8;
     using Sm = UtSmem<D, Act>;
     constexpr int NT = kMaxNodes;                 // nodes padded to two tiles of 16
-    constexpr int RT = D >= 64 ? D / 64 : 1;      // row tiles of 16 per wave in the last product
+    static_assert(SPLIT == 1 || (SPLIT == 2 && D == 128), "rows split in two for D = 128 only");
+    constexpr int RT = D >= 64 ? D / 64 / SPLIT : 1;   // row tiles of 16 per wave in the last product
     constexpr int NTW = D >= 64 ? 2 : 1;          // node tiles per wave in the last product
     constexpr int KS = D / 16;                    // 16-wide blocks of the key dim
     constexpr int ET = D / 32;                    // tiles of e per wave
@@ -849,12 +854,13 @@ __device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
     // argument loads issue together (one kernel-argument round trip).
     asm volatile("" : "+s"(Hv) : "s"(Sc), "s"(tail), "s"(w), "s"(n), "s"(parent), "s"(x), "s"(a), "s"(b), "s"(o),
                  "s"(status), "s"(Hk), "s"(C));
-    const int id = xcd_packed_id(bid, nblocks);
+    const int idp = xcd_packed_id(bid, nblocks);
+    const int id = idp / SPLIT, half = idp % SPLIT;   // a head's two halves share an XCD
     const int bq = id / Hv, h = id % Hv, g = h / (Hv / Hk);
     const int m0 = bq * n;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int q = lane >> 4, c = lane & 15;
-    const int rb = D >= 64 ? wave * 16 * RT : 16 * (wave >> 1);   // first checkpoint row of this wave
+    const int rb = D >= 64 ? half * (D / SPLIT) + wave * 16 * RT : 16 * (wave >> 1);   // first checkpoint row of this wave
     const int u0 = D >= 64 ? 0 : (wave & 1);                      // first node tile of this wave
 
     // Loads, all unconditional: the raw inputs of every node (padding nodes
@@ -984,11 +990,11 @@ __device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
     }
     __syncthreads();
     if (!sm.ok) {   // malformed tree: reported, nothing written
-        if (status && h == 0 && tid == 0)
+        if (status && h == 0 && half == 0 && tid == 0)
             status[bq] = 5;
         return;
     }
-    if (status && h == 0 && tid == 0)
+    if (status && h == 0 && half == 0 && tid == 0)
         status[bq] = 0;
 
     // The conv.  q and k: thread (node tid / 8, part tid % 8) convolves CPS
@@ -1321,12 +1327,12 @@ __device__ __forceinline__ void tree_ut_body(int bid, int nblocks,
             }
 }
 
-template <int D, typename Act>
+template <int D, typename Act, int SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void tree_ut_kernel(
     const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
     const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
     const float* __restrict__ b, float* __restrict__ o, int32_t* __restrict__ status, int Hk, int Hv, int C) {
-    tree_ut_body<D, Act>(blockIdx.x, gridDim.x, Sc, tail, w, n, parent, x, a, b, o, status, Hk, Hv, C);
+    tree_ut_body<D, Act, SPLIT>(blockIdx.x, gridDim.x, Sc, tail, w, n, parent, x, a, b, o, status, Hk, Hv, C);
 }
 
 // The one-launch UT verify and the prep of a workspace for a prepared commit,
@@ -1335,14 +1341,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
 // parts share nothing but the inputs, so at small batches (where neither
 // fills the chip) they run side by side instead of one after the other.
 // The tree's status is written by the verify part only.
-template <int D, typename Act>
+template <int D, typename Act, int SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void tree_ut_prep_kernel(
     const float* __restrict__ Sc, const Act* __restrict__ tail, const Act* __restrict__ w, int n,
     const int32_t* __restrict__ parent, const Act* __restrict__ x, const float* __restrict__ a,
     const float* __restrict__ b, float* __restrict__ o, int32_t* __restrict__ status, TreeWs ws, int B, int Hk,
     int Hv, int C, int ut_blocks) {
     if (static_cast<int>(blockIdx.x) < ut_blocks)
-        tree_ut_body<D, Act>(blockIdx.x, ut_blocks, Sc, tail, w, n, parent, x, a, b, o, status, Hk, Hv, C);
+        tree_ut_body<D, Act, SPLIT>(blockIdx.x, ut_blocks, Sc, tail, w, n, parent, x, a, b, o, status, Hk, Hv, C);
     else
         tree_prep_body<D, Act, 1>(blockIdx.x - ut_blocks, tail, w, n, parent, x, a, b, ws, nullptr, B, Hk, Hv, C);
 }
@@ -1679,17 +1685,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 // 13.3 / 16.4 us at batch 1, 13.9 / 18.2 at 2, 20.5 / 22.1 at 4, 40.3 / 31.2
 // at 8 (the prep part's many small workgroups then queue behind the verify's).
 constexpr int kUtPrepMaxBatch = 4;
+// Up to this many sequences (D = 128) each (sequence, value head) of the UT
+// verify is split over two workgroups by rows: at batch 1 and 2 only 48 or 96
+// of the 256 CUs would work, and the halves' shorter last step and smaller
+// checkpoint share outweigh building the small matrices twice.  Measured on the
+// 27B-class layer (32-node trees, graphs of 32 calls, bit-identical outputs),
+// split against whole: one launch 10.98 / 12.68 us at batch 1, 11.17 / 12.69
+// at 2, 15.01 / 13.36 at 4, 19.80 / 19.17 at 8, 112.1 / 93.0 at 64.
+constexpr int kUtSplitMaxBatch = 2;
 
 hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail, const void* w, int n,
                                  const int32_t* parent, const void* x, const float* a, const float* b, float* o,
                                  int32_t* status, void* ws, hipStream_t s) {
+    const bool split = g.D == 128 && g.B <= kUtSplitMaxBatch;
     if (ws == nullptr)
         return dispatch(g, [&](auto dtag, auto atag) {
             constexpr int D = decltype(dtag)::value;
             using Act = decltype(atag);
-            hipLaunchKernelGGL((tree_ut_kernel<D, Act>), dim3(static_cast<unsigned>(g.B * g.Hv)), dim3(256), 0, s,
-                               S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                               static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C);
+            if (D == 128 && split)
+                hipLaunchKernelGGL((tree_ut_kernel<D, Act, D == 128 ? 2 : 1>), dim3(static_cast<unsigned>(2 * g.B * g.Hv)),
+                                   dim3(256), 0, s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n,
+                                   parent, static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C);
+            else
+                hipLaunchKernelGGL((tree_ut_kernel<D, Act, 1>), dim3(static_cast<unsigned>(g.B * g.Hv)), dim3(256), 0,
+                                   s, S, static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                                   static_cast<const Act*>(x), a, b, o, status, g.Hk, g.Hv, g.C);
         });
     const TreeWs W = tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D);
     // bf16 activations only: with fp32 ones the verify's staging alone takes
@@ -1699,11 +1719,22 @@ hipError_t launch_tree_verify_ut(const Geo& g, const float* S, const void* tail,
             constexpr int D = decltype(dtag)::value;
             using Act = decltype(atag);
             if constexpr (sizeof(Act) == 2) {
-                const int ut_blocks = g.B * g.Hv, prep_blocks = g.B + g.B * g.Hk * n;
-                hipLaunchKernelGGL((tree_ut_prep_kernel<D, Act>),
-                                   dim3(static_cast<unsigned>(ut_blocks + prep_blocks)), dim3(256), 0, s, S,
-                                   static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
-                                   static_cast<const Act*>(x), a, b, o, status, W, g.B, g.Hk, g.Hv, g.C, ut_blocks);
+                const int prep_blocks = g.B + g.B * g.Hk * n;
+                if (D == 128 && split) {
+                    const int ut_blocks = 2 * g.B * g.Hv;
+                    hipLaunchKernelGGL((tree_ut_prep_kernel<D, Act, D == 128 ? 2 : 1>),
+                                       dim3(static_cast<unsigned>(ut_blocks + prep_blocks)), dim3(256), 0, s, S,
+                                       static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                                       static_cast<const Act*>(x), a, b, o, status, W, g.B, g.Hk, g.Hv, g.C,
+                                       ut_blocks);
+                } else {
+                    const int ut_blocks = g.B * g.Hv;
+                    hipLaunchKernelGGL((tree_ut_prep_kernel<D, Act, 1>),
+                                       dim3(static_cast<unsigned>(ut_blocks + prep_blocks)), dim3(256), 0, s, S,
+                                       static_cast<const Act*>(tail), static_cast<const Act*>(w), n, parent,
+                                       static_cast<const Act*>(x), a, b, o, status, W, g.B, g.Hk, g.Hv, g.C,
+                                       ut_blocks);
+                }
             }
         });
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
