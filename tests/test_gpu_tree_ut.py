@@ -10,7 +10,11 @@ sequence of a batch (status set, its outputs unwritten, the others verified),
 the checkpoint left untouched, and the full-size batch of 64 sampled against
 the oracle.  Batches of 6 (27B-class) and 70 (tiny) also run the prep
 launch with four nodes per workgroup and two or more UT workgroups per CU.
+At batch 1 and 2 the 27B-class verify splits each head over two workgroups;
+a batch of 4 (whole heads) equals its sequences' batch-1 calls bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -138,3 +142,26 @@ def test_batch64_full_size_sampled(form):
     ow = o_w.cpu().numpy().astype(np.float64)
     for s in range(B):
         per_node(og[s], ow[s], f"sequence {s}")
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_split_heads_equal_whole_heads_bitwise(form):
+    """At batch 1 and 2 each (sequence, value head) of the 27B-class layer is verified by
+    two workgroups, one per half of the rows; from batch 4 on by one.  The arithmetic is
+    the same either way, so every sequence of a batch of 4 equals its own batch-1 call, and
+    the first two equal a batch-2 call, bit for bit."""
+    from tests.test_gpu_tree_batch import one_case
+    inp = gi.tree_batch_inputs(240, QWEN27B_LAYER, 4, n_nodes=32, max_depth=8)
+    n = inp.steps
+    o4, st4 = verify(batch_case(inp), 4, n, form=form)
+    assert (st4 == 0).all()
+    for s in range(4):
+        o1, st1 = verify(one_case(inp, s), 1, n, form=form)
+        assert st1[0] == 0
+        assert torch.equal(o4[s].view(torch.int32), o1[0].view(torch.int32)), f"{form}: sequence {s}"
+    two = dataclasses.replace(inp, batch=2, x=inp.x[:, :2], a=inp.a[:, :2], b=inp.b[:, :2], state=inp.state[:2],
+                              tail=inp.tail[:2],
+                              extra={k: v[:2] if isinstance(v, np.ndarray) else v for k, v in inp.extra.items()})
+    o2, st2 = verify(batch_case(two), 2, n, form=form)
+    assert (st2 == 0).all()
+    assert torch.equal(o2.view(torch.int32), o4[:2].view(torch.int32)), form
