@@ -21,7 +21,7 @@ import torch
 
 import gdn_inputs as gi
 import oracle
-from gdn_inputs import QWEN27B_LAYER, TINY
+from gdn_inputs import F32, QWEN27B_LAYER, TINY, LayerShape
 from tests.conftest import normwise
 from tests.test_gpu_tree_batch import batch_case, seq_major
 
@@ -144,14 +144,18 @@ def test_batch64_full_size_sampled(form):
         per_node(og[s], ow[s], f"sequence {s}")
 
 
+LAYER_F32 = LayerShape(16, 48, 128, 128, 4, F32)   # the 27B-class layer with fp32 activations
+
+
+@pytest.mark.parametrize("shape", [QWEN27B_LAYER, LAYER_F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("form", FORMS)
-def test_split_heads_equal_whole_heads_bitwise(form):
+def test_split_heads_equal_whole_heads_bitwise(form, shape):
     """At batch 1 and 2 each (sequence, value head) of the 27B-class layer is verified by
     two workgroups, one per half of the rows; from batch 4 on by one.  The arithmetic is
     the same either way, so every sequence of a batch of 4 equals its own batch-1 call, and
     the first two equal a batch-2 call, bit for bit."""
     from tests.test_gpu_tree_batch import one_case
-    inp = gi.tree_batch_inputs(240, QWEN27B_LAYER, 4, n_nodes=32, max_depth=8)
+    inp = gi.tree_batch_inputs(240, shape, 4, n_nodes=32, max_depth=8)
     n = inp.steps
     o4, st4 = verify(batch_case(inp), 4, n, form=form)
     assert (st4 == 0).all()
@@ -165,3 +169,13 @@ def test_split_heads_equal_whole_heads_bitwise(form):
     o2, st2 = verify(batch_case(two), 2, n, form=form)
     assert (st2 == 0).all()
     assert torch.equal(o2.view(torch.int32), o4[:2].view(torch.int32)), form
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_f32_activations_27b_layer_matches_oracle(form):
+    """The 27B-class layer with fp32 activations at batch 1 (heads split over two workgroups
+    in the one-launch form): every node within the bar of the oracle's path replay."""
+    inp = gi.tree_batch_inputs(241, LAYER_F32, 1, n_nodes=32, max_depth=8)
+    o, st = verify(batch_case(inp), 1, inp.steps, form=form)
+    assert st[0] == 0
+    per_node(o[0].cpu().numpy(), oracle_tree(inp, 0), f"{form}")
