@@ -327,3 +327,33 @@ def test_tree_verify_ut_noalloc_refusals(lib):
     assert lib.gdn_tree_workspace_bytes(C.byref(mk(batch=12)), 32) <= scratch
     assert lib.gdn_tree_workspace_bytes(C.byref(mk(batch=13)), 32) > scratch
     assert call(mk(batch=13)) == 6
+
+
+def test_prefill_refusals(lib):
+    """gdn_prefill_chunked refuses, before any launch: an empty or negative prompt, head
+    widths other than 128, more than eight value heads per q/k head (GDN_ERR_SHAPE), a
+    missing or short workspace (GDN_ERR_WORKSPACE), a misaligned one (GDN_ERR_ALIGN) and
+    a NULL operand (GDN_ERR_NULL)."""
+    P = C.c_void_p
+    fake = P(0x1000)
+    lib.gdn_prefill_chunked.restype = C.c_int
+    lib.gdn_prefill_chunked.argtypes = [C.POINTER(Dims), P, P, P, C.c_int32, P, P, P, P, P, C.c_size_t, P]
+    lib.gdn_prefill_workspace_bytes.restype = C.c_size_t
+    lib.gdn_prefill_workspace_bytes.argtypes = [C.POINTER(Dims), C.c_int32]
+    d = mk()
+    T = 100
+    need = lib.gdn_prefill_workspace_bytes(C.byref(d), T)
+    assert need > 0
+    call = lambda dd, t, ws, nbytes, state=fake: lib.gdn_prefill_chunked(
+        C.byref(dd), state, fake, fake, t, fake, fake, fake, fake, ws, nbytes, None)
+    for t in (0, -1):
+        assert lib.gdn_prefill_workspace_bytes(C.byref(d), t) == 0
+        assert call(d, t, fake, need) == 2
+    narrow = mk(num_k_heads=4, num_v_heads=4, head_k_dim=32, head_v_dim=32)
+    assert lib.gdn_prefill_workspace_bytes(C.byref(narrow), T) == 0
+    assert call(narrow, T, fake, need) == 2
+    assert call(mk(num_k_heads=1, num_v_heads=16), T, fake, need) == 2   # 16 value heads per q/k head
+    assert call(d, T, None, 0) == 6
+    assert call(d, T, fake, need - 1) == 6
+    assert call(d, T, P(0x1008), need) == 4
+    assert call(d, T, fake, need, state=None) == 1
