@@ -1773,6 +1773,13 @@ static int row_blocks_per_head(const Geo& g) {   // one pass of 4 row groups per
 // 2% at 1 and 2; 16-token blocks, 502 tokens accepted over 64 sequences:
 // 94.1 / 113.7 against 118.9 / 133.0.
 constexpr int64_t kCommitTwoPassMin = 192;
+// From this many pairs on, a block commit gives each wave four row groups (a
+// workgroup covers 64 rows, two workgroups per head).  16-token blocks on the
+// 27B-class layer, 512 tokens accepted over 64 sequences, prepared: 100.6 /
+// 99.0 against 101.7 / 102.0 us (two runs); replaying: 127.1 / 126.3 against
+// 128.5 / 126.5.  A path commit keeps two (four: 85.4 against 82.4 us for 64
+// prepared path commits).
+constexpr int64_t kBlockCommitFourPassMin = 3072;
 
 // Block commit from the prepared operands of the block's positions (the prep
 // launch's workspace): each sequence's state advances by its first len =
@@ -1837,7 +1844,7 @@ __global__ __launch_bounds__(256) void block_commit_kernel(float* __restrict__ S
         return;
 
     // This thread's tail channel (the sequence's workgroups share the C
-    // channels out: at most 96 per workgroup for the supported head widths)
+    // channels out: at most 192 per workgroup for the supported head widths)
     // and its last four inputs, loaded with the operands.
     const int per = (C + blocks_per_head * Hv - 1) / (blocks_per_head * Hv);
     const int tc = (wid % (blocks_per_head * Hv)) * per + static_cast<int>(threadIdx.x);
@@ -1937,7 +1944,8 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
                         const float* a, const float* b, const int32_t* accepted, float* o, int32_t* status, void* ws,
                         bool prepared, hipStream_t s) {
     const bool two = commit && g.D == 128 && static_cast<int64_t>(g.B) * g.Hv >= kCommitTwoPassMin;
-    const int cbph = row_blocks_per_head(g) / (two ? 2 : 1);   // row blocks per head of the commit
+    const bool four = two && static_cast<int64_t>(g.B) * g.Hv >= kBlockCommitFourPassMin;
+    const int cbph = row_blocks_per_head(g) / (four ? 4 : two ? 2 : 1);   // row blocks per head of the commit
     if (commit && !tail_share_fits(g, cbph))
         return hipErrorInvalidValue;
     const TreeWs W = tree_ws_carve(ws, g.B, k, g.Hk, g.Hv, g.D);
@@ -1971,6 +1979,10 @@ hipError_t launch_block(const Geo& g, bool commit, float* S, void* tail, const v
         };
         if (commit) {
             if constexpr (D == 128) {
+                if (four) {
+                    commit_go(std::integral_constant<int, 4>{});
+                    return;
+                }
                 if (two) {
                     commit_go(std::integral_constant<int, 2>{});
                     return;

@@ -196,7 +196,8 @@ def test_prep_in_groups_of_four_with_a_ragged_tail():
 
 
 @pytest.mark.parametrize("shape,B,k,ut", [(QWEN27B_LAYER, 3, 12, False), (QWEN27B_LAYER, 16, 13, True),
-                                          (TINY, 5, 32, True)], ids=["27b_B3_walk", "27b_B16_ut", "tiny_B5_ut"])
+                                          (QWEN27B_LAYER, 64, 16, True), (TINY, 5, 32, True)],
+                         ids=["27b_B3_walk", "27b_B16_ut", "27b_B64_ut", "tiny_B5_ut"])
 def test_prepared_block_commit_equals_block_commit_bitwise(shape, B, k, ut):
     """A block commit that reads the operands from the verify's workspace leaves the same
     state, tail, outputs and statuses, bit for bit, as the one that prepares them again
