@@ -1777,8 +1777,9 @@ constexpr int64_t kCommitTwoPassMin = 192;
 // workgroup covers 64 rows, two workgroups per head).  16-token blocks on the
 // 27B-class layer, 512 tokens accepted over 64 sequences, prepared: 100.6 /
 // 99.0 against 101.7 / 102.0 us (two runs); replaying: 127.1 / 126.3 against
-// 128.5 / 126.5.  A path commit keeps two (four: 85.4 against 82.4 us for 64
-// prepared path commits).
+// 128.5 / 126.5.  A path commit from the prepared operands keeps two (four:
+// 85.4 against 82.4 us for 64 prepared path commits); the replaying path commit
+// takes four here too (101.0 / 101.1 against 106.6 / 106.6 us at 64 paths).
 constexpr int64_t kBlockCommitFourPassMin = 3072;
 
 // Block commit from the prepared operands of the block's positions (the prep
@@ -2236,9 +2237,12 @@ __global__ __launch_bounds__(256) void commit_tail_kernel(Act* __restrict__ tail
 hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int n, const int32_t* parent,
                          const void* x, const float* a, const float* b, int L, const int32_t* path, float* o,
                          int32_t* status, void* ws, hipStream_t s) {
-    // Two passes per wave (half as many workgroups) once the batch fills the chip.
+    // Two passes per wave (half as many workgroups) once the batch fills the chip;
+    // four in the replaying form at the block commit's threshold, where fewer
+    // workgroups also means fewer convolutions of the path's tokens.
     const bool two = g.D == 128 && static_cast<int64_t>(g.B) * g.Hv >= kCommitTwoPassMin;
-    const int bph = row_blocks_per_head(g) / (two ? 2 : 1);
+    const bool four = two && ws == nullptr && static_cast<int64_t>(g.B) * g.Hv >= kBlockCommitFourPassMin;
+    const int bph = row_blocks_per_head(g) / (four ? 4 : two ? 2 : 1);
     if (ws != nullptr && !tail_share_fits(g, bph))
         return hipErrorInvalidValue;
     hipError_t e = dispatch(g, [&](auto dtag, auto atag) {
@@ -2259,6 +2263,10 @@ hipError_t launch_commit(const Geo& g, float* S, void* tail, const void* w, int 
                                    tree_ws_carve(ws, g.B, n, g.Hk, g.Hv, g.D));
         };
         if constexpr (D == 128) {
+            if (four) {
+                go(std::integral_constant<int, 4>{});
+                return;
+            }
             if (two) {
                 go(std::integral_constant<int, 2>{});
                 return;
